@@ -1,0 +1,268 @@
+#!/usr/bin/env python3
+"""Benchmark of one DFlash drafting round on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload q1]
+
+A step is one pass of the whole hot path over one batch: fuse the target
+features of the rows accepted last round (1-16 rows per sequence, a seeded
+schedule), inject them into every layer's context K/V, run the drafter forward
+on [anchor, MASK x 15] with the fused argmax and greedy accept against seeded
+target tokens, and take the bonus token as the next anchor. Inputs are resident
+in HBM before the timed region; each step starts from the same context length
+(the prefilled 2048 positions), so every step does the same work.
+
+Prints one JSON line: throughput in drafted block-tokens/s (batch * 16 per
+step), the dominant kernel against its roofline (timed live with HIP events on
+the library's stream), the whole step against its roofline, and the CPU oracle
+timed on this host on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+METRIC = "drafted block-tokens/sec (5-layer, block 16) + % HBM/MFMA roofline"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="q1", choices=["q1", "q32", "q4l", "l16"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="approximate CPU time budget of the oracle sample")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="run one 1 GiB device copy before timing (HBM counter calibration)")
+    return ap.parse_args()
+
+
+def main() -> int:
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {a.gpus} is not supported by this "
+              "single-GPU build (the drafter pass needs no exchange between GPUs).",
+              file=sys.stderr)
+        return 2
+    import torch
+    from block_diffusion_drafter_amd import binding as B
+    from synth import WORKLOADS
+    from synth import inputs as I
+    from synth import torch_io
+
+    if not torch.cuda.is_available():
+        print("no GPU visible: bench.py needs an MI355X", file=sys.stderr)
+        return 1
+    W = WORKLOADS[a.workload]
+    cfg = W.model
+    b, Bk, d = W.batch, cfg.block_size, cfg.hidden
+    ctx_lens = I.ctx_lengths(W)
+    max_new = 16
+    cap = int(((int(ctx_lens.max()) + max_new + Bk + 31) // 32) * 32)
+    print(f"[bench] workload {W.name}: batch {b}, ctx {int(ctx_lens.min())}-{int(ctx_lens.max())}, "
+          f"capacity {cap}", file=sys.stderr, flush=True)
+
+    host = I.Weights(cfg, W.seeds["weights"])
+    dev = torch_io.weights_to_device(host)
+    model = B.DraftModel(cfg, dev)
+    dt = model.dtype
+
+    # ---- prefill (untimed): the context the rounds draft against -------------
+    n_pre = int(ctx_lens.sum())
+    chunk_rows = 8192
+    ws = model.new_workspace(b, cap, max(chunk_rows, b * max_new))
+    cache = model.new_cache(b, cap)
+    cu_all = np.concatenate([[0], np.cumsum(ctx_lens)]).astype(np.int64)
+    for s in range(b):
+        for lo in range(0, int(ctx_lens[s]), chunk_rows):
+            n = min(chunk_rows, int(ctx_lens[s]) - lo)
+            feats = I.target_hiddens(cfg, n, seed=W.seeds["hiddens"], tag=f"prefill.{s}.{lo}")
+            fd = [torch_io.to_device(f) for f in feats]
+            ctx = torch.empty((n, d), dtype=dt, device="cuda")
+            model.ctx_project(fd, ctx, ws)
+            counts = np.zeros(b, np.int32)
+            counts[s] = n
+            cu = torch.from_numpy(np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)).cuda()
+            model.ctx_kv_append(cache, ctx, cu, ws)
+    torch.cuda.synchronize()
+    base_len = cache.ctx_len.clone()
+
+    # ---- per-round inputs (resident before timing) ----------------------------
+    rng = np.random.Generator(np.random.PCG64(W.seeds["round_base"]))
+    n_new = rng.integers(1, max_new + 1, size=b).astype(np.int32)
+    n_tok = int(n_new.sum())
+    feats = I.target_hiddens(cfg, n_tok, seed=W.seeds["round_base"], tag="round")
+    feats_d = [torch_io.to_device(f) for f in feats]
+    cu_new = torch.from_numpy(np.concatenate([[0], np.cumsum(n_new)]).astype(np.int32)).cuda()
+    ctx_new = torch.empty((n_tok, d), dtype=dt, device="cuda")
+    anchor0 = torch.from_numpy(I.anchors(cfg, b, seed=W.seeds["targets"])).cuda()
+    anchor = anchor0.clone()
+    targets = torch.from_numpy(I.uniform_tokens(cfg, (b, Bk), W.seeds["targets"], "bench")).cuda()
+    drafts = torch.empty((b, Bk - 1), dtype=torch.int32, device="cuda")
+    acc = torch.empty(b, dtype=torch.int32, device="cuda")
+    bonus = torch.empty(b, dtype=torch.int32, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+
+    def step():
+        cache.ctx_len.copy_(base_len)
+        model.ctx_project(feats_d, ctx_new, ws)
+        model.ctx_kv_append(cache, ctx_new, cu_new, ws, status)
+        model.draft_forward(cache, anchor, drafts, ws, target_tokens=targets, accept_len=acc,
+                            bonus=bonus, dev_status=status)
+        anchor.copy_(bonus)  # next round's anchor is the bonus token
+
+    if a.copy_probe:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    assert status.item() == 0, f"device status {status.item()}"
+
+    # ---- timed region ----------------------------------------------------------
+    B.profiler_start(100000)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(a.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    B.profiler_stop()
+    ms_total = e0.elapsed_time(e1)
+    ms_step = ms_total / a.steps
+    prof = B.profiler_read()
+    B.profiler_reset()
+    assert status.item() == 0, f"device status {status.item()}"
+
+    value = b * Bk / (ms_step / 1e3)
+
+    # ---- algorithmic bytes / flops per kernel class -----------------------------
+    es = 2 if cfg.dtype == "bf16" else 4
+    L, hd, Hkv, Hq = cfg.n_layers, cfg.head_dim, cfg.n_kv_heads, cfg.n_heads
+    keys = (base_len.cpu().numpy().astype(np.int64) + n_new + Bk)
+    attn_bytes_per_launch = float(keys.sum() * Hkv * hd * es * 2)   # K and V of every key
+    attn_flops_per_launch = float(keys.sum() * Hq * Bk * hd * 4)
+    prof["attention"]["bytes"] = attn_bytes_per_launch * prof["attention"]["launches"]
+    prof["attention"]["flops"] = attn_flops_per_launch * prof["attention"]["launches"]
+
+    def frac_of(entry):
+        t = entry["ms"] / 1e3
+        if t <= 0:
+            return None
+        gbs = entry["bytes"] / t / 1e9
+        tfl = entry["flops"] / t / 1e12
+        ai = entry["flops"] / max(entry["bytes"], 1.0)
+        bound = "mfma" if ai > BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9) else "hbm"
+        return gbs, tfl, bound
+
+    dom_name = max((k for k in prof if prof[k]["launches"]), key=lambda k: prof[k]["ms"])
+    dom = prof[dom_name]
+    gbs, tfl, bound = frac_of(dom)
+    per_launch_ms = dom["ms"] / dom["launches"]
+    if bound == "hbm":
+        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    else:
+        roof = {"bound": "mfma", "achieved": round(tfl, 1), "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(tfl / BF16_PEAK_TFLOPS, 4)}
+    roof.update({"traffic": None, "kernel": dom_name, "launches_per_step": dom["launches"] // a.steps,
+                 "ms_per_launch": round(per_launch_ms, 5),
+                 "algorithmic_bytes_per_launch": dom["bytes"] / dom["launches"],
+                 "algorithmic_flops_per_launch": dom["flops"] / dom["launches"]})
+
+    # whole-step roofline: sum over kernels of max(bytes/BW, flops/peak)
+    t_roof = 0.0
+    for k, e in prof.items():
+        if e["launches"]:
+            t_roof += max(e["bytes"] / (HBM_PEAK_GBS * 1e9), e["flops"] / (BF16_PEAK_TFLOPS * 1e12))
+    t_roof /= a.steps
+    kernels = {k: {"launches_per_step": e["launches"] // a.steps,
+                   "ms_per_step": round(e["ms"] / a.steps, 5),
+                   "GBps": round(e["bytes"] / (e["ms"] / 1e3) / 1e9, 1) if e["ms"] > 0 else None}
+               for k, e in prof.items() if e["launches"]}
+
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "block-tokens/s",
+        "n_gpus": 1, "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic: seeded random-init drafter N(0,0.02^2), N(0,1) target hidden states",
+        "config": {"workload": W.name, "batch": b, "block": Bk, "layers": L,
+                   "ctx_len": [int(ctx_lens.min()), int(ctx_lens.max())],
+                   "new_rows_per_round": int(n_tok), "hidden": d, "heads": [Hq, Hkv],
+                   "intermediate": cfg.intermediate, "vocab": cfg.vocab,
+                   "parallelism": "none (1 GPU)"},
+        "roofline": roof,
+        "step_roofline": {"t_roof_ms": round(t_roof * 1e3, 5),
+                          "frac": round(t_roof * 1e3 / ms_step, 4),
+                          "peaks": {"hbm_GBps": HBM_PEAK_GBS, "bf16_TFLOPs": BF16_PEAK_TFLOPS}},
+        "kernels": kernels,
+        "wall_s_timed": round(wall, 4),
+    }
+
+    if not a.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(W, host, ctx_lens, n_new, feats, a.cpu_seconds)
+
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def cpu_baseline(W, host, ctx_lens, n_new, feats, budget_s):
+    """The CPU oracle (fp64 NumPy, as it stands) on one sequence of the same
+    round: fuse + inject its new rows, run the drafter forward and accept.
+    The sequence's existing context K/V is a seeded synthetic cache state
+    (setup, untimed). Reported in block-tokens/s."""
+    from oracle import dflash_oracle as O
+    from synth import inputs as I
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    cfg = W.model
+    ow = {n: host.get(n).f32() for n in host.names()}
+    if cfg.tied_embeddings:
+        ow["lm_head"] = ow["embed"]
+    c0 = int(ctx_lens[0])
+    st = I.cache_state(cfg, [c0], seed=W.seeds["hiddens"] + 100)
+    cache = O.SeqCache([st[l][0][0].f64() for l in range(cfg.n_layers)],
+                       [st[l][0][1].f64() for l in range(cfg.n_layers)])
+    n0 = int(n_new[0])
+    f0 = [f.f32()[:n0] for f in feats]
+    anchor = I.anchors(cfg, 1, seed=W.seeds["targets"])
+    targets = I.uniform_tokens(cfg, (1, cfg.block_size), W.seeds["targets"], "bench")
+    rounds, t_used = 0, 0.0
+    while rounds < 1 or (t_used < budget_s and rounds < 20):
+        t0 = time.perf_counter()
+        ctx = O.ctx_project(f0, ow["fc"], ow["fc_norm"], cfg.rms_eps)
+        new = O.prefill_cache(ctx, c0, ow, cfg)
+        res = O.draft_forward(cfg, ow, [cache.append(new)], anchor)
+        O.accept(res.drafts, targets)
+        t_used += time.perf_counter() - t0
+        rounds += 1
+    return {"value": round(cfg.block_size * rounds / t_used, 3), "unit": "block-tokens/s",
+            "cores": cores, "kind": "oracle",
+            "sample": f"{rounds} round(s) of 1 sequence of {W.name} (ctx {c0}, {n0} new rows), "
+                      f"fp64 NumPy, {t_used:.1f} s"}
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,583 @@
+// C ABI of the drafter library: argument validation, workspace layout, and
+// the launch sequence of each call. No device memory is allocated here; all
+// scratch comes from the caller's workspace.
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <vector>
+
+#include "internal.h"
+
+struct dflash_handle {
+  dflash_config cfg;
+  dflash_weights w;
+  std::vector<dflash_layer_weights> layers;
+};
+
+namespace dflash {
+
+// ---------------------------------------------------------------------------
+// Kernel timing: HIP events bracket every launch while enabled.
+// ---------------------------------------------------------------------------
+struct ProfRec {
+  int kind;
+  double bytes, flops;
+  hipEvent_t e0, e1;
+  bool closed;
+};
+static std::vector<ProfRec> g_rec;
+static std::vector<hipEvent_t> g_pool;
+static size_t g_pool_next = 0;
+static bool g_prof_on = false;
+static int g_open = -1;
+
+void prof_begin(int kind, double bytes, double flops, hipStream_t st) {
+  if (!g_prof_on || g_pool_next + 2 > g_pool.size()) return;
+  ProfRec r{kind, bytes, flops, g_pool[g_pool_next], g_pool[g_pool_next + 1], false};
+  g_pool_next += 2;
+  if (hipEventRecord(r.e0, st) != hipSuccess) return;
+  g_rec.push_back(r);
+  g_open = (int)g_rec.size() - 1;
+}
+
+void prof_end(hipStream_t st) {
+  if (g_open < 0) return;
+  if (hipEventRecord(g_rec[g_open].e1, st) == hipSuccess) g_rec[g_open].closed = true;
+  g_open = -1;
+}
+
+}  // namespace dflash
+
+using namespace dflash;
+
+namespace {
+
+inline int elem_size(int dtype) { return dtype == DFLASH_BF16 ? 2 : 4; }
+inline bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+#define DF_HIP(expr)                         \
+  do {                                       \
+    if ((expr) != hipSuccess) return DFLASH_ERR_HIP; \
+  } while (0)
+
+struct Plan {
+  size_t x, h, qkv, q, po, pml, attn, act, y, amax, fwd_end;
+  size_t u, proj_end;
+  size_t kv, app_end;
+  int chunk, max_chunks, n_vtiles;
+  size_t total;
+};
+
+// Keys per attention work item: aim for ~2048 items over the cache so every
+// CU has several, but never below 64 keys (partials would rival the K/V
+// stream) nor above 2048.
+int choose_chunk(int batch, int hkv, int cap) {
+  long long keys = (long long)batch * hkv * cap;
+  long long c = (keys + 2047) / 2048;
+  c = (c + 31) / 32 * 32;
+  c = std::max(64LL, std::min(2048LL, c));
+  return (int)c;
+}
+
+Plan make_plan(const dflash_config& c, int batch, int cap, int max_tokens) {
+  Plan p{};
+  const size_t es = elem_size(c.dtype);
+  const size_t B = c.block_size, M = (size_t)batch * B, d = c.hidden, hd = c.head_dim;
+  const size_t Hq = c.n_heads, Hkv = c.n_kv_heads, G = Hq / Hkv, I = c.intermediate;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = align256(off + bytes);
+    return o;
+  };
+  p.x = take(M * d * 4);
+  p.h = take(M * d * es);
+  p.qkv = take(M * (Hq + 2 * Hkv) * hd * 4);
+  p.q = take((size_t)batch * Hq * 16 * hd * es);
+  p.chunk = choose_chunk(batch, (int)Hkv, cap);
+  p.max_chunks = (cap + p.chunk - 1) / p.chunk;
+  p.po = take((size_t)batch * Hkv * p.max_chunks * G * hd * 16 * 4);
+  p.pml = take((size_t)batch * Hkv * p.max_chunks * G * 16 * 2 * 4);
+  p.attn = take(M * Hq * hd * es);
+  p.act = take(M * I * es);
+  const size_t R = (size_t)batch * (B - 1);
+  p.y = take(R * d * es);
+  p.n_vtiles = (c.vocab + 15) / 16;
+  p.amax = take(R * p.n_vtiles * 8);
+  p.fwd_end = off;
+  off = 0;
+  p.u = take((size_t)max_tokens * d * 4);
+  p.proj_end = off;
+  off = 0;
+  p.kv = take((size_t)max_tokens * c.n_layers * 2 * Hkv * hd * 4);
+  p.app_end = off;
+  p.total = std::max(p.fwd_end, std::max(p.proj_end, p.app_end));
+  return p;
+}
+
+int32_t check_config(const dflash_config& c) {
+  if (c.dtype != DFLASH_BF16 && c.dtype != DFLASH_FP32) return DFLASH_ERR_DTYPE;
+  const int mult = c.dtype == DFLASH_BF16 ? 32 : 16;
+  if (c.hidden <= 0 || c.n_heads <= 0 || c.n_kv_heads <= 0 || c.intermediate <= 0 ||
+      c.n_target_feats <= 0 || c.target_hidden <= 0 || c.vocab < 2 || c.n_layers <= 0)
+    return DFLASH_ERR_SHAPE;
+  if (c.n_heads % c.n_kv_heads) return DFLASH_ERR_SHAPE;
+  const int G = c.n_heads / c.n_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return DFLASH_ERR_UNSUPPORTED;
+  if (c.head_dim != 64 && c.head_dim != 128) return DFLASH_ERR_UNSUPPORTED;
+  if (c.block_size < 1 || c.block_size > 16) return DFLASH_ERR_UNSUPPORTED;
+  if (c.n_layers > kMaxLayers) return DFLASH_ERR_UNSUPPORTED;
+  if (c.n_target_feats > kMaxASeg) return DFLASH_ERR_UNSUPPORTED;
+  if (c.hidden % mult || c.intermediate % mult || c.target_hidden % mult) return DFLASH_ERR_SHAPE;
+  if (c.mask_token_id < 0 || c.mask_token_id >= c.vocab) return DFLASH_ERR_SHAPE;
+  if (!(c.rms_eps >= 0.f) || !std::isfinite(c.rms_eps)) return DFLASH_ERR_SHAPE;
+  if (!std::isfinite(c.rope_theta)) return DFLASH_ERR_SHAPE;
+  return DFLASH_OK;
+}
+
+GemmArgs gemm_base(const void* a, int64_t a_stride, int M, int N, int K) {
+  GemmArgs g;
+  std::memset(&g, 0, sizeof(g));
+  g.a[0] = a;
+  g.a_stride = a_stride;
+  g.a_seg_k = K;
+  g.a_nseg = 1;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  return g;
+}
+
+void one_seg(GemmArgs& g, const void* w, const void* w2 = nullptr) {
+  g.w[0] = w;
+  g.w2[0] = w2;
+  g.w_row0[0] = 0;
+  g.w_row0[1] = g.N;
+  g.w_nseg = 1;
+}
+
+int32_t run_gemm(int dtype, int epi, const GemmArgs& g, hipStream_t st) {
+  const int kind = epi == EPI_STORE_F32 ? DFLASH_K_GEMM_F32OUT
+                   : epi == EPI_RESID   ? DFLASH_K_GEMM_RESID
+                   : epi == EPI_SWIGLU  ? DFLASH_K_GEMM_SWIGLU
+                                        : DFLASH_K_LMHEAD;
+  const double es = elem_size(dtype);
+  const double nb = epi == EPI_SWIGLU ? 2.0 : 1.0;
+  double out_bytes = 0;
+  if (epi == EPI_STORE_F32) out_bytes = 4.0 * g.M * g.N;
+  else if (epi == EPI_RESID) out_bytes = 8.0 * g.M * g.N;
+  else if (epi == EPI_SWIGLU) out_bytes = es * g.M * g.N;
+  else out_bytes = 8.0 * g.M * ((g.N + 15) / 16);
+  const double bytes = nb * es * g.N * g.K + es * g.M * g.K + out_bytes;
+  const double flops = 2.0 * nb * g.M * g.N * g.K;
+  prof_begin(kind, bytes, flops, st);
+  const hipError_t e = launch_gemm(dtype, epi, g, st);
+  prof_end(st);
+  return e == hipSuccess ? DFLASH_OK : DFLASH_ERR_HIP;
+}
+
+int32_t check_cache(const dflash_handle* h, const dflash_kv_cache* c) {
+  if (!c || !c->k || !c->v || !c->ctx_len) return DFLASH_ERR_NULL;
+  if (!al16(c->k) || !al16(c->v)) return DFLASH_ERR_ALIGN;
+  if (c->batch <= 0 || c->capacity <= 0 || c->capacity % kKeyBlock) return DFLASH_ERR_SHAPE;
+  if (c->capacity < h->cfg.block_size) return DFLASH_ERR_SHAPE;
+  return DFLASH_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dflash_status_string(int32_t code) {
+  switch (code) {
+    case DFLASH_OK: return "ok";
+    case DFLASH_ERR_NULL: return "a required pointer is NULL";
+    case DFLASH_ERR_SHAPE: return "a size is out of range or inconsistent";
+    case DFLASH_ERR_DTYPE: return "unknown dtype";
+    case DFLASH_ERR_ALIGN: return "a pointer or stride is not 16-byte aligned";
+    case DFLASH_ERR_WORKSPACE: return "workspace is smaller than dflash_workspace_bytes()";
+    case DFLASH_ERR_UNSUPPORTED: return "configuration not covered by the kernels";
+    case DFLASH_ERR_HIP: return "a HIP launch reported an error";
+    case DFLASH_ERR_STATE: return "profiler misuse";
+    default: return "unknown status";
+  }
+}
+
+int32_t dflash_create(const dflash_config* cfg, const dflash_weights* w, dflash_handle** out) {
+  if (!out) return DFLASH_ERR_NULL;
+  *out = nullptr;
+  if (!cfg || !w) return DFLASH_ERR_NULL;
+  int32_t rc = check_config(*cfg);
+  if (rc) return rc;
+  if (!w->embed || !w->lm_head || !w->fc || !w->fc_norm || !w->final_norm || !w->layers)
+    return DFLASH_ERR_NULL;
+  const void* top[] = {w->embed, w->lm_head, w->fc, w->fc_norm, w->final_norm};
+  for (const void* p : top)
+    if (!al16(p)) return DFLASH_ERR_ALIGN;
+  for (int l = 0; l < cfg->n_layers; ++l) {
+    const dflash_layer_weights& lw = w->layers[l];
+    const void* ps[] = {lw.in_norm, lw.wq, lw.wk, lw.wv, lw.q_norm, lw.k_norm,
+                        lw.wo, lw.post_norm, lw.w_gate, lw.w_up, lw.w_down};
+    for (const void* p : ps) {
+      if (!p) return DFLASH_ERR_NULL;
+      if (!al16(p)) return DFLASH_ERR_ALIGN;
+    }
+  }
+  dflash_handle* hd = new (std::nothrow) dflash_handle;
+  if (!hd) return DFLASH_ERR_SHAPE;
+  hd->cfg = *cfg;
+  hd->w = *w;
+  hd->layers.assign(w->layers, w->layers + cfg->n_layers);
+  hd->w.layers = hd->layers.data();
+  *out = hd;
+  return DFLASH_OK;
+}
+
+void dflash_destroy(dflash_handle* h) { delete h; }
+
+int64_t dflash_workspace_bytes(const dflash_handle* h, int32_t max_batch, int32_t capacity,
+                               int32_t max_tokens) {
+  if (!h) return DFLASH_ERR_NULL;
+  if (max_batch < 1 || capacity < 1 || max_tokens < 0) return DFLASH_ERR_SHAPE;
+  size_t best = 0;
+  for (int b = 1; b <= max_batch; ++b)
+    best = std::max(best, make_plan(h->cfg, b, capacity, max_tokens).total);
+  return (int64_t)best;
+}
+
+int32_t dflash_ctx_project(const dflash_handle* h, const void* const* feats,
+                           int64_t feat_row_stride, int32_t n_tok, void* ctx_out, void* ws,
+                           int64_t ws_bytes, void* stream) {
+  if (!h) return DFLASH_ERR_NULL;
+  const dflash_config& c = h->cfg;
+  if (n_tok < 0) return DFLASH_ERR_SHAPE;
+  if (n_tok == 0) return DFLASH_OK;
+  if (!feats || !ctx_out || !ws) return DFLASH_ERR_NULL;
+  if (feat_row_stride < c.target_hidden || feat_row_stride % 8) return DFLASH_ERR_SHAPE;
+  for (int f = 0; f < c.n_target_feats; ++f) {
+    if (!feats[f]) return DFLASH_ERR_NULL;
+    if (!al16(feats[f])) return DFLASH_ERR_ALIGN;
+  }
+  if (!al16(ctx_out) || !al16(ws)) return DFLASH_ERR_ALIGN;
+  const Plan P = make_plan(c, 1, kKeyBlock, n_tok);
+  if (ws_bytes < (int64_t)P.proj_end) return DFLASH_ERR_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  float* u = reinterpret_cast<float*>((char*)ws + P.u);
+  GemmArgs g = gemm_base(nullptr, feat_row_stride, n_tok, c.hidden, c.n_target_feats * c.target_hidden);
+  for (int f = 0; f < c.n_target_feats; ++f) g.a[f] = feats[f];
+  g.a_nseg = c.n_target_feats;
+  g.a_seg_k = c.target_hidden;
+  one_seg(g, h->w.fc);
+  g.out = u;
+  g.out_stride = c.hidden;
+  int32_t rc = run_gemm(c.dtype, EPI_STORE_F32, g, st);
+  if (rc) return rc;
+  prof_begin(DFLASH_K_RMSNORM, 0, 0, st);
+  hipError_t e = launch_rmsnorm(c.dtype, u, c.hidden, h->w.fc_norm, ctx_out, c.hidden, n_tok,
+                                c.hidden, c.rms_eps, n_tok, 0, 0, st);
+  prof_end(st);
+  return e == hipSuccess ? DFLASH_OK : DFLASH_ERR_HIP;
+}
+
+int32_t dflash_ctx_kv_append(const dflash_handle* h, const dflash_kv_cache* cache, const void* ctx,
+                             const int32_t* cu_new, int32_t n_tok, int32_t* dev_status, void* ws,
+                             int64_t ws_bytes, void* stream) {
+  if (!h) return DFLASH_ERR_NULL;
+  const dflash_config& c = h->cfg;
+  int32_t rc = check_cache(h, cache);
+  if (rc) return rc;
+  if (n_tok < 0) return DFLASH_ERR_SHAPE;
+  if (!cu_new) return DFLASH_ERR_NULL;
+  if (n_tok > 0 && (!ctx || !ws)) return DFLASH_ERR_NULL;
+  if ((ctx && !al16(ctx)) || (ws && !al16(ws))) return DFLASH_ERR_ALIGN;
+  const Plan P = make_plan(c, 1, cache->capacity, n_tok);
+  if (n_tok > 0 && ws_bytes < (int64_t)P.app_end) return DFLASH_ERR_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  const int Hkv = c.n_kv_heads, hd = c.head_dim, L = c.n_layers;
+  if (n_tok > 0) {
+    float* kv = reinterpret_cast<float*>((char*)ws + P.kv);
+    const int N = L * 2 * Hkv * hd;
+    GemmArgs g = gemm_base(ctx, c.hidden, n_tok, N, c.hidden);
+    for (int l = 0; l < L; ++l) {
+      g.w[2 * l] = h->layers[l].wk;
+      g.w[2 * l + 1] = h->layers[l].wv;
+      g.w_row0[2 * l] = (2 * l) * Hkv * hd;
+      g.w_row0[2 * l + 1] = (2 * l + 1) * Hkv * hd;
+    }
+    g.w_row0[2 * L] = N;
+    g.w_nseg = 2 * L;
+    g.out = kv;
+    g.out_stride = N;
+    rc = run_gemm(c.dtype, EPI_STORE_F32, g, st);
+    if (rc) return rc;
+    NormRopeArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.src = kv;
+    a.src_stride = N;
+    a.k_cache = cache->k;
+    a.v_cache = cache->v;
+    for (int l = 0; l < L; ++l) a.k_norm[l] = h->layers[l].k_norm;
+    a.ctx_len = cache->ctx_len;
+    a.cu_new = cu_new;
+    a.dev_status = dev_status;
+    a.batch = cache->batch;
+    a.cache_batch = cache->batch;
+    a.n_heads = c.n_heads;
+    a.n_kv_heads = Hkv;
+    a.head_dim = hd;
+    a.block = c.block_size;
+    a.cap = cache->capacity;
+    a.n_layers = L;
+    a.n_tok = n_tok;
+    a.eps = c.rms_eps;
+    a.rope_theta = c.rope_theta;
+    prof_begin(DFLASH_K_NORM_ROPE, 0, 0, st);
+    hipError_t e = launch_norm_rope_append(c.dtype, a, st);
+    prof_end(st);
+    if (e != hipSuccess) return DFLASH_ERR_HIP;
+  }
+  prof_begin(DFLASH_K_SMALL, 0, 0, st);
+  hipError_t e = launch_ctx_len_add(cache->ctx_len, cu_new, cache->batch, n_tok, cache->capacity,
+                                    dev_status, st);
+  prof_end(st);
+  return e == hipSuccess ? DFLASH_OK : DFLASH_ERR_HIP;
+}
+
+int32_t dflash_draft_forward(const dflash_handle* h, const dflash_kv_cache* cache,
+                             const int32_t* anchor, int32_t batch, int32_t* draft_tokens,
+                             float* logits, float* hidden_out, const int32_t* target_tokens,
+                             int32_t* accept_len, int32_t* bonus, int32_t* dev_status, void* ws,
+                             int64_t ws_bytes, void* stream) {
+  if (!h) return DFLASH_ERR_NULL;
+  const dflash_config& c = h->cfg;
+  int32_t rc = check_cache(h, cache);
+  if (rc) return rc;
+  if (batch < 1 || batch > cache->batch) return DFLASH_ERR_SHAPE;
+  const int B = c.block_size;
+  if (!anchor || !ws) return DFLASH_ERR_NULL;
+  if (B > 1 && !draft_tokens) return DFLASH_ERR_NULL;
+  if (target_tokens && (!accept_len || !bonus)) return DFLASH_ERR_NULL;
+  if (!al16(ws) || (logits && !al16(logits)) || (hidden_out && !al16(hidden_out)))
+    return DFLASH_ERR_ALIGN;
+  const int cap = cache->capacity;
+  const Plan P = make_plan(c, batch, cap, 0);
+  if (ws_bytes < (int64_t)P.fwd_end) return DFLASH_ERR_WORKSPACE;
+
+  hipStream_t st = (hipStream_t)stream;
+  char* w = (char*)ws;
+  float* x = reinterpret_cast<float*>(w + P.x);
+  void* hbuf = w + P.h;
+  float* qkv = reinterpret_cast<float*>(w + P.qkv);
+  void* qbuf = w + P.q;
+  void* attn = w + P.attn;
+  void* act = w + P.act;
+  void* ybuf = w + P.y;
+  unsigned long long* amax = reinterpret_cast<unsigned long long*>(w + P.amax);
+
+  const int es = elem_size(c.dtype);
+  const int d = c.hidden, hd = c.head_dim, Hq = c.n_heads, Hkv = c.n_kv_heads, I = c.intermediate;
+  const int M = batch * B, L = c.n_layers;
+  const size_t layer_elems = (size_t)cache->batch * Hkv * cap * hd;
+
+  prof_begin(DFLASH_K_SMALL, 0, 0, st);
+  hipError_t e = launch_embed(c.dtype, h->w.embed, anchor, batch, B, d, c.vocab, c.mask_token_id,
+                              x, dev_status, st);
+  prof_end(st);
+  if (e != hipSuccess) return DFLASH_ERR_HIP;
+
+  for (int l = 0; l < L; ++l) {
+    const dflash_layer_weights& lw = h->layers[l];
+    prof_begin(DFLASH_K_RMSNORM, 0, 0, st);
+    e = launch_rmsnorm(c.dtype, x, d, lw.in_norm, hbuf, d, M, d, c.rms_eps, M, 0, 0, st);
+    prof_end(st);
+    if (e != hipSuccess) return DFLASH_ERR_HIP;
+
+    const int Nqkv = (Hq + 2 * Hkv) * hd;
+    GemmArgs g = gemm_base(hbuf, d, M, Nqkv, d);
+    g.w[0] = lw.wq;
+    g.w[1] = lw.wk;
+    g.w[2] = lw.wv;
+    g.w_row0[0] = 0;
+    g.w_row0[1] = Hq * hd;
+    g.w_row0[2] = (Hq + Hkv) * hd;
+    g.w_row0[3] = Nqkv;
+    g.w_nseg = 3;
+    g.out = qkv;
+    g.out_stride = Nqkv;
+    if ((rc = run_gemm(c.dtype, EPI_STORE_F32, g, st))) return rc;
+
+    NormRopeArgs nr;
+    std::memset(&nr, 0, sizeof(nr));
+    nr.src = qkv;
+    nr.src_stride = Nqkv;
+    nr.q_out = qbuf;
+    nr.k_cache = (char*)cache->k + layer_elems * es * l;
+    nr.v_cache = (char*)cache->v + layer_elems * es * l;
+    nr.q_norm[0] = lw.q_norm;
+    nr.k_norm[0] = lw.k_norm;
+    nr.ctx_len = cache->ctx_len;
+    nr.dev_status = dev_status;
+    nr.batch = batch;
+    nr.cache_batch = cache->batch;
+    nr.n_heads = Hq;
+    nr.n_kv_heads = Hkv;
+    nr.head_dim = hd;
+    nr.block = B;
+    nr.cap = cap;
+    nr.n_layers = 1;
+    nr.eps = c.rms_eps;
+    nr.rope_theta = c.rope_theta;
+    prof_begin(DFLASH_K_NORM_ROPE, 0, 0, st);
+    e = launch_norm_rope_forward(c.dtype, nr, st);
+    prof_end(st);
+    if (e != hipSuccess) return DFLASH_ERR_HIP;
+
+    AttnArgs at;
+    std::memset(&at, 0, sizeof(at));
+    at.q = qbuf;
+    at.k = nr.k_cache;
+    at.v = nr.v_cache;
+    at.ctx_len = cache->ctx_len;
+    at.batch = batch;
+    at.n_heads = Hq;
+    at.n_kv_heads = Hkv;
+    at.head_dim = hd;
+    at.block = B;
+    at.cap = cap;
+    at.chunk = P.chunk;
+    at.max_chunks = P.max_chunks;
+    at.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)hd));
+    at.part_o = reinterpret_cast<float*>(w + P.po);
+    at.part_ml = reinterpret_cast<float*>(w + P.pml);
+    at.out = attn;
+    prof_begin(DFLASH_K_ATTN, 0, 0, st);
+    e = launch_attention(c.dtype, at, st);
+    prof_end(st);
+    if (e != hipSuccess) return DFLASH_ERR_HIP;
+
+    g = gemm_base(attn, Hq * hd, M, d, Hq * hd);
+    one_seg(g, lw.wo);
+    g.resid = x;
+    g.out_stride = d;
+    if ((rc = run_gemm(c.dtype, EPI_RESID, g, st))) return rc;
+
+    prof_begin(DFLASH_K_RMSNORM, 0, 0, st);
+    e = launch_rmsnorm(c.dtype, x, d, lw.post_norm, hbuf, d, M, d, c.rms_eps, M, 0, 0, st);
+    prof_end(st);
+    if (e != hipSuccess) return DFLASH_ERR_HIP;
+
+    g = gemm_base(hbuf, d, M, I, d);
+    one_seg(g, lw.w_gate, lw.w_up);
+    g.out = act;
+    g.out_stride = I;
+    if ((rc = run_gemm(c.dtype, EPI_SWIGLU, g, st))) return rc;
+
+    g = gemm_base(act, I, M, d, I);
+    one_seg(g, lw.w_down);
+    g.resid = x;
+    g.out_stride = d;
+    if ((rc = run_gemm(c.dtype, EPI_RESID, g, st))) return rc;
+
+    if (hidden_out) {
+      DF_HIP(hipMemcpy2DAsync(hidden_out + (size_t)l * B * d, (size_t)L * B * d * 4, x,
+                              (size_t)B * d * 4, (size_t)B * d * 4, batch,
+                              hipMemcpyDeviceToDevice, st));
+    }
+  }
+
+  const int R = batch * (B - 1);
+  if (R > 0) {
+    prof_begin(DFLASH_K_RMSNORM, 0, 0, st);
+    e = launch_rmsnorm(c.dtype, x, d, h->w.final_norm, ybuf, d, R, d, c.rms_eps, B - 1, B, 1, st);
+    prof_end(st);
+    if (e != hipSuccess) return DFLASH_ERR_HIP;
+    GemmArgs g = gemm_base(ybuf, d, R, c.vocab, d);
+    one_seg(g, h->w.lm_head);
+    g.amax = amax;
+    g.amax_stride = P.n_vtiles;
+    g.logits = logits;
+    g.logits_stride = c.vocab;
+    if ((rc = run_gemm(c.dtype, EPI_ARGMAX, g, st))) return rc;
+    prof_begin(DFLASH_K_SMALL, 0, 0, st);
+    e = launch_argmax_reduce(amax, P.n_vtiles, P.n_vtiles, R, draft_tokens, st);
+    prof_end(st);
+    if (e != hipSuccess) return DFLASH_ERR_HIP;
+  }
+  if (target_tokens) {
+    prof_begin(DFLASH_K_SMALL, 0, 0, st);
+    e = launch_accept(draft_tokens, target_tokens, batch, B, accept_len, bonus, nullptr, st);
+    prof_end(st);
+    if (e != hipSuccess) return DFLASH_ERR_HIP;
+  }
+  return DFLASH_OK;
+}
+
+int32_t dflash_accept(const int32_t* draft_tokens, const int32_t* target_tokens, int32_t batch,
+                      int32_t block_size, int32_t* accept_len, int32_t* bonus,
+                      int32_t* anchor_out, void* stream) {
+  if (batch < 0 || block_size < 1) return DFLASH_ERR_SHAPE;
+  if (batch == 0) return DFLASH_OK;
+  if (!target_tokens || !accept_len || !bonus) return DFLASH_ERR_NULL;
+  if (block_size > 1 && !draft_tokens) return DFLASH_ERR_NULL;
+  hipStream_t st = (hipStream_t)stream;
+  prof_begin(DFLASH_K_SMALL, 0, 0, st);
+  hipError_t e = launch_accept(draft_tokens, target_tokens, batch, block_size, accept_len, bonus,
+                               anchor_out, st);
+  prof_end(st);
+  return e == hipSuccess ? DFLASH_OK : DFLASH_ERR_HIP;
+}
+
+int32_t dflash_profiler_start(int32_t max_launches) {
+  if (max_launches < 1) return DFLASH_ERR_SHAPE;
+  if (g_prof_on) return DFLASH_ERR_STATE;
+  const size_t need = 2 * (size_t)max_launches;
+  while (g_pool.size() < need) {
+    hipEvent_t ev;
+    if (hipEventCreate(&ev) != hipSuccess) return DFLASH_ERR_HIP;
+    g_pool.push_back(ev);
+  }
+  g_prof_on = true;
+  return DFLASH_OK;
+}
+
+int32_t dflash_profiler_stop(void) {
+  g_prof_on = false;
+  g_open = -1;
+  return DFLASH_OK;
+}
+
+int32_t dflash_profiler_read(int32_t kind, int64_t* launches, double* total_ms, double* total_bytes,
+                             double* total_flops) {
+  if (kind < 0 || kind >= DFLASH_K_NCLASSES) return DFLASH_ERR_SHAPE;
+  if (!launches || !total_ms || !total_bytes || !total_flops) return DFLASH_ERR_NULL;
+  int64_t n = 0;
+  double ms = 0, by = 0, fl = 0;
+  for (const ProfRec& r : g_rec) {
+    if (r.kind != kind || !r.closed) continue;
+    if (hipEventSynchronize(r.e1) != hipSuccess) return DFLASH_ERR_HIP;
+    float t = 0.f;
+    if (hipEventElapsedTime(&t, r.e0, r.e1) != hipSuccess) return DFLASH_ERR_HIP;
+    ++n;
+    ms += t;
+    by += r.bytes;
+    fl += r.flops;
+  }
+  *launches = n;
+  *total_ms = ms;
+  *total_bytes = by;
+  *total_flops = fl;
+  return DFLASH_OK;
+}
+
+int32_t dflash_profiler_reset(void) {
+  if (g_prof_on) return DFLASH_ERR_STATE;
+  g_rec.clear();
+  g_pool_next = 0;
+  for (hipEvent_t ev : g_pool) (void)hipEventDestroy(ev);
+  g_pool.clear();
+  return DFLASH_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,119 @@
+// Host-side launch interfaces shared by the library's translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "dflash.h"
+
+namespace dflash {
+
+constexpr int kMaxASeg = 8;    // K-segments of the GEMM A operand (fused target features)
+constexpr int kMaxWSeg = 32;   // N-segments of the GEMM weight operand (stacked projections)
+constexpr int kKeyBlock = 32;  // V cache position block
+constexpr int kMaxLayers = 16;
+
+enum Epilogue : int {
+  EPI_STORE_F32 = 0,  // out (fp32) = acc
+  EPI_RESID = 1,      // resid (fp32) += acc
+  EPI_SWIGLU = 2,     // out (model dtype) = SiLU(acc_gate) * acc_up
+  EPI_ARGMAX = 3,     // per-row (max, argmax) over the tile -> partial keys; optional fp32 logits
+};
+
+// Y[M, N] = A[M, K] · W[N, K]^T with a fused epilogue.
+//  A: row m, column k lives at a[k / a_seg_k] + m * a_stride + k % a_seg_k
+//     (a_nseg > 1 concatenates several [M, a_seg_k] matrices along k).
+//  W: output column n lives in segment s with w_row0[s] <= n < w_row0[s+1],
+//     row n - w_row0[s] of w[s] ([rows, K], row-major). For EPI_SWIGLU, w2
+//     holds the second (up) matrix with the same segmentation.
+struct GemmArgs {
+  const void* a[kMaxASeg];
+  int64_t a_stride;
+  int a_seg_k;
+  int a_nseg;
+  const void* w[kMaxWSeg];
+  const void* w2[kMaxWSeg];
+  int w_row0[kMaxWSeg + 1];
+  int w_nseg;
+  int M, N, K;
+  int k_per_wave;                 // K range per wave (multiple of the chunk)
+  void* out;                      // EPI_STORE_F32 (fp32) / EPI_SWIGLU (model dtype)
+  int64_t out_stride;
+  float* resid;                   // EPI_RESID
+  unsigned long long* amax;       // EPI_ARGMAX: [M][n_tiles] partial keys
+  int64_t amax_stride;
+  float* logits;                  // EPI_ARGMAX, optional
+  int64_t logits_stride;
+};
+
+// Launch the weight-streaming GEMM. flops/bytes are the algorithmic figures
+// recorded by the profiler.
+hipError_t launch_gemm(int dtype, int epi, const GemmArgs& args, hipStream_t st);
+
+struct AttnArgs {
+  const void* q;         // [batch][n_heads][16][head_dim] model dtype, rows >= B are zero
+  const void* k;         // this layer's K cache base: [cache_batch][Hkv][cap][hd]
+  const void* v;         // this layer's V cache base: [cache_batch][Hkv][cap/32][hd][32]
+  const int32_t* ctx_len;
+  int batch, n_heads, n_kv_heads, head_dim, block, cap;
+  int chunk;             // keys per work item (multiple of 32)
+  int max_chunks;        // ceil(cap / chunk)
+  float scale_log2;      // log2(e) / sqrt(head_dim)
+  float* part_o;         // [batch][Hkv][max_chunks][G][hd][16]
+  float* part_ml;        // [batch][Hkv][max_chunks][G][16][2]  (running max in log2 units, sum)
+  void* out;             // combine output: [batch*B][n_heads*hd] model dtype
+};
+
+hipError_t launch_attention(int dtype, const AttnArgs& a, hipStream_t st);
+
+// Per-head RMSNorm + RoPE of q/k and the K/V cache scatter.
+//  Forward mode (kv_rows == nullptr): src is the fused QKV output
+//   [batch*B][(Hq + 2*Hkv)*hd] fp32; q heads go to q_out ([batch][Hq][16][hd],
+//   rows B..15 zero-filled), k/v heads to cache position ctx_len[s] + i.
+//  Append mode: src is [n_tok][n_layers * 2 * Hkv * hd] fp32 (layer-major,
+//   K then V per layer); row r of sequence s goes to position
+//   ctx_len[s] + r - cu_new[s] of every layer.
+struct NormRopeArgs {
+  const float* src;
+  int64_t src_stride;
+  void* q_out;
+  void* k_cache;          // layer 0 base; layer stride = cache_batch*Hkv*cap*hd
+  void* v_cache;
+  const void* q_norm[kMaxLayers];   // per-layer gains [hd] (forward mode: only [0])
+  const void* k_norm[kMaxLayers];
+  const int32_t* ctx_len;
+  const int32_t* cu_new;  // append mode only
+  int32_t* dev_status;
+  int batch, cache_batch, n_heads, n_kv_heads, head_dim, block, cap, n_layers;
+  int n_tok;              // append mode
+  float eps;
+  float rope_theta;       // <= 0: no rotation
+};
+
+hipError_t launch_norm_rope_forward(int dtype, const NormRopeArgs& a, hipStream_t st);
+hipError_t launch_norm_rope_append(int dtype, const NormRopeArgs& a, hipStream_t st);
+
+// y[r] = RMSNorm(x[src_row(r)]) * gain, src_row(r) = (r / rpg) * grp_stride + grp_off + r % rpg.
+hipError_t launch_rmsnorm(int dtype, const float* x, int64_t x_stride, const void* gain, void* y,
+                          int64_t y_stride, int rows, int d, float eps, int rpg, int grp_stride,
+                          int grp_off, hipStream_t st);
+
+hipError_t launch_embed(int dtype, const void* embed, const int32_t* anchor, int batch, int block,
+                        int d, int vocab, int mask_id, float* x, int32_t* dev_status,
+                        hipStream_t st);
+
+hipError_t launch_argmax_reduce(const unsigned long long* amax, int64_t stride, int n_tiles,
+                                int rows, int32_t* tokens, hipStream_t st);
+
+hipError_t launch_accept(const int32_t* drafts, const int32_t* targets, int batch, int block,
+                         int32_t* accept_len, int32_t* bonus, int32_t* anchor_out,
+                         hipStream_t st);
+
+hipError_t launch_ctx_len_add(int32_t* ctx_len, const int32_t* cu_new, int batch, int n_tok,
+                              int cap, int32_t* dev_status, hipStream_t st);
+
+// Profiler hooks (api.hip).
+void prof_begin(int kind, double bytes, double flops, hipStream_t st);
+void prof_end(hipStream_t st);
+
+}  // namespace dflash

@@ -1,0 +1,218 @@
+/*
+ * dflash.h -- C ABI of the MI355X (gfx950) DFlash drafter library.
+ *
+ * One parallel forward pass of the DFlash block-diffusion drafter, as the
+ * pages describe it:
+ *   [W] "DFlash: Block Diffusion for Flash Speculative Decoding" (wikillm
+ *       summary: "Method" > Inference, "Paper vs code", and its decoding-loop
+ *       and draft-layer pseudocode);
+ *   [R] "DFlash: Why a Diffusion Drafter Can Accelerate an Autoregressive
+ *       Model" (technical review: sec. 4.1, sec. 5.1 eqs. 9-10, sec. 5.3).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Every tensor argument is CALLER-OWNED DEVICE MEMORY on the current HIP
+ *    device. The library never allocates, frees or retains device memory; it
+ *    only reads and writes the buffers it is given for the duration of the
+ *    call's kernels. Scratch space comes from the caller's workspace.
+ *  - Every compute call takes the caller's stream (a hipStream_t passed as
+ *    void*) and is asynchronous on it: it enqueues kernels and returns; it
+ *    never synchronises the device. Results are valid once the stream reaches
+ *    that point.
+ *  - Weights are row-major [out, in] (the Linear layout), all in the model
+ *    dtype (DFLASH_BF16 or DFLASH_FP32), norm gains included.
+ *  - Every device pointer must be 16-byte aligned.
+ *  - Return value: DFLASH_OK (0) or a negative dflash_status. Arguments are
+ *    validated on the host before anything is enqueued; a call that returns an
+ *    error has enqueued nothing (except DFLASH_ERR_HIP, which reports a launch
+ *    failure after earlier launches of the same call may have been enqueued).
+ *  - Conditions only the device can see (a context longer than the cache
+ *    capacity, a token id outside the vocabulary, inconsistent prefix offsets)
+ *    are clamped so that nothing is written out of bounds, and the matching
+ *    DFLASH_DEV_* bit is OR-ed into *dev_status when dev_status is non-NULL.
+ *  - A handle is immutable after dflash_create; concurrent calls with one
+ *    handle on different streams are safe when their workspaces and output
+ *    buffers differ.
+ */
+#ifndef DFLASH_H
+#define DFLASH_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum dflash_status {
+  DFLASH_OK = 0,
+  DFLASH_ERR_NULL = -1,          /* a required pointer is NULL */
+  DFLASH_ERR_SHAPE = -2,         /* a size is out of range or inconsistent */
+  DFLASH_ERR_DTYPE = -3,         /* unknown dtype */
+  DFLASH_ERR_ALIGN = -4,         /* a pointer or stride breaks 16-byte alignment */
+  DFLASH_ERR_WORKSPACE = -5,     /* workspace smaller than dflash_workspace_bytes() */
+  DFLASH_ERR_UNSUPPORTED = -6,   /* a configuration the kernels do not cover */
+  DFLASH_ERR_HIP = -7,           /* a HIP launch reported an error */
+  DFLASH_ERR_STATE = -8          /* profiler misuse */
+} dflash_status;
+
+typedef enum dflash_dtype { DFLASH_FP32 = 0, DFLASH_BF16 = 1 } dflash_dtype;
+
+/* Bits OR-ed into *dev_status by kernels that detect bad device-side data. */
+#define DFLASH_DEV_CAPACITY 1   /* ctx_len + new rows (or + block) exceeds capacity: rows dropped */
+#define DFLASH_DEV_TOKEN 2      /* a token id outside [0, vocab): clamped */
+#define DFLASH_DEV_OFFSETS 4    /* cu_new not monotone or not ending at n_tok: rows dropped */
+
+/* Drafter shape. Supported: head_dim 64 or 128; n_heads a multiple of
+ * n_kv_heads with n_heads/n_kv_heads <= 8; 1 <= block_size <= 16;
+ * 1 <= n_layers <= 16; hidden, intermediate, n_heads*head_dim and
+ * target_hidden multiples of 32 (bf16) / 16 (fp32); vocab >= 2.
+ * rope_theta <= 0 disables the rotary embedding. */
+typedef struct dflash_config {
+  int32_t hidden;
+  int32_t n_heads;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t n_layers;
+  int32_t intermediate;
+  int32_t n_target_feats;   /* number of target layers whose features are fused */
+  int32_t target_hidden;    /* width of each target feature */
+  int32_t vocab;
+  int32_t block_size;       /* B: anchor + B-1 mask slots */
+  int32_t mask_token_id;
+  int32_t dtype;            /* dflash_dtype */
+  float rms_eps;
+  float rope_theta;
+} dflash_config;
+
+/* One draft layer. Shapes (d = hidden, hd = head_dim, I = intermediate):
+ * in_norm/post_norm [d]; wq [n_heads*hd, d]; wk, wv [n_kv_heads*hd, d];
+ * q_norm, k_norm [hd]; wo [d, n_heads*hd]; w_gate, w_up [I, d]; w_down [d, I]. */
+typedef struct dflash_layer_weights {
+  const void *in_norm, *wq, *wk, *wv, *q_norm, *k_norm, *wo, *post_norm;
+  const void *w_gate, *w_up, *w_down;
+} dflash_layer_weights;
+
+/* embed, lm_head [vocab, d] (may alias); fc [d, n_target_feats*target_hidden];
+ * fc_norm, final_norm [d]; layers: host array of n_layers entries (copied by
+ * dflash_create; the device buffers it points to must outlive the handle). */
+typedef struct dflash_weights {
+  const void *embed, *lm_head, *fc, *fc_norm, *final_norm;
+  const dflash_layer_weights *layers;
+} dflash_weights;
+
+/* Per-layer context K/V cache, caller-owned, model dtype.
+ *   k: [n_layers][batch][n_kv_heads][capacity][head_dim]   (row per position)
+ *   v: [n_layers][batch][n_kv_heads][capacity/32][head_dim][32]
+ *      (positions grouped in blocks of 32; inside a block the 32 positions of
+ *      one channel are contiguous, so attention reads V channel-major)
+ *   ctx_len: device int32 [batch], number of valid positions per sequence.
+ * capacity must be a multiple of 32. Positions [ctx_len, ctx_len+block_size)
+ * are scratch for the draft forward, so a forward needs
+ * ctx_len + block_size <= capacity. */
+typedef struct dflash_kv_cache {
+  void *k;
+  void *v;
+  int32_t *ctx_len;
+  int32_t batch;
+  int32_t capacity;
+} dflash_kv_cache;
+
+typedef struct dflash_handle dflash_handle;
+
+/* Validate the shape and keep a copy of the weight pointers.
+ * Returns DFLASH_OK and *out, or an error with *out = NULL. */
+int32_t dflash_create(const dflash_config *cfg, const dflash_weights *w, dflash_handle **out);
+void dflash_destroy(dflash_handle *h);
+
+/* Bytes of workspace that every call below needs when batch <= max_batch,
+ * capacity <= the given capacity and n_tok <= max_tokens (ctx_project and
+ * ctx_kv_append). Returns a negative dflash_status on bad arguments. */
+int64_t dflash_workspace_bytes(const dflash_handle *h, int32_t max_batch, int32_t capacity,
+                               int32_t max_tokens);
+
+/* Target-context-feature fusion [R eq. 9; W "Method" step 1]:
+ *   ctx = RMSNorm(fc · concat(feats[0..n_target_feats-1]); fc_norm).
+ * feats: HOST array of n_target_feats device pointers, each [n_tok, target_hidden]
+ *        with a row stride of feat_row_stride ELEMENTS (multiple of 8).
+ * ctx_out: [n_tok, hidden], model dtype. n_tok >= 0 (0 is a no-op). */
+int32_t dflash_ctx_project(const dflash_handle *h, const void *const *feats,
+                           int64_t feat_row_stride, int32_t n_tok, void *ctx_out, void *ws,
+                           int64_t ws_bytes, void *stream);
+
+/* Context K/V injection [R eq. 10; W "Paper vs code" KV-injection bullet]:
+ * for every layer l and every new context row r of sequence s,
+ *   K = RoPE(headRMS(ctx_r · wk_l^T; k_norm_l), pos),  V = ctx_r · wv_l^T,
+ * stored at pos = ctx_len[s] + (r - cu_new[s]); afterwards
+ * ctx_len[s] += cu_new[s+1] - cu_new[s].
+ * ctx: [n_tok, hidden] model dtype (rows of all sequences, packed in order);
+ * cu_new: DEVICE int32 [cache->batch + 1] prefix offsets, cu_new[0] = 0,
+ *         cu_new[batch] = n_tok. */
+int32_t dflash_ctx_kv_append(const dflash_handle *h, const dflash_kv_cache *cache,
+                             const void *ctx, const int32_t *cu_new, int32_t n_tok,
+                             int32_t *dev_status, void *ws, int64_t ws_bytes, void *stream);
+
+/* One parallel drafter pass over batch sequences [W decoding-loop and
+ * draft-layer pseudocode; "Method" steps 2-3]:
+ *   block = [anchor[s], MASK x (B-1)] embedded with `embed`;
+ *   n_layers x { pre-norm, QKV, per-head q/k RMSNorm + RoPE at ctx_len[s]+i,
+ *                non-causal attention over [cached context ; block] K/V,
+ *                O + residual, post-norm, SwiGLU MLP + residual };
+ *   final RMSNorm of slots 1..B-1, LM head, greedy argmax (lowest id on ties).
+ * The cache is read; its scratch positions [ctx_len, ctx_len+B) are
+ * overwritten; ctx_len is not changed.
+ * anchor: device int32 [batch]; batch <= cache->batch.
+ * draft_tokens: device int32 [batch, B-1] (required).
+ * logits: optional fp32 [batch, B-1, vocab].
+ * hidden_out: optional fp32 [batch, n_layers, B, hidden]: residual stream
+ *             after each layer.
+ * target_tokens: optional device int32 [batch, B]; when given, accept_len and
+ *             bonus (device int32 [batch]) receive dflash_accept's result. */
+int32_t dflash_draft_forward(const dflash_handle *h, const dflash_kv_cache *cache,
+                             const int32_t *anchor, int32_t batch, int32_t *draft_tokens,
+                             float *logits, float *hidden_out, const int32_t *target_tokens,
+                             int32_t *accept_len, int32_t *bonus, int32_t *dev_status,
+                             void *ws, int64_t ws_bytes, void *stream);
+
+/* Greedy accept-prefix [W decoding-loop pseudocode; R sec. 4.1]:
+ *   accept_len[s] = number of leading i < B-1 with draft[s][i] == target[s][i],
+ *   bonus[s] = target[s][accept_len[s]]; anchor_out (optional) = bonus.
+ * draft_tokens [batch, B-1], target_tokens [batch, B], all device int32. */
+int32_t dflash_accept(const int32_t *draft_tokens, const int32_t *target_tokens, int32_t batch,
+                      int32_t block_size, int32_t *accept_len, int32_t *bonus,
+                      int32_t *anchor_out, void *stream);
+
+/* Static text for a dflash_status code. */
+const char *dflash_status_string(int32_t code);
+
+/* Kernel timing (benchmarking aid, process-wide, not thread-safe).
+ * dflash_profiler_start(n): from now on every library kernel launch is
+ * bracketed by HIP events on its own stream, up to n launches.
+ * dflash_profiler_stop(): stop recording (events are kept).
+ * dflash_profiler_read(kind, ...): waits for the recorded events and returns,
+ * for kernel class `kind` (see dflash_kernel_class), the number of launches,
+ * their summed duration in ms, and their summed algorithmic HBM bytes and
+ * flops (from the launch shapes). dflash_profiler_reset() frees the events. */
+typedef enum dflash_kernel_class {
+  DFLASH_K_GEMM_F32OUT = 0,  /* projections with an fp32 output: QKV, fusion, context K/V */
+  DFLASH_K_GEMM_RESID = 1,   /* projections added into the residual stream: O, down */
+  DFLASH_K_GEMM_SWIGLU = 2,  /* gate/up projection with the SwiGLU product */
+  DFLASH_K_LMHEAD = 3,       /* LM head with fused argmax */
+  DFLASH_K_ATTN = 4,         /* KV-injected attention partials */
+  DFLASH_K_ATTN_COMBINE = 5,
+  DFLASH_K_NORM_ROPE = 6,    /* per-head q/k RMSNorm + RoPE + cache scatter */
+  DFLASH_K_RMSNORM = 7,
+  DFLASH_K_SMALL = 8,        /* embedding, argmax reduce, accept, ctx_len update */
+  DFLASH_K_NCLASSES = 9
+} dflash_kernel_class;
+
+int32_t dflash_profiler_start(int32_t max_launches);
+int32_t dflash_profiler_stop(void);
+int32_t dflash_profiler_read(int32_t kind, int64_t *launches, double *total_ms,
+                             double *total_bytes, double *total_flops);
+int32_t dflash_profiler_reset(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DFLASH_H */

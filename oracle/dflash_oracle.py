@@ -189,7 +189,7 @@ def embed_block(anchor: int, weights, cfg) -> np.ndarray:
     """Block [anchor, MASK x (B-1)] embedded with the shared embedding table
     (input_embedding_scale 1.0) [W "Method" step 3, "Paper vs code"]."""
     ids = np.array([anchor] + [cfg.mask_token_id] * (cfg.block_size - 1))
-    return _f64(weights["embed"])[ids]
+    return _f64(np.asarray(weights["embed"])[ids])
 
 
 def kv_injected_attention(q, k_blk, v_blk, k_ctx, v_ctx, group: int) -> np.ndarray:

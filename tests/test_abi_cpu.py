@@ -1,0 +1,140 @@
+"""The C-ABI library without a GPU: it loads, exports every function that
+include/dflash.h declares, and rejects bad arguments on the host before it
+enqueues anything (no call here reaches a HIP launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from block_diffusion_drafter_amd import binding as B
+from synth import TINY_FP32, QWEN3_8B_SHAPED
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "dflash.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(dflash_[a-z_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_function():
+    names = header_functions()
+    assert len(names) >= 12, names
+    lib = B.lib()
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_status_strings():
+    lib = B.lib()
+    for code in range(0, -9, -1):
+        s = lib.dflash_status_string(code).decode()
+        assert s and s != "unknown status", code
+    assert lib.dflash_status_string(-99).decode() == "unknown status"
+
+
+FAKE = 1 << 20  # a 16-byte-aligned non-null address; never dereferenced here
+
+
+def fake_weights(n_layers):
+    layers = (B.LayerWeights * n_layers)()
+    for l in range(n_layers):
+        for f in B.LAYER_FIELDS:
+            setattr(layers[l], f, FAKE)
+    w = B.WeightsStruct(FAKE, FAKE, FAKE, FAKE, FAKE,
+                        ctypes.cast(layers, ctypes.POINTER(B.LayerWeights)))
+    return w, layers
+
+
+def create(cfg_struct, n_layers=None):
+    w, layers = fake_weights(n_layers if n_layers is not None else max(1, cfg_struct.n_layers))
+    h = ctypes.c_void_p()
+    rc = B.lib().dflash_create(ctypes.byref(cfg_struct), ctypes.byref(w), ctypes.byref(h))
+    return rc, h
+
+
+@pytest.mark.parametrize("cfg", [TINY_FP32, QWEN3_8B_SHAPED], ids=lambda c: c.name)
+def test_create_and_workspace(cfg):
+    rc, h = create(B.make_config(cfg))
+    assert rc == 0 and h.value
+    lib = B.lib()
+    n1 = lib.dflash_workspace_bytes(h, 1, 2080, 16)
+    n32 = lib.dflash_workspace_bytes(h, 32, 8224, 512)
+    assert 0 < n1 < n32
+    assert lib.dflash_workspace_bytes(h, 0, 64, 0) == -2
+    assert lib.dflash_workspace_bytes(None, 1, 64, 0) == -1
+    lib.dflash_destroy(h)
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("dtype", 7, -3), ("head_dim", 96, -6), ("block_size", 17, -6), ("block_size", 0, -6),
+    ("n_kv_heads", 3, -2), ("hidden", 250, -2), ("mask_token_id", 1000, -2),
+    ("n_layers", 17, -6), ("vocab", 1, -2)])
+def test_create_rejects_bad_config(field, value, code):
+    c = B.make_config(TINY_FP32)
+    setattr(c, field, value)
+    rc, h = create(c, n_layers=1)
+    assert rc == code and not h.value
+
+
+def test_create_rejects_null_and_misaligned_weights():
+    c = B.make_config(TINY_FP32)
+    w, layers = fake_weights(1)
+    layers[0].wq = None
+    h = ctypes.c_void_p()
+    assert B.lib().dflash_create(ctypes.byref(c), ctypes.byref(w), ctypes.byref(h)) == -1
+    layers[0].wq = FAKE + 4
+    assert B.lib().dflash_create(ctypes.byref(c), ctypes.byref(w), ctypes.byref(h)) == -4
+    assert B.lib().dflash_create(ctypes.byref(c), ctypes.byref(w), None) == -1
+
+
+def test_calls_reject_bad_arguments_before_launching():
+    lib = B.lib()
+    rc, h = create(B.make_config(TINY_FP32))
+    assert rc == 0
+    cache = B.KVCacheStruct(FAKE, FAKE, FAKE, 2, 64)
+    bad_cap = B.KVCacheStruct(FAKE, FAKE, FAKE, 2, 48)
+    no_k = B.KVCacheStruct(None, FAKE, FAKE, 2, 64)
+    ws_need = lib.dflash_workspace_bytes(h, 1, 64, 0)
+    fwd = lambda c, batch=1, ws=FAKE, wsb=ws_need, drafts=FAKE: lib.dflash_draft_forward(
+        h, ctypes.byref(c), FAKE, batch, drafts, None, None, None, None, None, None, ws, wsb, None)
+    assert fwd(bad_cap) == -2
+    assert fwd(no_k) == -1
+    assert fwd(cache, batch=3) == -2
+    assert fwd(cache, batch=0) == -2
+    assert fwd(cache, wsb=ws_need - 1) == -5
+    assert fwd(cache, ws=FAKE + 8) == -4
+    assert fwd(cache, drafts=None) == -1
+    # fused accept needs both outputs
+    assert lib.dflash_draft_forward(h, ctypes.byref(cache), FAKE, 1, FAKE, None, None, FAKE,
+                                    None, FAKE, None, FAKE, ws_need, None) == -1
+    # append: misaligned ctx, too-small workspace, negative rows
+    assert lib.dflash_ctx_kv_append(h, ctypes.byref(cache), FAKE + 2, FAKE, 4, None, FAKE,
+                                    1 << 30, None) == -4
+    assert lib.dflash_ctx_kv_append(h, ctypes.byref(cache), FAKE, FAKE, 4, None, FAKE, 16,
+                                    None) == -5
+    assert lib.dflash_ctx_kv_append(h, ctypes.byref(cache), FAKE, FAKE, -1, None, FAKE, 16,
+                                    None) == -2
+    # project: bad stride, null feature pointer
+    feats = (ctypes.c_void_p * 3)(FAKE, FAKE, None)
+    assert lib.dflash_ctx_project(h, feats, 256, 4, FAKE, FAKE, 1 << 30, None) == -1
+    feats = (ctypes.c_void_p * 3)(FAKE, FAKE, FAKE)
+    assert lib.dflash_ctx_project(h, feats, 100, 4, FAKE, FAKE, 1 << 30, None) == -2
+    assert lib.dflash_ctx_project(h, feats, 256, 0, None, None, 0, None) == 0  # no-op
+    # accept
+    assert lib.dflash_accept(FAKE, None, 2, 4, FAKE, FAKE, None, None) == -1
+    assert lib.dflash_accept(FAKE, FAKE, -1, 4, FAKE, FAKE, None, None) == -2
+    assert lib.dflash_accept(None, None, 0, 4, None, None, None, None) == 0
+    lib.dflash_destroy(h)
+
+
+def test_profiler_state_machine():
+    lib = B.lib()
+    assert lib.dflash_profiler_read(99, None, None, None, None) == -2
+    n = ctypes.c_int64()
+    d = ctypes.c_double()
+    assert lib.dflash_profiler_read(0, ctypes.byref(n), ctypes.byref(d), ctypes.byref(d),
+                                    ctypes.byref(d)) == 0
+    assert n.value == 0
