@@ -53,14 +53,15 @@ __device__ __forceinline__ f32x4 mfma_frag<bf16>(u32x4 a, u32x4 b, f32x4 acc) {
 
 template <>
 __device__ __forceinline__ f32x4 mfma_frag<float>(u32x4 a, u32x4 b, f32x4 acc) {
-  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__builtin_bit_cast(float, a.x),
-                                             __builtin_bit_cast(float, b.x), acc, 0, 0, 0);
-  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__builtin_bit_cast(float, a.y),
-                                             __builtin_bit_cast(float, b.y), acc, 0, 0, 0);
-  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__builtin_bit_cast(float, a.z),
-                                             __builtin_bit_cast(float, b.z), acc, 0, 0, 0);
-  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__builtin_bit_cast(float, a.w),
-                                             __builtin_bit_cast(float, b.w), acc, 0, 0, 0);
+  // Reinterpret the whole vector, then index it: bit-casting single elements
+  // of an ext-vector (bit_cast<float>(a.y)) is folded to element 0 by this
+  // compiler, which silently drops three quarters of the products.
+  const f32x4 af = __builtin_bit_cast(f32x4, a);
+  const f32x4 bf = __builtin_bit_cast(f32x4, b);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(af[0], bf[0], acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(af[1], bf[1], acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(af[2], bf[2], acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(af[3], bf[3], acc, 0, 0, 0);
   return acc;
 }
 
