@@ -79,7 +79,7 @@ def lib() -> ctypes.CDLL:
         L.dflash_accept.restype = i32
         L.dflash_accept.argtypes = [vp, vp, i32, i32, vp, vp, vp, vp]
         L.dflash_profiler_start.restype = i32
-        L.dflash_profiler_start.argtypes = [i32]
+        L.dflash_profiler_start.argtypes = [i32, ctypes.c_uint32]
         L.dflash_profiler_stop.restype = i32
         L.dflash_profiler_read.restype = i32
         L.dflash_profiler_read.argtypes = [i32, ctypes.POINTER(i64),
@@ -254,8 +254,13 @@ def accept(draft_tokens: torch.Tensor, target_tokens: torch.Tensor, block_size: 
                                _stream()), "dflash_accept")
 
 
-def profiler_start(max_launches: int = 100000) -> None:
-    _check(lib().dflash_profiler_start(max_launches), "dflash_profiler_start")
+def profiler_start(max_launches: int = 100000, classes: Optional[List[str]] = None) -> None:
+    """Bracket library launches with HIP events; ``classes`` limits it to some
+    kernel classes (names from KERNEL_CLASSES), None means all."""
+    mask = 0
+    for c in (classes or []):
+        mask |= 1 << KERNEL_CLASSES.index(c)
+    _check(lib().dflash_profiler_start(max_launches, mask), "dflash_profiler_start")
 
 
 def profiler_stop() -> None:

@@ -30,10 +30,12 @@ static std::vector<ProfRec> g_rec;
 static std::vector<hipEvent_t> g_pool;
 static size_t g_pool_next = 0;
 static bool g_prof_on = false;
+static uint32_t g_prof_mask = 0xFFFFFFFFu;
 static int g_open = -1;
 
 void prof_begin(int kind, double bytes, double flops, hipStream_t st) {
-  if (!g_prof_on || g_pool_next + 2 > g_pool.size()) return;
+  g_open = -1;
+  if (!g_prof_on || !((g_prof_mask >> kind) & 1u) || g_pool_next + 2 > g_pool.size()) return;
   ProfRec r{kind, bytes, flops, g_pool[g_pool_next], g_pool[g_pool_next + 1], false};
   g_pool_next += 2;
   if (hipEventRecord(r.e0, st) != hipSuccess) return;
@@ -70,14 +72,14 @@ struct Plan {
   size_t total;
 };
 
-// Keys per attention work item: aim for ~2048 items over the cache so every
-// CU has several, but never below 64 keys (partials would rival the K/V
-// stream) nor above 2048.
-int choose_chunk(int batch, int hkv, int cap) {
-  long long keys = (long long)batch * hkv * cap;
-  long long c = (keys + 2047) / 2048;
-  c = (c + 31) / 32 * 32;
-  c = std::max(64LL, std::min(2048LL, c));
+// Keys per attention work item (one workgroup of G waves): aim for ~2048
+// waves over the whole cache, but keep chunks >= 256 keys so the fp32
+// partials (64 rows x head_dim per chunk) stay small next to the K/V stream,
+// and <= 1024 keys.
+int choose_chunk(int batch, int hkv, int group, int cap) {
+  long long waves_if_32 = (long long)batch * hkv * group * ((cap + 31) / 32);
+  long long c = 32 * ((waves_if_32 + 2047) / 2048);
+  c = std::max(256LL, std::min(1024LL, c));
   return (int)c;
 }
 
@@ -96,7 +98,7 @@ Plan make_plan(const dflash_config& c, int batch, int cap, int max_tokens) {
   p.h = take(M * d * es);
   p.qkv = take(M * (Hq + 2 * Hkv) * hd * 4);
   p.q = take((size_t)batch * Hq * 16 * hd * es);
-  p.chunk = choose_chunk(batch, (int)Hkv, cap);
+  p.chunk = choose_chunk(batch, (int)Hkv, (int)G, cap);
   p.max_chunks = (cap + p.chunk - 1) / p.chunk;
   p.po = take((size_t)batch * Hkv * p.max_chunks * G * hd * 16 * 4);
   p.pml = take((size_t)batch * Hkv * p.max_chunks * G * 16 * 2 * 4);
@@ -104,7 +106,8 @@ Plan make_plan(const dflash_config& c, int batch, int cap, int max_tokens) {
   p.act = take(M * I * es);
   const size_t R = (size_t)batch * (B - 1);
   p.y = take(R * d * es);
-  p.n_vtiles = (c.vocab + 15) / 16;
+  // LM head: one (max, argmax) key per row and workgroup column.
+  p.n_vtiles = R > 0 ? plan_gemm(c.dtype, EPI_ARGMAX, (int)R, c.vocab, c.hidden, 0).grid_x : 1;
   p.amax = take(R * p.n_vtiles * 8);
   p.fwd_end = off;
   off = 0;
@@ -131,6 +134,9 @@ int32_t check_config(const dflash_config& c) {
   if (c.n_layers > kMaxLayers) return DFLASH_ERR_UNSUPPORTED;
   if (c.n_target_feats > kMaxASeg) return DFLASH_ERR_UNSUPPORTED;
   if (c.hidden % mult || c.intermediate % mult || c.target_hidden % mult) return DFLASH_ERR_SHAPE;
+  // Fused features are separate A segments; a 256-byte GEMM chunk must not straddle two.
+  if (c.n_target_feats > 1 && c.target_hidden % (c.dtype == DFLASH_BF16 ? 128 : 64))
+    return DFLASH_ERR_SHAPE;
   if (c.mask_token_id < 0 || c.mask_token_id >= c.vocab) return DFLASH_ERR_SHAPE;
   if (!(c.rms_eps >= 0.f) || !std::isfinite(c.rms_eps)) return DFLASH_ERR_SHAPE;
   if (!std::isfinite(c.rope_theta)) return DFLASH_ERR_SHAPE;
@@ -383,16 +389,18 @@ int32_t dflash_draft_forward(const dflash_handle* h, const dflash_kv_cache* cach
 
   prof_begin(DFLASH_K_SMALL, 0, 0, st);
   hipError_t e = launch_embed(c.dtype, h->w.embed, anchor, batch, B, d, c.vocab, c.mask_token_id,
-                              x, dev_status, st);
+                              x, h->layers[0].in_norm, c.rms_eps, hbuf, dev_status, st);
   prof_end(st);
   if (e != hipSuccess) return DFLASH_ERR_HIP;
 
   for (int l = 0; l < L; ++l) {
     const dflash_layer_weights& lw = h->layers[l];
-    prof_begin(DFLASH_K_RMSNORM, 0, 0, st);
-    e = launch_rmsnorm(c.dtype, x, d, lw.in_norm, hbuf, d, M, d, c.rms_eps, M, 0, 0, st);
-    prof_end(st);
-    if (e != hipSuccess) return DFLASH_ERR_HIP;
+    if (l > 0) {  // layer 0's pre-norm came with the embedding
+      prof_begin(DFLASH_K_RMSNORM, 0, 0, st);
+      e = launch_rmsnorm(c.dtype, x, d, lw.in_norm, hbuf, d, M, d, c.rms_eps, M, 0, 0, st);
+      prof_end(st);
+      if (e != hipSuccess) return DFLASH_ERR_HIP;
+    }
 
     const int Nqkv = (Hq + 2 * Hkv) * hd;
     GemmArgs g = gemm_base(hbuf, d, M, Nqkv, d);
@@ -501,11 +509,11 @@ int32_t dflash_draft_forward(const dflash_handle* h, const dflash_kv_cache* cach
     g.logits_stride = c.vocab;
     if ((rc = run_gemm(c.dtype, EPI_ARGMAX, g, st))) return rc;
     prof_begin(DFLASH_K_SMALL, 0, 0, st);
-    e = launch_argmax_reduce(amax, P.n_vtiles, P.n_vtiles, R, draft_tokens, st);
+    e = launch_argmax_accept(amax, P.n_vtiles, P.n_vtiles, batch, B, draft_tokens, target_tokens,
+                             accept_len, bonus, st);
     prof_end(st);
     if (e != hipSuccess) return DFLASH_ERR_HIP;
-  }
-  if (target_tokens) {
+  } else if (target_tokens) {  // B == 1: nothing drafted, the bonus is the first target
     prof_begin(DFLASH_K_SMALL, 0, 0, st);
     e = launch_accept(draft_tokens, target_tokens, batch, B, accept_len, bonus, nullptr, st);
     prof_end(st);
@@ -529,9 +537,10 @@ int32_t dflash_accept(const int32_t* draft_tokens, const int32_t* target_tokens,
   return e == hipSuccess ? DFLASH_OK : DFLASH_ERR_HIP;
 }
 
-int32_t dflash_profiler_start(int32_t max_launches) {
+int32_t dflash_profiler_start(int32_t max_launches, uint32_t class_mask) {
   if (max_launches < 1) return DFLASH_ERR_SHAPE;
   if (g_prof_on) return DFLASH_ERR_STATE;
+  g_prof_mask = class_mask ? class_mask : 0xFFFFFFFFu;
   const size_t need = 2 * (size_t)max_launches;
   while (g_pool.size() < need) {
     hipEvent_t ev;

@@ -8,7 +8,7 @@
 
 namespace dflash {
 
-__device__ __forceinline__ float block_sum_256(float v, float* sh) {
+__device__ __forceinline__ float block_sum(float v, float* sh) {
   v = wave_sum(v);
   const int w = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 0) sh[w] = v;
@@ -18,41 +18,98 @@ __device__ __forceinline__ float block_sum_256(float v, float* sh) {
   return t;
 }
 
+// Four consecutive gain values as fp32.
+template <typename T> __device__ __forceinline__ float4 load4(const T* g);
+template <> __device__ __forceinline__ float4 load4<float>(const float* g) {
+  return *reinterpret_cast<const float4*>(g);
+}
+template <> __device__ __forceinline__ float4 load4<bf16>(const bf16* g) {
+  const uint2 u = *reinterpret_cast<const uint2*>(g);
+  return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xFFFF0000u),
+                     __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xFFFF0000u));
+}
+
+template <typename T> __device__ __forceinline__ void store4(T* y, float4 v);
+template <> __device__ __forceinline__ void store4<float>(float* y, float4 v) {
+  *reinterpret_cast<float4*>(y) = v;
+}
+template <> __device__ __forceinline__ void store4<bf16>(bf16* y, float4 v) {
+  y[0] = (bf16)v.x;
+  y[1] = (bf16)v.y;
+  y[2] = (bf16)v.z;
+  y[3] = (bf16)v.w;
+}
+
+// One row per workgroup, VPT float4 per thread held in registers: one load
+// pass, one block reduction, one store pass (d <= 4 * 256 * VPT).
+template <typename T, int VPT>
+__device__ __forceinline__ void rmsnorm_row(const float* xr, const T* gain, T* yr, int d, float eps,
+                                            float* sh) {
+  float4 v[VPT];
+  float ss = 0.f;
+#pragma unroll
+  for (int u = 0; u < VPT; ++u) {
+    const int k = 4 * (threadIdx.x + u * blockDim.x);
+    v[u] = k < d ? *reinterpret_cast<const float4*>(xr + k) : make_float4(0.f, 0.f, 0.f, 0.f);
+    ss += v[u].x * v[u].x + v[u].y * v[u].y + v[u].z * v[u].z + v[u].w * v[u].w;
+  }
+  ss = block_sum(ss, sh);
+  const float inv = rsqrtf(ss / (float)d + eps);
+#pragma unroll
+  for (int u = 0; u < VPT; ++u) {
+    const int k = 4 * (threadIdx.x + u * blockDim.x);
+    if (k < d) {
+      const float4 g = load4<T>(gain + k);
+      store4<T>(yr + k, make_float4(v[u].x * inv * g.x, v[u].y * inv * g.y, v[u].z * inv * g.z,
+                                    v[u].w * inv * g.w));
+    }
+  }
+}
+
 // y[r] = x[src(r)] / sqrt(mean(x^2) + eps) * gain, statistics in fp32.
-template <typename T>
+template <typename T, int VPT>
 __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* x, int64_t xs, const T* gain,
                                                       T* y, int64_t ys, int d, float eps, int rpg,
                                                       int grp_stride, int grp_off) {
   __shared__ float sh[4];
   const int r = blockIdx.x;
   const int64_t src = (int64_t)(r / rpg) * grp_stride + grp_off + r % rpg;
-  const float* xr = x + src * xs;
-  T* yr = y + (int64_t)r * ys;
-  float ss = 0.f;
-  for (int k = threadIdx.x; k < d; k += blockDim.x) ss += xr[k] * xr[k];
-  ss = block_sum_256(ss, sh);
-  const float inv = rsqrtf(ss / (float)d + eps);
-  for (int k = threadIdx.x; k < d; k += blockDim.x) yr[k] = from_f32<T>(xr[k] * inv * to_f32(gain[k]));
+  rmsnorm_row<T, VPT>(x + src * xs, gain, y + (int64_t)r * ys, d, eps, sh);
+}
+
+template <typename T>
+static void launch_rmsnorm_t(const float* x, int64_t xs, const T* g, T* y, int64_t ys, int rows,
+                             int d, float eps, int rpg, int gs, int go, hipStream_t st) {
+  const int vpt = (d + 1023) / 1024;
+  dim3 grid(rows), block(256);
+  if (vpt <= 1) hipLaunchKernelGGL((rmsnorm_kernel<T, 1>), grid, block, 0, st, x, xs, g, y, ys, d, eps, rpg, gs, go);
+  else if (vpt <= 2) hipLaunchKernelGGL((rmsnorm_kernel<T, 2>), grid, block, 0, st, x, xs, g, y, ys, d, eps, rpg, gs, go);
+  else if (vpt <= 4) hipLaunchKernelGGL((rmsnorm_kernel<T, 4>), grid, block, 0, st, x, xs, g, y, ys, d, eps, rpg, gs, go);
+  else hipLaunchKernelGGL((rmsnorm_kernel<T, 8>), grid, block, 0, st, x, xs, g, y, ys, d, eps, rpg, gs, go);
 }
 
 hipError_t launch_rmsnorm(int dtype, const float* x, int64_t x_stride, const void* gain, void* y,
                           int64_t y_stride, int rows, int d, float eps, int rpg, int grp_stride,
                           int grp_off, hipStream_t st) {
   if (rows <= 0) return hipSuccess;
+  if (d > 8192 || d % 4) return hipErrorInvalidValue;
   if (dtype == DFLASH_BF16)
-    hipLaunchKernelGGL(rmsnorm_kernel<bf16>, dim3(rows), dim3(256), 0, st, x, x_stride,
-                       (const bf16*)gain, (bf16*)y, y_stride, d, eps, rpg, grp_stride, grp_off);
+    launch_rmsnorm_t<bf16>(x, x_stride, (const bf16*)gain, (bf16*)y, y_stride, rows, d, eps, rpg,
+                           grp_stride, grp_off, st);
   else
-    hipLaunchKernelGGL(rmsnorm_kernel<float>, dim3(rows), dim3(256), 0, st, x, x_stride,
-                       (const float*)gain, (float*)y, y_stride, d, eps, rpg, grp_stride, grp_off);
+    launch_rmsnorm_t<float>(x, x_stride, (const float*)gain, (float*)y, y_stride, rows, d, eps,
+                            rpg, grp_stride, grp_off, st);
   return hipGetLastError();
 }
 
-// x[s*B + i] = E[i == 0 ? anchor[s] : mask] (input_embedding_scale 1).
-template <typename T>
+// x[s*B + i] = E[i == 0 ? anchor[s] : mask] (input_embedding_scale 1), and the
+// first layer's pre-norm of that row, h = RMSNorm(x; gain).
+template <typename T, int VPT>
 __global__ __launch_bounds__(256) void embed_kernel(const T* E, const int32_t* anchor, int block,
                                                     int d, int vocab, int mask_id, float* x,
+                                                    const T* gain, float eps, T* h,
                                                     int32_t* dev_status) {
+  __shared__ float sh[4];
   const int row = blockIdx.x, s = row / block, i = row % block;
   int id = i == 0 ? anchor[s] : mask_id;
   if (id < 0 || id >= vocab) {
@@ -61,18 +118,32 @@ __global__ __launch_bounds__(256) void embed_kernel(const T* E, const int32_t* a
   }
   const T* e = E + (int64_t)id * d;
   float* xr = x + (int64_t)row * d;
-  for (int k = threadIdx.x; k < d; k += blockDim.x) xr[k] = to_f32(e[k]);
+#pragma unroll
+  for (int u = 0; u < VPT; ++u) {
+    const int k = 4 * (threadIdx.x + u * blockDim.x);
+    if (k < d) *reinterpret_cast<float4*>(xr + k) = load4<T>(e + k);
+  }
+  __syncthreads();
+  rmsnorm_row<T, VPT>(xr, gain, h + (int64_t)row * d, d, eps, sh);
 }
 
 hipError_t launch_embed(int dtype, const void* embed, const int32_t* anchor, int batch, int block,
-                        int d, int vocab, int mask_id, float* x, int32_t* dev_status,
-                        hipStream_t st) {
-  if (dtype == DFLASH_BF16)
-    hipLaunchKernelGGL(embed_kernel<bf16>, dim3(batch * block), dim3(256), 0, st,
-                       (const bf16*)embed, anchor, block, d, vocab, mask_id, x, dev_status);
-  else
-    hipLaunchKernelGGL(embed_kernel<float>, dim3(batch * block), dim3(256), 0, st,
-                       (const float*)embed, anchor, block, d, vocab, mask_id, x, dev_status);
+                        int d, int vocab, int mask_id, float* x, const void* gain, float eps,
+                        void* h, int32_t* dev_status, hipStream_t st) {
+  if (d > 8192 || d % 4) return hipErrorInvalidValue;
+  const int vpt = (d + 1023) / 1024;
+  dim3 grid(batch * block), blk(256);
+#define DF_EMBED(T, V)                                                                            \
+  hipLaunchKernelGGL((embed_kernel<T, V>), grid, blk, 0, st, (const T*)embed, anchor, block, d,   \
+                     vocab, mask_id, x, (const T*)gain, eps, (T*)h, dev_status)
+  if (dtype == DFLASH_BF16) {
+    if (vpt <= 1) DF_EMBED(bf16, 1); else if (vpt <= 2) DF_EMBED(bf16, 2);
+    else if (vpt <= 4) DF_EMBED(bf16, 4); else DF_EMBED(bf16, 8);
+  } else {
+    if (vpt <= 1) DF_EMBED(float, 1); else if (vpt <= 2) DF_EMBED(float, 2);
+    else if (vpt <= 4) DF_EMBED(float, 4); else DF_EMBED(float, 8);
+  }
+#undef DF_EMBED
   return hipGetLastError();
 }
 
@@ -253,33 +324,53 @@ hipError_t launch_norm_rope_append(int dtype, const NormRopeArgs& a, hipStream_t
   return launch_nr<1>(dtype, a, dim3(a.n_layers * 2 * a.n_kv_heads, a.n_tok), st);
 }
 
-__global__ __launch_bounds__(256) void argmax_reduce_kernel(const unsigned long long* amax,
-                                                            int64_t stride, int n_tiles,
-                                                            int32_t* tokens) {
-  __shared__ unsigned long long sh[256];
-  const int row = blockIdx.x;
-  unsigned long long best = 0ull;
-  for (int t = threadIdx.x; t < n_tiles; t += blockDim.x) {
-    const unsigned long long k = amax[(int64_t)row * stride + t];
-    best = k > best ? k : best;
-  }
-  sh[threadIdx.x] = best;
-  __syncthreads();
-  for (int o = blockDim.x / 2; o > 0; o >>= 1) {
-    if ((int)threadIdx.x < o) {
-      const unsigned long long k = sh[threadIdx.x + o];
-      if (k > sh[threadIdx.x]) sh[threadIdx.x] = k;
+// Per sequence: wave i reduces row i's per-workgroup (max, argmax) keys into
+// draft token i; then, when targets are given, one thread applies the greedy
+// accept rule to the sequence's drafts.
+__global__ __launch_bounds__(1024) void argmax_accept_kernel(const unsigned long long* amax,
+                                                             int64_t stride, int n_cols, int block,
+                                                             int32_t* drafts,
+                                                             const int32_t* targets,
+                                                             int32_t* accept_len, int32_t* bonus) {
+  __shared__ int32_t dsh[16];
+  const int s = blockIdx.x, m = block - 1;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (wave < m) {
+    const int row = s * m + wave;
+    const unsigned long long* keys = amax + (int64_t)row * stride;
+    unsigned long long best = 0ull;
+#pragma unroll 8
+    for (int c = lane; c < n_cols; c += 64) {
+      const unsigned long long k = keys[c];
+      best = k > best ? k : best;
     }
-    __syncthreads();
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const unsigned long long other = __shfl_xor(best, o);
+      best = other > best ? other : best;
+    }
+    if (lane == 0) {
+      const int32_t tok = (int32_t)argmax_index(best);
+      drafts[row] = tok;
+      dsh[wave] = tok;
+    }
   }
-  if (threadIdx.x == 0) tokens[row] = (int32_t)argmax_index(sh[0]);
+  __syncthreads();
+  if (targets && threadIdx.x == 0) {
+    const int32_t* t = targets + (int64_t)s * block;
+    int a = 0;
+    while (a < m && dsh[a] == t[a]) ++a;
+    accept_len[s] = a;
+    bonus[s] = t[a];
+  }
 }
 
-hipError_t launch_argmax_reduce(const unsigned long long* amax, int64_t stride, int n_tiles,
-                                int rows, int32_t* tokens, hipStream_t st) {
-  if (rows <= 0) return hipSuccess;
-  hipLaunchKernelGGL(argmax_reduce_kernel, dim3(rows), dim3(256), 0, st, amax, stride, n_tiles,
-                     tokens);
+hipError_t launch_argmax_accept(const unsigned long long* amax, int64_t stride, int n_cols,
+                                int batch, int block, int32_t* drafts, const int32_t* targets,
+                                int32_t* accept_len, int32_t* bonus, hipStream_t st) {
+  if (batch <= 0 || block < 2 || block > 17) return block == 1 ? hipSuccess : hipErrorInvalidValue;
+  hipLaunchKernelGGL(argmax_accept_kernel, dim3(batch), dim3(1024), 0, st, amax, stride, n_cols,
+                     block, drafts, targets, accept_len, bonus);
   return hipGetLastError();
 }
 

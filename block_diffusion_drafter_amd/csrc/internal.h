@@ -46,8 +46,16 @@ struct GemmArgs {
   int64_t logits_stride;
 };
 
-// Launch the weight-streaming GEMM. flops/bytes are the algorithmic figures
-// recorded by the profiler.
+// Launch geometry of one weight-streaming GEMM (also used to size LM-head partials).
+struct GemmPlan {
+  int mt, nt;           // 16-row m-tiles and 16-column n-tiles per workgroup
+  int grid_x, grid_y;
+  int ksplit;           // waves per workgroup, each taking k_per_wave of K
+  int k_per_wave;
+  size_t lds;
+};
+// a_seg_k: width of each A segment when A is several matrices side by side, else 0.
+GemmPlan plan_gemm(int dtype, int epi, int M, int N, int K, int a_seg_k);
 hipError_t launch_gemm(int dtype, int epi, const GemmArgs& args, hipStream_t st);
 
 struct AttnArgs {
@@ -61,7 +69,8 @@ struct AttnArgs {
   float scale_log2;      // log2(e) / sqrt(head_dim)
   float* part_o;         // [batch][Hkv][max_chunks][G][hd][16]
   float* part_ml;        // [batch][Hkv][max_chunks][G][16][2]  (running max in log2 units, sum)
-  void* out;             // combine output: [batch*B][n_heads*hd] model dtype
+  void* out;             // [batch*B][n_heads*hd] model dtype; written by the partial kernel
+                         // when a sequence fits in one chunk, else by the combine
 };
 
 hipError_t launch_attention(int dtype, const AttnArgs& a, hipStream_t st);
@@ -98,12 +107,16 @@ hipError_t launch_rmsnorm(int dtype, const float* x, int64_t x_stride, const voi
                           int64_t y_stride, int rows, int d, float eps, int rpg, int grp_stride,
                           int grp_off, hipStream_t st);
 
+// Block embedding into the fp32 residual x, plus h = RMSNorm(x; gain) for layer 0.
 hipError_t launch_embed(int dtype, const void* embed, const int32_t* anchor, int batch, int block,
-                        int d, int vocab, int mask_id, float* x, int32_t* dev_status,
-                        hipStream_t st);
+                        int d, int vocab, int mask_id, float* x, const void* gain, float eps,
+                        void* h, int32_t* dev_status, hipStream_t st);
 
-hipError_t launch_argmax_reduce(const unsigned long long* amax, int64_t stride, int n_tiles,
-                                int rows, int32_t* tokens, hipStream_t st);
+// Draft tokens from the LM head's per-workgroup keys ([batch*(B-1)][n_cols]),
+// plus the greedy accept rule when targets is non-null.
+hipError_t launch_argmax_accept(const unsigned long long* amax, int64_t stride, int n_cols,
+                                int batch, int block, int32_t* drafts, const int32_t* targets,
+                                int32_t* accept_len, int32_t* bonus, hipStream_t st);
 
 hipError_t launch_accept(const int32_t* drafts, const int32_t* targets, int batch, int block,
                          int32_t* accept_len, int32_t* bonus, int32_t* anchor_out,

@@ -166,7 +166,9 @@ int32_t dflash_ctx_kv_append(const dflash_handle *h, const dflash_kv_cache *cach
  * hidden_out: optional fp32 [batch, n_layers, B, hidden]: residual stream
  *             after each layer.
  * target_tokens: optional device int32 [batch, B]; when given, accept_len and
- *             bonus (device int32 [batch]) receive dflash_accept's result. */
+ *             bonus (device int32 [batch]) receive dflash_accept's result.
+ *             bonus may alias anchor: the anchor is read before the bonus is
+ *             written, so the bonus becomes the next round's anchor in place. */
 int32_t dflash_draft_forward(const dflash_handle *h, const dflash_kv_cache *cache,
                              const int32_t *anchor, int32_t batch, int32_t *draft_tokens,
                              float *logits, float *hidden_out, const int32_t *target_tokens,
@@ -185,8 +187,9 @@ int32_t dflash_accept(const int32_t *draft_tokens, const int32_t *target_tokens,
 const char *dflash_status_string(int32_t code);
 
 /* Kernel timing (benchmarking aid, process-wide, not thread-safe).
- * dflash_profiler_start(n): from now on every library kernel launch is
- * bracketed by HIP events on its own stream, up to n launches.
+ * dflash_profiler_start(n, mask): from now on every library kernel launch of a
+ * class whose bit (1 << class) is set in mask (0 = every class) is bracketed
+ * by HIP events on its own stream, up to n launches.
  * dflash_profiler_stop(): stop recording (events are kept).
  * dflash_profiler_read(kind, ...): waits for the recorded events and returns,
  * for kernel class `kind` (see dflash_kernel_class), the number of launches,
@@ -205,7 +208,7 @@ typedef enum dflash_kernel_class {
   DFLASH_K_NCLASSES = 9
 } dflash_kernel_class;
 
-int32_t dflash_profiler_start(int32_t max_launches);
+int32_t dflash_profiler_start(int32_t max_launches, uint32_t class_mask);
 int32_t dflash_profiler_stop(void);
 int32_t dflash_profiler_read(int32_t kind, int64_t *launches, double *total_ms,
                              double *total_bytes, double *total_flops);
