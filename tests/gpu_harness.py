@@ -78,7 +78,17 @@ class Model:
     oracle_w: dict
 
 
+_MODELS = {}
+
+
 def build_model(cfg, seed: int = 0) -> Model:
+    """Seeded drafter on both sides; the last full-size one is reused across tests."""
+    key = (cfg, seed)
+    if key in _MODELS:
+        return _MODELS[key]
+    if cfg.hidden >= 2048:
+        _MODELS.clear()
+        log(f"  drawing {cfg.name} weights")
     host = I.Weights(cfg, seed)
     dev = torch_io.weights_to_device(host)
     gpu = B.DraftModel(cfg, dev)
@@ -86,7 +96,10 @@ def build_model(cfg, seed: int = 0) -> Model:
     ow = {n: host.get(n).f32() for n in host.names()}
     if cfg.tied_embeddings:
         ow["lm_head"] = ow["embed"]
-    return Model(cfg, host, gpu, ow)
+    model = Model(cfg, host, gpu, ow)
+    if cfg.hidden >= 2048:
+        _MODELS[key] = model
+    return model
 
 
 def feats_to_device(feats: List[I.HostTensor]) -> List[torch.Tensor]:
