@@ -73,13 +73,14 @@ struct Plan {
 };
 
 // Keys per attention work item (one workgroup of G waves): aim for ~2048
-// waves over the whole cache, but keep chunks >= 256 keys so the fp32
-// partials (64 rows x head_dim per chunk) stay small next to the K/V stream,
-// and <= 1024 keys.
+// waves over the whole cache so every CU has work, within [64, 1024] keys.
+// Small contexts get short chunks (parallelism); long ones long chunks, which
+// keeps the fp32 partials (16 rows x head_dim per wave) a few percent of the
+// K/V stream.
 int choose_chunk(int batch, int hkv, int group, int cap) {
   long long waves_if_32 = (long long)batch * hkv * group * ((cap + 31) / 32);
   long long c = 32 * ((waves_if_32 + 2047) / 2048);
-  c = std::max(256LL, std::min(1024LL, c));
+  c = std::max(64LL, std::min(1024LL, c));
   return (int)c;
 }
 

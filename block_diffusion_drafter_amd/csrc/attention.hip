@@ -79,14 +79,15 @@ template <typename T, int HD>
 __device__ __forceinline__ void load_block(KVBlock<T, HD>& b, const T* K, const T* V, int kb,
                                            int k_hi, int r, int grp) {
   using KB = KVBlock<T, HD>;
-  constexpr int SPAN = HD / 4;
+  // Fragment f of lane group g holds head-dim channels [4*EPF*f + EPF*g, +EPF):
+  // one load instruction reads 64 contiguous bytes of 16 key rows.
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     const int key = kb + key_of<T>(t, r);
     const bool ok = key < k_hi;
-    const T* kp = K + (size_t)key * HD + grp * SPAN;
+    const T* kp = K + (size_t)key * HD + grp * KB::EPF;
 #pragma unroll
-    for (int f = 0; f < KB::FR; ++f) b.k[t][f] = ok ? ld16(kp + f * KB::EPF) : zero16();
+    for (int f = 0; f < KB::FR; ++f) b.k[t][f] = ok ? ld16(kp + f * 4 * KB::EPF) : zero16();
   }
   const T* vb = V + (size_t)(kb / kKeyBlock) * HD * kKeyBlock;
   const bool tail = kb + 32 > k_hi;
@@ -107,7 +108,6 @@ template <typename T, int HD>
 __global__ __launch_bounds__(512) void attn_partial_kernel(AttnArgs p) {
   using KB = KVBlock<T, HD>;
   constexpr int EPF = KB::EPF, FR = KB::FR, NDT = KB::NDT;
-  constexpr int SPAN = HD / 4;
   const int lane = threadIdx.x & 63, j = threadIdx.x >> 6;
   const int r = lane & 15, grp = lane >> 4;
   const int c = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
@@ -124,12 +124,12 @@ __global__ __launch_bounds__(512) void attn_partial_kernel(AttnArgs p) {
   const T* K = reinterpret_cast<const T*>(p.k) + kvoff;
   const T* V = reinterpret_cast<const T*>(p.v) + kvoff;
 
-  u32x4 qf[FR];
+  u32x4 qf[FR];  // same channel order as the K fragments
   {
     const T* qp = reinterpret_cast<const T*>(p.q) + (((size_t)s * p.n_heads + h) * 16 + r) * HD +
-                  grp * SPAN;
+                  grp * EPF;
 #pragma unroll
-    for (int f = 0; f < FR; ++f) qf[f] = ld16(qp + f * EPF);
+    for (int f = 0; f < FR; ++f) qf[f] = ld16(qp + f * 4 * EPF);
   }
 
   float m_run = -INFINITY, l_run = 0.f;
@@ -241,58 +241,63 @@ __global__ __launch_bounds__(512) void attn_partial_kernel(AttnArgs p) {
     for (int i = 0; i < 4; ++i) po[(16 * dt + 4 * grp + i) * 16 + r] = o[dt][i];
 }
 
-// One workgroup per (query head, sequence). Thread t owns query row t % 16 and
-// channels t / 16 + 16 k; the chunk weights exp2(m_c - M) / L are computed once
-// into LDS, and every thread's chunk loop issues independent loads.
+// Merge of the chunk partials of one (query head, sequence, 16-channel slice).
+// Thread (q, cg) owns query row q and the chunks c = cg, cg + 16, ...: it
+// reduces the row's running max and sum over its chunks, the 16 threads of a
+// row combine them through LDS, then each thread accumulates its chunks'
+// weighted partial outputs for the slice's 16 channels and LDS sums the 16
+// chunk groups. Every thread's loads are independent of each other.
 template <typename T, int HD>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs p) {
-  extern __shared__ float wsh[];  // [nch][16]: m_c, then the chunk weight
-  __shared__ float lsh[16 * 16];
-  const int h = blockIdx.x, s = blockIdx.y;
+  __shared__ float red_m[16][17], red_l[16][17];
+  __shared__ float red_o[16][16][17];
+  const int h = blockIdx.x, s = blockIdx.y, slice = blockIdx.z;
   const int G = p.n_heads / p.n_kv_heads;
   const int g = h / G, j = h % G;
   const int n_keys = seq_keys(p, s);
   const int nch = (n_keys + p.chunk - 1) / p.chunk;
   if (nch <= 1) return;  // written by the partial kernel
-  const int t = threadIdx.x, q = t & 15, part = t >> 4;
+  const int t = threadIdx.x, q = t & 15, cg = t >> 4;
   const size_t item0 = (size_t)(s * p.n_kv_heads + g) * p.max_chunks * G + j;
-  // 1. every chunk's running max into LDS
-  for (int idx = t; idx < nch * 16; idx += 256) {
-    const int c = idx >> 4, qq = idx & 15;
-    wsh[idx] = p.part_ml[((item0 + (size_t)c * G) * 16 + qq) * 2];
-  }
+  float m = -INFINITY;
+  for (int c = cg; c < nch; c += 16) m = fmaxf(m, p.part_ml[((item0 + (size_t)c * G) * 16 + q) * 2]);
+  red_m[q][cg] = m;
   __syncthreads();
-  // 2. the row's global max; 3. its sum, split over the 16 threads of the row
   float M = -INFINITY;
-  for (int c = 0; c < nch; ++c) M = fmaxf(M, wsh[c * 16 + q]);
-  float L = 0.f;
-  for (int c = part; c < nch; c += 16)
-    L += p.part_ml[((item0 + (size_t)c * G) * 16 + q) * 2 + 1] * exp2f(wsh[c * 16 + q] - M);
-  lsh[part * 16 + q] = L;
-  __syncthreads();
-  L = 0.f;
 #pragma unroll
-  for (int k = 0; k < 16; ++k) L += lsh[k * 16 + q];
-  const float inv = 1.0f / L;
-  // 4. one thread per row turns the chunk maxima into weights exp2(m_c - M) / L
-  if (part == 0)
-    for (int c = 0; c < nch; ++c) wsh[c * 16 + q] = exp2f(wsh[c * 16 + q] - M) * inv;
-  __syncthreads();
-  if (q >= p.block) return;
-  constexpr int PER = HD / 16;
-  float acc[PER];
-#pragma unroll
-  for (int k = 0; k < PER; ++k) acc[k] = 0.f;
-#pragma unroll 2
-  for (int c = 0; c < nch; ++c) {
-    const float wgt = wsh[c * 16 + q];
-    const float* po = p.part_o + (item0 + (size_t)c * G) * HD * 16;
-#pragma unroll
-    for (int k = 0; k < PER; ++k) acc[k] += po[(part + 16 * k) * 16 + q] * wgt;
+  for (int k = 0; k < 16; ++k) M = fmaxf(M, red_m[q][k]);
+  float l = 0.f;
+  for (int c = cg; c < nch; c += 16) {
+    const float* ml = p.part_ml + ((item0 + (size_t)c * G) * 16 + q) * 2;
+    l += ml[1] * exp2f(ml[0] - M);
   }
-  T* out = reinterpret_cast<T*>(p.out) + ((size_t)s * p.block + q) * p.n_heads * HD + (size_t)h * HD;
+  red_l[q][cg] = l;
+  __syncthreads();
+  float L = 0.f;
 #pragma unroll
-  for (int k = 0; k < PER; ++k) out[part + 16 * k] = from_f32<T>(acc[k]);
+  for (int k = 0; k < 16; ++k) L += red_l[q][k];
+  const float inv = 1.0f / L;
+  float acc[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) acc[k] = 0.f;
+  for (int c = cg; c < nch; c += 16) {
+    const size_t it = item0 + (size_t)c * G;
+    const float w = exp2f(p.part_ml[(it * 16 + q) * 2] - M) * inv;
+    const float* po = p.part_o + (it * HD + 16 * slice) * 16 + q;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) acc[k] += po[k * 16] * w;
+  }
+#pragma unroll
+  for (int k = 0; k < 16; ++k) red_o[k][cg][q] = acc[k];
+  __syncthreads();
+  // thread (q, d = cg) sums the 16 chunk groups of channel 16*slice + d
+  if (q < p.block) {
+    float o = 0.f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) o += red_o[cg][k][q];
+    T* out = reinterpret_cast<T*>(p.out) + ((size_t)s * p.block + q) * p.n_heads * HD + (size_t)h * HD;
+    out[16 * slice + cg] = from_f32<T>(o);
+  }
 }
 
 template <typename T, int HD>
@@ -304,8 +309,8 @@ static hipError_t launch_hd(const AttnArgs& a, hipStream_t st) {
   if (e != hipSuccess || a.max_chunks <= 1) return e;
   prof_end(st);
   prof_begin(DFLASH_K_ATTN_COMBINE, 0.0, 0.0, st);
-  const size_t lds = (size_t)a.max_chunks * 16 * sizeof(float);
-  hipLaunchKernelGGL((attn_combine_kernel<T, HD>), dim3(a.n_heads, a.batch), dim3(256), lds, st, a);
+  hipLaunchKernelGGL((attn_combine_kernel<T, HD>), dim3(a.n_heads, a.batch, HD / 16), dim3(256), 0,
+                     st, a);
   return hipGetLastError();
 }
 
