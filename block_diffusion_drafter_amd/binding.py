@@ -39,7 +39,8 @@ class LayerWeights(ctypes.Structure):
 class WeightsStruct(ctypes.Structure):
     _fields_ = [("embed", ctypes.c_void_p), ("lm_head", ctypes.c_void_p),
                 ("fc", ctypes.c_void_p), ("fc_norm", ctypes.c_void_p),
-                ("final_norm", ctypes.c_void_p), ("layers", ctypes.POINTER(LayerWeights))]
+                ("final_norm", ctypes.c_void_p), ("layers", ctypes.POINTER(LayerWeights)),
+                ("packed", ctypes.c_void_p), ("packed_bytes", ctypes.c_int64)]
 
 
 class KVCacheStruct(ctypes.Structure):
@@ -64,6 +65,11 @@ def lib() -> ctypes.CDLL:
         L.dflash_create.restype = i32
         L.dflash_create.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(WeightsStruct),
                                     ctypes.POINTER(vp)]
+        L.dflash_packed_weight_bytes.restype = i64
+        L.dflash_packed_weight_bytes.argtypes = [ctypes.POINTER(Config)]
+        L.dflash_pack_weights.restype = i32
+        L.dflash_pack_weights.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(WeightsStruct),
+                                          vp, i64, vp]
         L.dflash_destroy.restype = None
         L.dflash_destroy.argtypes = [vp]
         L.dflash_workspace_bytes.restype = i64
@@ -169,6 +175,9 @@ class DraftModel:
 
     weights: name -> device tensor in the model dtype, with the names
     embed, lm_head, fc, fc_norm, final_norm and layers.{l}.{field}.
+    The projections are copied once into the library's tiled layout (a device
+    buffer this object owns, written by dflash_pack_weights on the current
+    stream); the row-major tensors stay referenced for the embedding and gains.
     """
 
     def __init__(self, cfg, weights: Dict[str, torch.Tensor]):
@@ -181,9 +190,17 @@ class DraftModel:
             for f in LAYER_FIELDS:
                 setattr(self._layers[l], f, _ptr(weights[f"layers.{l}.{f}"]))
         lm = weights.get("lm_head", weights["embed"])
+        n_packed = lib().dflash_packed_weight_bytes(ctypes.byref(self.c))
+        if n_packed < 0:
+            _check(int(n_packed), "dflash_packed_weight_bytes")
+        self.packed = torch.empty(int(n_packed), dtype=torch.uint8, device="cuda")
         self._w = WeightsStruct(_ptr(weights["embed"]), _ptr(lm), _ptr(weights["fc"]),
                                 _ptr(weights["fc_norm"]), _ptr(weights["final_norm"]),
-                                ctypes.cast(self._layers, ctypes.POINTER(LayerWeights)))
+                                ctypes.cast(self._layers, ctypes.POINTER(LayerWeights)),
+                                _ptr(self.packed), int(n_packed))
+        _check(lib().dflash_pack_weights(ctypes.byref(self.c), ctypes.byref(self._w),
+                                         _ptr(self.packed), int(n_packed), _stream()),
+               "dflash_pack_weights")
         h = ctypes.c_void_p()
         _check(lib().dflash_create(ctypes.byref(self.c), ctypes.byref(self._w), ctypes.byref(h)),
                "dflash_create")

@@ -1,6 +1,7 @@
-// C ABI of the drafter library: argument validation, workspace layout, and
-// the launch sequence of each call. No device memory is allocated here; all
-// scratch comes from the caller's workspace.
+// C ABI of the drafter library: argument validation, workspace and
+// packed-weight layouts, and the launch sequence of each call. No device
+// memory is allocated here: scratch comes from the caller's workspace, the
+// tiled weight copy from the caller's packed buffer.
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
@@ -9,10 +10,18 @@
 
 #include "internal.h"
 
+// Offsets (bytes) of the tiled projection weights inside the packed buffer.
+struct PackedLayout {
+  size_t qkv[dflash::kMaxLayers], wo[dflash::kMaxLayers], gate[dflash::kMaxLayers];
+  size_t up[dflash::kMaxLayers], down[dflash::kMaxLayers];
+  size_t fc, kv, lm, total;
+};
+
 struct dflash_handle {
   dflash_config cfg;
   dflash_weights w;
   std::vector<dflash_layer_weights> layers;
+  PackedLayout pl;
 };
 
 namespace dflash {
@@ -64,6 +73,33 @@ inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
     if ((expr) != hipSuccess) return DFLASH_ERR_HIP; \
   } while (0)
 
+// Tiled copies, in order: per layer [wq; wk; wv] (stacked rows), wo, w_gate,
+// w_up, w_down; then fc; then every layer's [wk; wv] stacked (the context K/V
+// projection of all layers in one GEMM); then the LM head.
+PackedLayout packed_layout(const dflash_config& c) {
+  PackedLayout p{};
+  const int dt = c.dtype, d = c.hidden, hd = c.head_dim, I = c.intermediate;
+  const int q_dim = c.n_heads * hd, kv_dim = c.n_kv_heads * hd;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = align256(off + bytes);
+    return o;
+  };
+  for (int l = 0; l < c.n_layers; ++l) {
+    p.qkv[l] = take(tiled_bytes(dt, q_dim + 2 * kv_dim, d));
+    p.wo[l] = take(tiled_bytes(dt, d, q_dim));
+    p.gate[l] = take(tiled_bytes(dt, I, d));
+    p.up[l] = take(tiled_bytes(dt, I, d));
+    p.down[l] = take(tiled_bytes(dt, d, I));
+  }
+  p.fc = take(tiled_bytes(dt, d, c.n_target_feats * c.target_hidden));
+  p.kv = take(tiled_bytes(dt, (int64_t)c.n_layers * 2 * kv_dim, d));
+  p.lm = take(tiled_bytes(dt, c.vocab, d));
+  p.total = off;
+  return p;
+}
+
 struct Plan {
   size_t x, h, qkv, q, po, pml, attn, act, y, amax, fwd_end;
   size_t u, proj_end;
@@ -95,18 +131,19 @@ Plan make_plan(const dflash_config& c, int batch, int cap, int max_tokens) {
     off = align256(off + bytes);
     return o;
   };
+  const int dt = c.dtype;
   p.x = take(M * d * 4);
-  p.h = take(M * d * es);
+  p.h = take(tiled_bytes(dt, (int64_t)M, (int)d));
   p.qkv = take(M * (Hq + 2 * Hkv) * hd * 4);
   p.q = take((size_t)batch * Hq * 16 * hd * es);
   p.chunk = choose_chunk(batch, (int)Hkv, (int)G, cap);
   p.max_chunks = (cap + p.chunk - 1) / p.chunk;
   p.po = take((size_t)batch * Hkv * p.max_chunks * G * hd * 16 * 4);
   p.pml = take((size_t)batch * Hkv * p.max_chunks * G * 16 * 2 * 4);
-  p.attn = take(M * Hq * hd * es);
-  p.act = take(M * I * es);
+  p.attn = take(tiled_bytes(dt, (int64_t)M, (int)(Hq * hd)));
+  p.act = take(tiled_bytes(dt, (int64_t)M, (int)I));
   const size_t R = (size_t)batch * (B - 1);
-  p.y = take(R * d * es);
+  p.y = take(tiled_bytes(dt, (int64_t)R, (int)d));
   // LM head: one (max, argmax) key per row and workgroup column.
   p.n_vtiles = R > 0 ? plan_gemm(c.dtype, EPI_ARGMAX, (int)R, c.vocab, c.hidden, 0).grid_x : 1;
   p.amax = take(R * p.n_vtiles * 8);
@@ -144,25 +181,29 @@ int32_t check_config(const dflash_config& c) {
   return DFLASH_OK;
 }
 
-GemmArgs gemm_base(const void* a, int64_t a_stride, int M, int N, int K) {
+// A projection reading a tiled activation matrix a [M, K] from the workspace
+// and the tiled weight w (w2: the up matrix of the SwiGLU pair).
+GemmArgs gemm_tiled(const void* a, const void* w, int M, int N, int K, const void* w2 = nullptr) {
   GemmArgs g;
   std::memset(&g, 0, sizeof(g));
   g.a[0] = a;
-  g.a_stride = a_stride;
-  g.a_seg_k = K;
   g.a_nseg = 1;
+  g.a_seg_k = K;
+  g.a_tiled = 1;
+  g.w = w;
+  g.w2 = w2;
   g.M = M;
   g.N = N;
   g.K = K;
   return g;
 }
 
-void one_seg(GemmArgs& g, const void* w, const void* w2 = nullptr) {
-  g.w[0] = w;
-  g.w2[0] = w2;
-  g.w_row0[0] = 0;
-  g.w_row0[1] = g.N;
-  g.w_nseg = 1;
+// A projection of caller-provided row-major rows (stride a_stride elements).
+GemmArgs gemm_rows(const void* a, int64_t a_stride, const void* w, int M, int N, int K) {
+  GemmArgs g = gemm_tiled(a, w, M, N, K);
+  g.a_tiled = 0;
+  g.a_stride = a_stride;
+  return g;
 }
 
 int32_t run_gemm(int dtype, int epi, const GemmArgs& g, hipStream_t st) {
@@ -204,12 +245,61 @@ const char* dflash_status_string(int32_t code) {
     case DFLASH_ERR_SHAPE: return "a size is out of range or inconsistent";
     case DFLASH_ERR_DTYPE: return "unknown dtype";
     case DFLASH_ERR_ALIGN: return "a pointer or stride is not 16-byte aligned";
-    case DFLASH_ERR_WORKSPACE: return "workspace is smaller than dflash_workspace_bytes()";
+    case DFLASH_ERR_WORKSPACE: return "workspace or packed buffer is smaller than its size query";
     case DFLASH_ERR_UNSUPPORTED: return "configuration not covered by the kernels";
     case DFLASH_ERR_HIP: return "a HIP launch reported an error";
     case DFLASH_ERR_STATE: return "profiler misuse";
     default: return "unknown status";
   }
+}
+
+int64_t dflash_packed_weight_bytes(const dflash_config* cfg) {
+  if (!cfg) return DFLASH_ERR_NULL;
+  const int32_t rc = check_config(*cfg);
+  if (rc) return rc;
+  return (int64_t)packed_layout(*cfg).total;
+}
+
+int32_t dflash_pack_weights(const dflash_config* cfg, const dflash_weights* w, void* packed,
+                            int64_t packed_bytes, void* stream) {
+  if (!cfg || !w) return DFLASH_ERR_NULL;
+  int32_t rc = check_config(*cfg);
+  if (rc) return rc;
+  if (!w->lm_head || !w->fc || !w->layers || !packed) return DFLASH_ERR_NULL;
+  if (!al16(w->lm_head) || !al16(w->fc) || !al16(packed)) return DFLASH_ERR_ALIGN;
+  for (int l = 0; l < cfg->n_layers; ++l) {
+    const dflash_layer_weights& lw = w->layers[l];
+    const void* ps[] = {lw.wq, lw.wk, lw.wv, lw.wo, lw.w_gate, lw.w_up, lw.w_down};
+    for (const void* q : ps) {
+      if (!q) return DFLASH_ERR_NULL;
+      if (!al16(q)) return DFLASH_ERR_ALIGN;
+    }
+  }
+  const PackedLayout pl = packed_layout(*cfg);
+  if (packed_bytes < (int64_t)pl.total) return DFLASH_ERR_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  const int dt = cfg->dtype, d = cfg->hidden, I = cfg->intermediate;
+  const int q_dim = cfg->n_heads * cfg->head_dim, kv_dim = cfg->n_kv_heads * cfg->head_dim;
+  char* base = (char*)packed;
+  // Stacked matrices: each part starts on a 16-row tile boundary (q_dim and
+  // kv_dim are multiples of 16), so a part is packed at its rows' byte offset.
+  auto pack = [&](const void* src, int rows, int K, size_t off, int64_t row0) {
+    return launch_pack_tiled(dt, src, rows, K, base + off + tiled_bytes(dt, row0, K), st) ==
+           hipSuccess;
+  };
+  bool ok = true;
+  for (int l = 0; l < cfg->n_layers && ok; ++l) {
+    const dflash_layer_weights& lw = w->layers[l];
+    ok = pack(lw.wq, q_dim, d, pl.qkv[l], 0) && pack(lw.wk, kv_dim, d, pl.qkv[l], q_dim) &&
+         pack(lw.wv, kv_dim, d, pl.qkv[l], q_dim + kv_dim) && pack(lw.wo, d, q_dim, pl.wo[l], 0) &&
+         pack(lw.w_gate, I, d, pl.gate[l], 0) && pack(lw.w_up, I, d, pl.up[l], 0) &&
+         pack(lw.w_down, d, I, pl.down[l], 0) &&
+         pack(lw.wk, kv_dim, d, pl.kv, (int64_t)(2 * l) * kv_dim) &&
+         pack(lw.wv, kv_dim, d, pl.kv, (int64_t)(2 * l + 1) * kv_dim);
+  }
+  ok = ok && pack(w->fc, d, cfg->n_target_feats * cfg->target_hidden, pl.fc, 0) &&
+       pack(w->lm_head, cfg->vocab, d, pl.lm, 0);
+  return ok ? DFLASH_OK : DFLASH_ERR_HIP;
 }
 
 int32_t dflash_create(const dflash_config* cfg, const dflash_weights* w, dflash_handle** out) {
@@ -218,26 +308,28 @@ int32_t dflash_create(const dflash_config* cfg, const dflash_weights* w, dflash_
   if (!cfg || !w) return DFLASH_ERR_NULL;
   int32_t rc = check_config(*cfg);
   if (rc) return rc;
-  if (!w->embed || !w->lm_head || !w->fc || !w->fc_norm || !w->final_norm || !w->layers)
+  if (!w->embed || !w->fc_norm || !w->final_norm || !w->layers || !w->packed)
     return DFLASH_ERR_NULL;
-  const void* top[] = {w->embed, w->lm_head, w->fc, w->fc_norm, w->final_norm};
+  const void* top[] = {w->embed, w->fc_norm, w->final_norm, w->packed};
   for (const void* p : top)
     if (!al16(p)) return DFLASH_ERR_ALIGN;
   for (int l = 0; l < cfg->n_layers; ++l) {
     const dflash_layer_weights& lw = w->layers[l];
-    const void* ps[] = {lw.in_norm, lw.wq, lw.wk, lw.wv, lw.q_norm, lw.k_norm,
-                        lw.wo, lw.post_norm, lw.w_gate, lw.w_up, lw.w_down};
+    const void* ps[] = {lw.in_norm, lw.q_norm, lw.k_norm, lw.post_norm};
     for (const void* p : ps) {
       if (!p) return DFLASH_ERR_NULL;
       if (!al16(p)) return DFLASH_ERR_ALIGN;
     }
   }
+  const PackedLayout pl = packed_layout(*cfg);
+  if (w->packed_bytes < (int64_t)pl.total) return DFLASH_ERR_WORKSPACE;
   dflash_handle* hd = new (std::nothrow) dflash_handle;
   if (!hd) return DFLASH_ERR_SHAPE;
   hd->cfg = *cfg;
   hd->w = *w;
   hd->layers.assign(w->layers, w->layers + cfg->n_layers);
   hd->w.layers = hd->layers.data();
+  hd->pl = pl;
   *out = hd;
   return DFLASH_OK;
 }
@@ -272,17 +364,18 @@ int32_t dflash_ctx_project(const dflash_handle* h, const void* const* feats,
   if (ws_bytes < (int64_t)P.proj_end) return DFLASH_ERR_WORKSPACE;
   hipStream_t st = (hipStream_t)stream;
   float* u = reinterpret_cast<float*>((char*)ws + P.u);
-  GemmArgs g = gemm_base(nullptr, feat_row_stride, n_tok, c.hidden, c.n_target_feats * c.target_hidden);
+  const char* pk = (const char*)h->w.packed;
+  GemmArgs g = gemm_rows(nullptr, feat_row_stride, pk + h->pl.fc, n_tok, c.hidden,
+                         c.n_target_feats * c.target_hidden);
   for (int f = 0; f < c.n_target_feats; ++f) g.a[f] = feats[f];
   g.a_nseg = c.n_target_feats;
   g.a_seg_k = c.target_hidden;
-  one_seg(g, h->w.fc);
   g.out = u;
   g.out_stride = c.hidden;
   int32_t rc = run_gemm(c.dtype, EPI_STORE_F32, g, st);
   if (rc) return rc;
   prof_begin(DFLASH_K_RMSNORM, 0, 0, st);
-  hipError_t e = launch_rmsnorm(c.dtype, u, c.hidden, h->w.fc_norm, ctx_out, c.hidden, n_tok,
+  hipError_t e = launch_rmsnorm(c.dtype, u, c.hidden, h->w.fc_norm, ctx_out, c.hidden, 0, n_tok,
                                 c.hidden, c.rms_eps, n_tok, 0, 0, st);
   prof_end(st);
   return e == hipSuccess ? DFLASH_OK : DFLASH_ERR_HIP;
@@ -306,15 +399,7 @@ int32_t dflash_ctx_kv_append(const dflash_handle* h, const dflash_kv_cache* cach
   if (n_tok > 0) {
     float* kv = reinterpret_cast<float*>((char*)ws + P.kv);
     const int N = L * 2 * Hkv * hd;
-    GemmArgs g = gemm_base(ctx, c.hidden, n_tok, N, c.hidden);
-    for (int l = 0; l < L; ++l) {
-      g.w[2 * l] = h->layers[l].wk;
-      g.w[2 * l + 1] = h->layers[l].wv;
-      g.w_row0[2 * l] = (2 * l) * Hkv * hd;
-      g.w_row0[2 * l + 1] = (2 * l + 1) * Hkv * hd;
-    }
-    g.w_row0[2 * L] = N;
-    g.w_nseg = 2 * L;
+    GemmArgs g = gemm_rows(ctx, c.hidden, (const char*)h->w.packed + h->pl.kv, n_tok, N, c.hidden);
     g.out = kv;
     g.out_stride = N;
     rc = run_gemm(c.dtype, EPI_STORE_F32, g, st);
@@ -387,6 +472,9 @@ int32_t dflash_draft_forward(const dflash_handle* h, const dflash_kv_cache* cach
   const int d = c.hidden, hd = c.head_dim, Hq = c.n_heads, Hkv = c.n_kv_heads, I = c.intermediate;
   const int M = batch * B, L = c.n_layers;
   const size_t layer_elems = (size_t)cache->batch * Hkv * cap * hd;
+  const int nck_d = tiled_nck(c.dtype, d);
+  const char* pk = (const char*)h->w.packed;
+  const PackedLayout& pl = h->pl;
 
   prof_begin(DFLASH_K_SMALL, 0, 0, st);
   hipError_t e = launch_embed(c.dtype, h->w.embed, anchor, batch, B, d, c.vocab, c.mask_token_id,
@@ -398,21 +486,13 @@ int32_t dflash_draft_forward(const dflash_handle* h, const dflash_kv_cache* cach
     const dflash_layer_weights& lw = h->layers[l];
     if (l > 0) {  // layer 0's pre-norm came with the embedding
       prof_begin(DFLASH_K_RMSNORM, 0, 0, st);
-      e = launch_rmsnorm(c.dtype, x, d, lw.in_norm, hbuf, d, M, d, c.rms_eps, M, 0, 0, st);
+      e = launch_rmsnorm(c.dtype, x, d, lw.in_norm, hbuf, 0, nck_d, M, d, c.rms_eps, M, 0, 0, st);
       prof_end(st);
       if (e != hipSuccess) return DFLASH_ERR_HIP;
     }
 
     const int Nqkv = (Hq + 2 * Hkv) * hd;
-    GemmArgs g = gemm_base(hbuf, d, M, Nqkv, d);
-    g.w[0] = lw.wq;
-    g.w[1] = lw.wk;
-    g.w[2] = lw.wv;
-    g.w_row0[0] = 0;
-    g.w_row0[1] = Hq * hd;
-    g.w_row0[2] = (Hq + Hkv) * hd;
-    g.w_row0[3] = Nqkv;
-    g.w_nseg = 3;
+    GemmArgs g = gemm_tiled(hbuf, pk + pl.qkv[l], M, Nqkv, d);
     g.out = qkv;
     g.out_stride = Nqkv;
     if ((rc = run_gemm(c.dtype, EPI_STORE_F32, g, st))) return rc;
@@ -461,30 +541,27 @@ int32_t dflash_draft_forward(const dflash_handle* h, const dflash_kv_cache* cach
     at.part_o = reinterpret_cast<float*>(w + P.po);
     at.part_ml = reinterpret_cast<float*>(w + P.pml);
     at.out = attn;
+    at.out_nck = tiled_nck(c.dtype, Hq * hd);
     prof_begin(DFLASH_K_ATTN, 0, 0, st);
     e = launch_attention(c.dtype, at, st);
     prof_end(st);
     if (e != hipSuccess) return DFLASH_ERR_HIP;
 
-    g = gemm_base(attn, Hq * hd, M, d, Hq * hd);
-    one_seg(g, lw.wo);
+    g = gemm_tiled(attn, pk + pl.wo[l], M, d, Hq * hd);
     g.resid = x;
     g.out_stride = d;
     if ((rc = run_gemm(c.dtype, EPI_RESID, g, st))) return rc;
 
     prof_begin(DFLASH_K_RMSNORM, 0, 0, st);
-    e = launch_rmsnorm(c.dtype, x, d, lw.post_norm, hbuf, d, M, d, c.rms_eps, M, 0, 0, st);
+    e = launch_rmsnorm(c.dtype, x, d, lw.post_norm, hbuf, 0, nck_d, M, d, c.rms_eps, M, 0, 0, st);
     prof_end(st);
     if (e != hipSuccess) return DFLASH_ERR_HIP;
 
-    g = gemm_base(hbuf, d, M, I, d);
-    one_seg(g, lw.w_gate, lw.w_up);
+    g = gemm_tiled(hbuf, pk + pl.gate[l], M, I, d, pk + pl.up[l]);
     g.out = act;
-    g.out_stride = I;
     if ((rc = run_gemm(c.dtype, EPI_SWIGLU, g, st))) return rc;
 
-    g = gemm_base(act, I, M, d, I);
-    one_seg(g, lw.w_down);
+    g = gemm_tiled(act, pk + pl.down[l], M, d, I);
     g.resid = x;
     g.out_stride = d;
     if ((rc = run_gemm(c.dtype, EPI_RESID, g, st))) return rc;
@@ -499,11 +576,11 @@ int32_t dflash_draft_forward(const dflash_handle* h, const dflash_kv_cache* cach
   const int R = batch * (B - 1);
   if (R > 0) {
     prof_begin(DFLASH_K_RMSNORM, 0, 0, st);
-    e = launch_rmsnorm(c.dtype, x, d, h->w.final_norm, ybuf, d, R, d, c.rms_eps, B - 1, B, 1, st);
+    e = launch_rmsnorm(c.dtype, x, d, h->w.final_norm, ybuf, 0, nck_d, R, d, c.rms_eps, B - 1, B,
+                       1, st);
     prof_end(st);
     if (e != hipSuccess) return DFLASH_ERR_HIP;
-    GemmArgs g = gemm_base(ybuf, d, R, c.vocab, d);
-    one_seg(g, h->w.lm_head);
+    GemmArgs g = gemm_tiled(ybuf, pk + pl.lm, R, c.vocab, d);
     g.amax = amax;
     g.amax_stride = P.n_vtiles;
     g.logits = logits;

@@ -219,13 +219,16 @@ __global__ __launch_bounds__(512) void attn_partial_kernel(AttnArgs p) {
   if (single) {
     // The whole sequence was in this chunk: normalise and write the output.
     if (r < p.block) {
+      // Four consecutive channels per lane and tile: contiguous in the tiled output.
       const float inv = 1.0f / l_run;
-      T* out = reinterpret_cast<T*>(p.out) + ((size_t)s * p.block + r) * p.n_heads * HD +
-               (size_t)h * HD;
+      T* out = reinterpret_cast<T*>(p.out);
+      const int row = s * p.block + r;
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt)
+      for (int dt = 0; dt < NDT; ++dt) {
+        T* dst = out + tiled_index<T>(row, h * HD + 16 * dt + 4 * grp, p.out_nck);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) out[16 * dt + 4 * grp + i] = from_f32<T>(o[dt][i] * inv);
+        for (int i = 0; i < 4; ++i) dst[i] = from_f32<T>(o[dt][i] * inv);
+      }
     }
     return;
   }
@@ -295,8 +298,8 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs p) {
     float o = 0.f;
 #pragma unroll
     for (int k = 0; k < 16; ++k) o += red_o[cg][k][q];
-    T* out = reinterpret_cast<T*>(p.out) + ((size_t)s * p.block + q) * p.n_heads * HD + (size_t)h * HD;
-    out[16 * slice + cg] = from_f32<T>(o);
+    T* out = reinterpret_cast<T*>(p.out);
+    out[tiled_index<T>(s * p.block + q, h * HD + 16 * slice + cg, p.out_nck)] = from_f32<T>(o);
   }
 }
 

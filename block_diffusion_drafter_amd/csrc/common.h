@@ -15,6 +15,17 @@
 //
 // Output (C/D) layout of a 16x16 tile: lane l holds rows 4*(l/16)+i, i=0..3,
 // of column l % 16.
+//
+// Tiled layout of the GEMM operands. Every projection weight, and every
+// activation matrix a projection reads from the library's own workspace, is
+// stored in the order the MFMA loop consumes it: rows in tiles of 16, k in
+// chunks of KC = 16 * EPF elements (256 bytes of a row), and inside one
+// (row tile, chunk) block four 1 KB fragments, fragment f holding for lane
+// l = r + 16 g the EPF elements of row r at k = KC*c + 4*EPF*f + EPF*g.
+// One load instruction of a wave then reads 1 KB of contiguous memory (eight
+// whole 128-byte lines) instead of 64 bytes from each of 16 rows. Rows are
+// padded to a multiple of 16 and k to a multiple of KC; weight padding is
+// zero, activation padding is never read into a stored result.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -34,6 +45,16 @@ template <> struct ElemInfo<float> {
 template <> struct ElemInfo<bf16> {
   static constexpr int per16 = 8;
 };
+
+// Element offset of (row, k) in a tiled matrix whose rows hold nck chunks.
+template <typename T>
+__host__ __device__ __forceinline__ int64_t tiled_index(int row, int k, int nck) {
+  constexpr int EPF = 16 / (int)sizeof(T);
+  constexpr int KC = 16 * EPF;
+  const int c = k / KC, kk = k % KC;
+  const int f = kk / (4 * EPF), g = (kk / EPF) & 3, e = kk % EPF;
+  return ((((int64_t)(row >> 4) * nck + c) * 4 + f) * 64 + g * 16 + (row & 15)) * EPF + e;
+}
 
 __device__ __forceinline__ u32x4 ld16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);

@@ -34,17 +34,17 @@ template <> __device__ __forceinline__ void store4<float>(float* y, float4 v) {
   *reinterpret_cast<float4*>(y) = v;
 }
 template <> __device__ __forceinline__ void store4<bf16>(bf16* y, float4 v) {
-  y[0] = (bf16)v.x;
-  y[1] = (bf16)v.y;
-  y[2] = (bf16)v.z;
-  y[3] = (bf16)v.w;
+  const bf16 b[4] = {(bf16)v.x, (bf16)v.y, (bf16)v.z, (bf16)v.w};
+  *reinterpret_cast<uint2*>(y) = __builtin_bit_cast(uint2, b);
 }
 
 // One row per workgroup, VPT float4 per thread held in registers: one load
-// pass, one block reduction, one store pass (d <= 4 * 256 * VPT).
+// pass, one block reduction, one store pass (d <= 4 * 256 * VPT). Output row
+// yrow of y: row-major with stride ys when nck == 0, else tiled with nck
+// chunks per row (four consecutive elements stay contiguous in both).
 template <typename T, int VPT>
-__device__ __forceinline__ void rmsnorm_row(const float* xr, const T* gain, T* yr, int d, float eps,
-                                            float* sh) {
+__device__ __forceinline__ void rmsnorm_row(const float* xr, const T* gain, T* y, int yrow,
+                                            int64_t ys, int nck, int d, float eps, float* sh) {
   float4 v[VPT];
   float ss = 0.f;
 #pragma unroll
@@ -60,8 +60,9 @@ __device__ __forceinline__ void rmsnorm_row(const float* xr, const T* gain, T* y
     const int k = 4 * (threadIdx.x + u * blockDim.x);
     if (k < d) {
       const float4 g = load4<T>(gain + k);
-      store4<T>(yr + k, make_float4(v[u].x * inv * g.x, v[u].y * inv * g.y, v[u].z * inv * g.z,
-                                    v[u].w * inv * g.w));
+      T* dst = nck ? y + tiled_index<T>(yrow, k, nck) : y + (int64_t)yrow * ys + k;
+      store4<T>(dst, make_float4(v[u].x * inv * g.x, v[u].y * inv * g.y, v[u].z * inv * g.z,
+                                 v[u].w * inv * g.w));
     }
   }
 }
@@ -69,45 +70,48 @@ __device__ __forceinline__ void rmsnorm_row(const float* xr, const T* gain, T* y
 // y[r] = x[src(r)] / sqrt(mean(x^2) + eps) * gain, statistics in fp32.
 template <typename T, int VPT>
 __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* x, int64_t xs, const T* gain,
-                                                      T* y, int64_t ys, int d, float eps, int rpg,
-                                                      int grp_stride, int grp_off) {
+                                                      T* y, int64_t ys, int nck, int d, float eps,
+                                                      int rpg, int grp_stride, int grp_off) {
   __shared__ float sh[4];
   const int r = blockIdx.x;
   const int64_t src = (int64_t)(r / rpg) * grp_stride + grp_off + r % rpg;
-  rmsnorm_row<T, VPT>(x + src * xs, gain, y + (int64_t)r * ys, d, eps, sh);
+  rmsnorm_row<T, VPT>(x + src * xs, gain, y, r, ys, nck, d, eps, sh);
 }
 
 template <typename T>
-static void launch_rmsnorm_t(const float* x, int64_t xs, const T* g, T* y, int64_t ys, int rows,
-                             int d, float eps, int rpg, int gs, int go, hipStream_t st) {
+static void launch_rmsnorm_t(const float* x, int64_t xs, const T* g, T* y, int64_t ys, int nck,
+                             int rows, int d, float eps, int rpg, int gs, int go, hipStream_t st) {
   const int vpt = (d + 1023) / 1024;
   dim3 grid(rows), block(256);
-  if (vpt <= 1) hipLaunchKernelGGL((rmsnorm_kernel<T, 1>), grid, block, 0, st, x, xs, g, y, ys, d, eps, rpg, gs, go);
-  else if (vpt <= 2) hipLaunchKernelGGL((rmsnorm_kernel<T, 2>), grid, block, 0, st, x, xs, g, y, ys, d, eps, rpg, gs, go);
-  else if (vpt <= 4) hipLaunchKernelGGL((rmsnorm_kernel<T, 4>), grid, block, 0, st, x, xs, g, y, ys, d, eps, rpg, gs, go);
-  else hipLaunchKernelGGL((rmsnorm_kernel<T, 8>), grid, block, 0, st, x, xs, g, y, ys, d, eps, rpg, gs, go);
+#define DF_NORM(V) \
+  hipLaunchKernelGGL((rmsnorm_kernel<T, V>), grid, block, 0, st, x, xs, g, y, ys, nck, d, eps, rpg, gs, go)
+  if (vpt <= 1) DF_NORM(1);
+  else if (vpt <= 2) DF_NORM(2);
+  else if (vpt <= 4) DF_NORM(4);
+  else DF_NORM(8);
+#undef DF_NORM
 }
 
 hipError_t launch_rmsnorm(int dtype, const float* x, int64_t x_stride, const void* gain, void* y,
-                          int64_t y_stride, int rows, int d, float eps, int rpg, int grp_stride,
-                          int grp_off, hipStream_t st) {
+                          int64_t y_stride, int y_nck, int rows, int d, float eps, int rpg,
+                          int grp_stride, int grp_off, hipStream_t st) {
   if (rows <= 0) return hipSuccess;
   if (d > 8192 || d % 4) return hipErrorInvalidValue;
   if (dtype == DFLASH_BF16)
-    launch_rmsnorm_t<bf16>(x, x_stride, (const bf16*)gain, (bf16*)y, y_stride, rows, d, eps, rpg,
-                           grp_stride, grp_off, st);
+    launch_rmsnorm_t<bf16>(x, x_stride, (const bf16*)gain, (bf16*)y, y_stride, y_nck, rows, d, eps,
+                           rpg, grp_stride, grp_off, st);
   else
-    launch_rmsnorm_t<float>(x, x_stride, (const float*)gain, (float*)y, y_stride, rows, d, eps,
-                            rpg, grp_stride, grp_off, st);
+    launch_rmsnorm_t<float>(x, x_stride, (const float*)gain, (float*)y, y_stride, y_nck, rows, d,
+                            eps, rpg, grp_stride, grp_off, st);
   return hipGetLastError();
 }
 
 // x[s*B + i] = E[i == 0 ? anchor[s] : mask] (input_embedding_scale 1), and the
-// first layer's pre-norm of that row, h = RMSNorm(x; gain).
+// first layer's pre-norm of that row, h = RMSNorm(x; gain), h tiled.
 template <typename T, int VPT>
 __global__ __launch_bounds__(256) void embed_kernel(const T* E, const int32_t* anchor, int block,
                                                     int d, int vocab, int mask_id, float* x,
-                                                    const T* gain, float eps, T* h,
+                                                    const T* gain, float eps, T* h, int nck,
                                                     int32_t* dev_status) {
   __shared__ float sh[4];
   const int row = blockIdx.x, s = row / block, i = row % block;
@@ -124,7 +128,7 @@ __global__ __launch_bounds__(256) void embed_kernel(const T* E, const int32_t* a
     if (k < d) *reinterpret_cast<float4*>(xr + k) = load4<T>(e + k);
   }
   __syncthreads();
-  rmsnorm_row<T, VPT>(xr, gain, h + (int64_t)row * d, d, eps, sh);
+  rmsnorm_row<T, VPT>(xr, gain, h, row, 0, nck, d, eps, sh);
 }
 
 hipError_t launch_embed(int dtype, const void* embed, const int32_t* anchor, int batch, int block,
@@ -132,10 +136,11 @@ hipError_t launch_embed(int dtype, const void* embed, const int32_t* anchor, int
                         void* h, int32_t* dev_status, hipStream_t st) {
   if (d > 8192 || d % 4) return hipErrorInvalidValue;
   const int vpt = (d + 1023) / 1024;
+  const int nck = tiled_nck(dtype, d);
   dim3 grid(batch * block), blk(256);
 #define DF_EMBED(T, V)                                                                            \
   hipLaunchKernelGGL((embed_kernel<T, V>), grid, blk, 0, st, (const T*)embed, anchor, block, d,   \
-                     vocab, mask_id, x, (const T*)gain, eps, (T*)h, dev_status)
+                     vocab, mask_id, x, (const T*)gain, eps, (T*)h, nck, dev_status)
   if (dtype == DFLASH_BF16) {
     if (vpt <= 1) DF_EMBED(bf16, 1); else if (vpt <= 2) DF_EMBED(bf16, 2);
     else if (vpt <= 4) DF_EMBED(bf16, 4); else DF_EMBED(bf16, 8);

@@ -1,22 +1,25 @@
 // Weight-streaming GEMM for the drafter's projections: Y = A · W^T, A [M, K]
-// (activations: the rows of the draft blocks, a few tens), W [N, K] row-major.
+// (activations: the rows of the draft blocks, a few tens), W [N, K].
 //
 // At drafting sizes every projection is a stream of the weight matrix through
 // HBM with ~16 flops per byte, so the kernel is organised for bandwidth:
 //   * a workgroup owns NT·16 output columns and up to 64 rows; its waves split
 //     K and meet in LDS at the end, so every weight byte is read once;
-//   * per 256-byte chunk of a weight row, instruction f of lane (r, g) reads
-//     bytes [64f + 16g, +16): one load instruction covers 64 contiguous bytes
-//     of 16 rows, and the four instructions of a chunk cover 256 contiguous
-//     bytes per row. That is the MFMA operand order itself (lane group g holds
-//     k = 8g..8g+7 of each 32-wide step), so no data is shuffled;
-//   * each wave carries NT n-tiles, so one activation fragment feeds NT MFMAs
-//     and activation traffic (L2 hits) stays a fraction of the weight stream;
-//   * chunk c+1 is in flight while chunk c is multiplied; interior tiles skip
-//     all bounds predication.
+//   * weights (always) and workspace activations are in the tiled layout of
+//     common.h: each load instruction of a wave reads one contiguous 1 KB
+//     fragment, which is the MFMA operand itself, so nothing is shuffled and
+//     the memory system sees whole lines. (With row-major operands a wave's
+//     load touches 16 rows x 64 bytes; the activation loads then cost as much
+//     as the weight stream although they hit in L2.)
+//   * each wave carries NT n-tiles, so one activation fragment feeds NT MFMAs;
+//   * loads go out in batches of P chunks before the batch's MFMAs; weight
+//     loads never need bounds checks (padded tiles, clamped tile indices).
+// Caller-provided row-major activations (the target features, context rows)
+// are read through the row-major path.
 // Epilogues: fp32 store, fp32 residual add (x += acc), SwiGLU of a gate and an
-// up stream computed side by side, and the LM head's per-row (max, argmax)
-// over each n-tile (keys reduced across tiles by a second kernel).
+// up stream computed side by side (tiled output: the next GEMM's A), and the
+// LM head's per-row (max, argmax) over each n-tile (keys reduced across tiles
+// by a second kernel).
 #include <algorithm>
 
 #include "common.h"
@@ -48,81 +51,91 @@ constexpr int gemm_threads_for(int mt, int nt_streams) {
                                                                                          : 512;
 }
 
-template <typename T, int MT, int NT, int EPI>
+template <typename T, int MT, int NT, int EPI, bool AT>
 __global__ __launch_bounds__((gemm_threads_for(MT, NT * (EPI == EPI_SWIGLU ? 2 : 1))))
 void gemm_stream_kernel(GemmArgs p) {
   constexpr int EPF = GemmGeom<T>::EPF;
   constexpr int KC = GemmGeom<T>::KC;
+  constexpr int FRAG = 64 * EPF;  // elements of one wave-wide 1 KB fragment
   constexpr int NB = (EPI == EPI_SWIGLU) ? 2 : 1;
   constexpr int P = gemm_stages(MT, NB * NT);
   extern __shared__ f32x4 red[];  // [ksplit][NB][MT*NT][64]
   __shared__ unsigned long long kred[EPI == EPI_ARGMAX ? MT * 16 * NT : 1];
 
   const int lane = threadIdx.x & 63;
-  // Wave-uniform values live in scalar registers: chunk and segment indices
-  // derived from them never need vector loads (or their waits) in the loop.
+  // Wave-uniform values live in scalar registers: chunk indices derived from
+  // them never need vector loads (or their waits) in the loop.
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int ksplit = blockDim.x >> 6;
   const int r = lane & 15, grp = lane >> 4;
-  const int n0 = blockIdx.x * (16 * NT);
+  const int nck = (p.K + KC - 1) / KC;
+  const int n_tiles = (p.N + 15) >> 4;
+  const int tile0 = blockIdx.x * NT;
   const int m_base = blockIdx.y * (16 * MT);
-  const bool tile_full = n0 + 16 * NT <= p.N;
 
-  // Weight row pointers: the lane's row in each n-tile, offset by its lane group.
-  const T* wrow[NB][NT];
-  bool n_ok[NT];
+  // Weight fragments of the lane in each n-tile. Tiles past the last one
+  // re-read the last tile (valid memory); their columns are never stored.
+  const T* wt[NB][NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
-    const int n = n0 + 16 * t + r;
-    n_ok[t] = n < p.N;
-    const int nn = n_ok[t] ? n : n0;
-    int s = 0;
-    while (s + 1 < p.w_nseg && nn >= p.w_row0[s + 1]) ++s;
-    const int64_t row = nn - p.w_row0[s];
-    wrow[0][t] = reinterpret_cast<const T*>(p.w[s]) + row * p.K + grp * EPF;
-    if constexpr (NB == 2)
-      wrow[1][t] = reinterpret_cast<const T*>(p.w2[s]) + row * p.K + grp * EPF;
-  }
-  // Rows past M read row M-1 (valid memory); their results are never stored.
-  bool m_ok[MT];
-  int64_t a_row_off[MT];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const int m = m_base + 16 * mt + r;
-    m_ok[mt] = m < p.M;
-    a_row_off[mt] = (int64_t)(m_ok[mt] ? m : p.M - 1) * p.a_stride + grp * EPF;
+    const int64_t off = (int64_t)min(tile0 + t, n_tiles - 1) * nck * 4 * FRAG + lane * EPF;
+    wt[0][t] = reinterpret_cast<const T*>(p.w) + off;
+    if constexpr (NB == 2) wt[1][t] = reinterpret_cast<const T*>(p.w2) + off;
   }
 
   const int k_begin = wave * p.k_per_wave;
   const int k_end = min(p.K, k_begin + p.k_per_wave);
+  const int c_begin = k_begin / KC;
   const int nchunks = k_end > k_begin ? (k_end - k_begin + KC - 1) / KC : 0;
-  // Chunks that need no bounds checks at all.
-  const int n_full = tile_full ? max(0, (k_end - k_begin) / KC) : 0;
-  // A operand: a wave's K range never crosses an A segment (the host sizes
-  // the split so), so the segment is resolved once, before the loop, and the
-  // loop addresses A linearly from this wave's base.
-  const int seg0 = __builtin_amdgcn_readfirstlane(k_begin / p.a_seg_k);
-  const T* a_wave = reinterpret_cast<const T*>(p.a[seg0 < p.a_nseg ? seg0 : 0]) +
-                    (k_begin - seg0 * p.a_seg_k) - k_begin;
-  auto a_base = [&](int kc) -> const T* { return a_wave + kc; };
+  // Chunks whose every k is inside K.
+  const int n_full = max(0, (k_end - k_begin) / KC);
+
+  // A operand. Tiled: per m-tile fragment base (tiles past the last re-read
+  // it). Row-major: rows past M read row M-1; a wave's K range never crosses
+  // an A segment (the host sizes the split so), so the segment is resolved
+  // once and the loop addresses A linearly from this wave's base.
+  int64_t a_off[MT];
+  const T* a_wave;
+  if constexpr (AT) {
+    const int m_tiles = (p.M + 15) >> 4;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+      a_off[mt] = (int64_t)min((int)blockIdx.y * MT + mt, m_tiles - 1) * nck * 4 * FRAG + lane * EPF;
+    a_wave = reinterpret_cast<const T*>(p.a[0]);
+  } else {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int m = m_base + 16 * mt + r;
+      a_off[mt] = (int64_t)(m < p.M ? m : p.M - 1) * p.a_stride + grp * EPF;
+    }
+    const int seg0 = __builtin_amdgcn_readfirstlane(k_begin / p.a_seg_k);
+    a_wave = reinterpret_cast<const T*>(p.a[seg0 < p.a_nseg ? seg0 : 0]) +
+             (k_begin - seg0 * p.a_seg_k) - k_begin;
+  }
+
+  // Fragment f of chunk c (counted from this wave's first chunk).
+  auto a_frag = [&](int mt, int c, int f) -> const T* {
+    if constexpr (AT) return a_wave + a_off[mt] + (int64_t)((c_begin + c) * 4 + f) * FRAG;
+    else return a_wave + a_off[mt] + k_begin + c * KC + f * 4 * EPF;
+  };
 
   auto load_full = [&](GemmRegs<MT, NT, NB>& g, int c) {
-    const int kc = k_begin + c * KC;
-    const T* ab = a_base(kc);
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
 #pragma unroll
       for (int b = 0; b < NB; ++b)
 #pragma unroll
-        for (int t = 0; t < NT; ++t) g.w[b][t][f] = ld16(wrow[b][t] + kc + f * 4 * EPF);
+        for (int t = 0; t < NT; ++t)
+          g.w[b][t][f] = ld16(wt[b][t] + (int64_t)((c_begin + c) * 4 + f) * FRAG);
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) g.a[mt][f] = ld16(ab + a_row_off[mt] + f * 4 * EPF);
+      for (int mt = 0; mt < MT; ++mt) g.a[mt][f] = ld16(a_frag(mt, c, f));
     }
   };
 
-  auto load_checked = [&](GemmRegs<MT, NT, NB>& g, int c) {
+  // The chunk that crosses K: weights are zero-padded there, activations past
+  // K are replaced by zeros (their memory is padding or another row).
+  auto load_tail = [&](GemmRegs<MT, NT, NB>& g, int c) {
     const int kc = k_begin + c * KC;
-    const T* ab = a_base(kc);
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
       const bool ok = kc + f * 4 * EPF + grp * EPF < k_end;
@@ -130,10 +143,9 @@ void gemm_stream_kernel(GemmArgs p) {
       for (int b = 0; b < NB; ++b)
 #pragma unroll
         for (int t = 0; t < NT; ++t)
-          g.w[b][t][f] = (ok && n_ok[t]) ? ld16(wrow[b][t] + kc + f * 4 * EPF) : zero16();
+          g.w[b][t][f] = ld16(wt[b][t] + (int64_t)((c_begin + c) * 4 + f) * FRAG);
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-        g.a[mt][f] = ok ? ld16(ab + a_row_off[mt] + f * 4 * EPF) : zero16();
+      for (int mt = 0; mt < MT; ++mt) g.a[mt][f] = ok ? ld16(a_frag(mt, c, f)) : zero16();
     }
   };
 
@@ -160,8 +172,10 @@ void gemm_stream_kernel(GemmArgs p) {
   // Main loop: batches of P full chunks. Each batch issues all of its loads,
   // then multiplies them; nothing is carried from one batch to the next, so
   // the compiler's wait counts inside a batch are exact (partial), and the
-  // other waves on the SIMD cover the gap between batches. The host sizes
-  // each wave's K range as a multiple of P chunks where it can.
+  // other waves on the SIMD cover the gap between batches (a wave that keeps
+  // two batches in registers instead measured slower: half the batch, and
+  // the SIMD's other waves already overlap). The host sizes each wave's K
+  // range as a multiple of P chunks where it can.
   const int n_batched = (n_full / P) * P;
   for (int base = 0; base < n_batched; base += P) {
     GemmRegs<MT, NT, NB> buf[P];
@@ -173,11 +187,15 @@ void gemm_stream_kernel(GemmArgs p) {
     for (int s = 0; s < P; ++s) compute(buf[s]);
     __builtin_amdgcn_sched_barrier(0);
   }
-  // Tail: leftover chunks, the partial chunk at the end of K, or every chunk
-  // of the last column tile when it is ragged.
-  for (int c = n_batched; c < nchunks; ++c) {
+  // Leftover full chunks, then the chunk that crosses K.
+  for (int c = n_batched; c < n_full; ++c) {
     GemmRegs<MT, NT, NB> g;
-    load_checked(g, c);
+    load_full(g, c);
+    compute(g);
+  }
+  if (n_full < nchunks) {
+    GemmRegs<MT, NT, NB> g;
+    load_tail(g, n_full);
     compute(g);
   }
 
@@ -201,7 +219,7 @@ void gemm_stream_kernel(GemmArgs p) {
       for (int w = 0; w < ksplit; ++w) v[b] += red[((w * NB + b) * PAIRS + pi) * 64 + lane];
     }
     const int m0 = m_base + 16 * mt + 4 * grp;
-    const int n = n0 + 16 * t + r;
+    const int n = 16 * (tile0 + t) + r;
     const bool nok = n < p.N;
     if constexpr (EPI == EPI_STORE_F32) {
       float* out = reinterpret_cast<float*>(p.out);
@@ -213,13 +231,15 @@ void gemm_stream_kernel(GemmArgs p) {
       for (int i = 0; i < 4; ++i)
         if (m0 + i < p.M && nok) p.resid[(int64_t)(m0 + i) * p.out_stride + n] += v[0][i];
     } else if constexpr (EPI == EPI_SWIGLU) {
+      // Tiled output [M, N]: the A operand of the down projection.
       T* out = reinterpret_cast<T*>(p.out);
+      const int out_nck = (p.N + KC - 1) / KC;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         if (m0 + i < p.M && nok) {
           const float gt = v[0][i];
           const float silu = gt / (1.0f + __expf(-gt));
-          out[(int64_t)(m0 + i) * p.out_stride + n] = from_f32<T>(silu * v[1][i]);
+          out[tiled_index<T>(m0 + i, n, out_nck)] = from_f32<T>(silu * v[1][i]);
         }
       }
     } else {  // EPI_ARGMAX: one (max, argmax) key per row and n-tile, merged below
@@ -253,39 +273,27 @@ void gemm_stream_kernel(GemmArgs p) {
   }
 }
 
-template <typename T, int MT, int NT, int EPI>
+template <typename T, int MT, int NT, int EPI, bool AT>
 static void launch_one(dim3 grid, dim3 block, size_t lds, const GemmArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((gemm_stream_kernel<T, MT, NT, EPI>), grid, block, lds, st, a);
+  hipLaunchKernelGGL((gemm_stream_kernel<T, MT, NT, EPI, AT>), grid, block, lds, st, a);
 }
 
-template <typename T, int EPI>
+// The (MT, NT) pairs plan_gemm produces; anything else is refused.
+template <typename T, int EPI, bool AT>
 static hipError_t dispatch(int mt, int nt, dim3 grid, dim3 block, size_t lds, const GemmArgs& a,
                            hipStream_t st) {
-  if constexpr (sizeof(T) == 4) {  // fp32 drafters: one n-tile per wave
-    switch (mt) {
-      case 1: launch_one<T, 1, 1, EPI>(grid, block, lds, a, st); break;
-      case 2: launch_one<T, 2, 1, EPI>(grid, block, lds, a, st); break;
-      case 3: launch_one<T, 3, 1, EPI>(grid, block, lds, a, st); break;
-      default: launch_one<T, 4, 1, EPI>(grid, block, lds, a, st); break;
-    }
-  } else if constexpr (EPI == EPI_SWIGLU) {  // two weight streams: fewer n-tiles fit
-    switch (mt * 10 + nt) {
-      case 11: launch_one<T, 1, 1, EPI>(grid, block, lds, a, st); break;
-      case 12: launch_one<T, 1, 2, EPI>(grid, block, lds, a, st); break;
-      case 21: launch_one<T, 2, 1, EPI>(grid, block, lds, a, st); break;
-      case 31: launch_one<T, 3, 1, EPI>(grid, block, lds, a, st); break;
-      default: launch_one<T, 4, 1, EPI>(grid, block, lds, a, st); break;
-    }
-  } else {
-    switch (mt * 10 + nt) {
-      case 11: launch_one<T, 1, 1, EPI>(grid, block, lds, a, st); break;
-      case 12: launch_one<T, 1, 2, EPI>(grid, block, lds, a, st); break;
-      case 14: launch_one<T, 1, 4, EPI>(grid, block, lds, a, st); break;
-      case 21: launch_one<T, 2, 1, EPI>(grid, block, lds, a, st); break;
-      case 22: launch_one<T, 2, 2, EPI>(grid, block, lds, a, st); break;
-      case 31: launch_one<T, 3, 1, EPI>(grid, block, lds, a, st); break;
-      default: launch_one<T, 4, 1, EPI>(grid, block, lds, a, st); break;
-    }
+  switch (mt * 10 + nt) {
+    case 11: launch_one<T, 1, 1, EPI, AT>(grid, block, lds, a, st); break;
+    case 21: launch_one<T, 2, 1, EPI, AT>(grid, block, lds, a, st); break;
+    case 31: launch_one<T, 3, 1, EPI, AT>(grid, block, lds, a, st); break;
+    case 41: launch_one<T, 4, 1, EPI, AT>(grid, block, lds, a, st); break;
+    case 22:
+      if constexpr (sizeof(T) == 2 && EPI != EPI_SWIGLU) {
+        launch_one<T, 2, 2, EPI, AT>(grid, block, lds, a, st);
+        break;
+      }
+      return hipErrorInvalidValue;
+    default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
@@ -300,16 +308,16 @@ GemmPlan plan_gemm(int dtype, int epi, int M, int N, int K, int a_seg_k) {
   g.mt = M >= 64 ? 4 : (M + 15) / 16;
   const int chunks = (K + KC - 1) / KC;
   const int col_tiles = (N + 15) / 16;
-  // Widest n-tiling (fewer activation re-reads) that still leaves >= 1024
-  // workgroups, i.e. several per CU on all 256 CUs.
+  // n-tiles per wave. With one m-tile, activation fragments are a small
+  // share of the traffic once they are tiled, and one n-tile per wave keeps
+  // the deepest load batches: it measured best or equal at every drafting
+  // shape (LM head, QKV, O, gate/up, down). With several m-tiles each weight
+  // fragment already feeds MT MFMAs; two n-tiles halve the activation
+  // re-reads where registers allow, as long as >= 1024 workgroups remain.
   g.nt = 1;
-  if (bf) {
-    // Register budget (256 VGPRs at 2 waves/SIMD) bounds the double-buffered
-    // fragments: (streams x n-tiles + m-tiles) <= 5 chunks of 16 registers.
-    const int max_nt = g.mt == 1 ? (nb == 2 ? 2 : 4) : (g.mt == 2 && nb == 1 ? 2 : 1);
+  if (bf && g.mt == 2 && nb == 1) {
     const long long rows_wg = (M + 16 * g.mt - 1) / (16 * g.mt);
-    while (g.nt < max_nt && (long long)((col_tiles + 2 * g.nt - 1) / (2 * g.nt)) * rows_wg >= 1024)
-      g.nt *= 2;
+    if ((long long)((col_tiles + 1) / 2) * rows_wg >= 1024) g.nt = 2;
   }
   g.grid_x = (N + 16 * g.nt - 1) / (16 * g.nt);
   g.grid_y = (M + 16 * g.mt - 1) / (16 * g.mt);
@@ -345,25 +353,70 @@ GemmPlan plan_gemm(int dtype, int epi, int M, int N, int K, int a_seg_k) {
 
 hipError_t launch_gemm(int dtype, int epi, const GemmArgs& a0, hipStream_t st) {
   if (a0.M <= 0 || a0.N <= 0 || a0.K <= 0) return hipSuccess;
-  const GemmPlan g = plan_gemm(dtype, epi, a0.M, a0.N, a0.K, a0.a_nseg > 1 ? a0.a_seg_k : 0);
+  // Row-major activations only come from callers, as inputs of fp32-output projections.
+  if (!a0.a_tiled && epi != EPI_STORE_F32) return hipErrorInvalidValue;
+  const bool multi = !a0.a_tiled && a0.a_nseg > 1;
+  const GemmPlan g = plan_gemm(dtype, epi, a0.M, a0.N, a0.K, multi ? a0.a_seg_k : 0);
   if (g.ksplit == 0) return hipErrorInvalidValue;
   GemmArgs a = a0;
   a.k_per_wave = g.k_per_wave;
+  if (!multi) a.a_seg_k = g.k_per_wave * g.ksplit;  // one segment covering every wave's range
   dim3 grid(g.grid_x, g.grid_y), block(64 * g.ksplit);
   if (dtype == DFLASH_BF16) {
+    if (!a.a_tiled) return dispatch<bf16, EPI_STORE_F32, false>(g.mt, g.nt, grid, block, g.lds, a, st);
     switch (epi) {
-      case EPI_STORE_F32: return dispatch<bf16, EPI_STORE_F32>(g.mt, g.nt, grid, block, g.lds, a, st);
-      case EPI_RESID: return dispatch<bf16, EPI_RESID>(g.mt, g.nt, grid, block, g.lds, a, st);
-      case EPI_SWIGLU: return dispatch<bf16, EPI_SWIGLU>(g.mt, g.nt, grid, block, g.lds, a, st);
-      default: return dispatch<bf16, EPI_ARGMAX>(g.mt, g.nt, grid, block, g.lds, a, st);
+      case EPI_STORE_F32: return dispatch<bf16, EPI_STORE_F32, true>(g.mt, g.nt, grid, block, g.lds, a, st);
+      case EPI_RESID: return dispatch<bf16, EPI_RESID, true>(g.mt, g.nt, grid, block, g.lds, a, st);
+      case EPI_SWIGLU: return dispatch<bf16, EPI_SWIGLU, true>(g.mt, g.nt, grid, block, g.lds, a, st);
+      default: return dispatch<bf16, EPI_ARGMAX, true>(g.mt, g.nt, grid, block, g.lds, a, st);
     }
   }
+  if (!a.a_tiled) return dispatch<float, EPI_STORE_F32, false>(g.mt, 1, grid, block, g.lds, a, st);
   switch (epi) {
-    case EPI_STORE_F32: return dispatch<float, EPI_STORE_F32>(g.mt, 1, grid, block, g.lds, a, st);
-    case EPI_RESID: return dispatch<float, EPI_RESID>(g.mt, 1, grid, block, g.lds, a, st);
-    case EPI_SWIGLU: return dispatch<float, EPI_SWIGLU>(g.mt, 1, grid, block, g.lds, a, st);
-    default: return dispatch<float, EPI_ARGMAX>(g.mt, 1, grid, block, g.lds, a, st);
+    case EPI_STORE_F32: return dispatch<float, EPI_STORE_F32, true>(g.mt, 1, grid, block, g.lds, a, st);
+    case EPI_RESID: return dispatch<float, EPI_RESID, true>(g.mt, 1, grid, block, g.lds, a, st);
+    case EPI_SWIGLU: return dispatch<float, EPI_SWIGLU, true>(g.mt, 1, grid, block, g.lds, a, st);
+    default: return dispatch<float, EPI_ARGMAX, true>(g.mt, 1, grid, block, g.lds, a, st);
   }
+}
+
+// One thread per 16-byte fragment of the tiled destination.
+template <typename T>
+__global__ __launch_bounds__(256) void pack_tiled_kernel(const T* __restrict__ src, int rows, int K,
+                                                         int nck, int64_t n_frags, T* __restrict__ dst) {
+  constexpr int EPF = GemmGeom<T>::EPF;
+  constexpr int KC = GemmGeom<T>::KC;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_frags; i += stride) {
+    const int lane = (int)(i & 63);
+    const int64_t q = i >> 6;
+    const int f = (int)(q & 3);
+    const int64_t blk = q >> 2;
+    const int c = (int)(blk % nck);
+    const int64_t tile = blk / nck;
+    const int64_t row = tile * 16 + (lane & 15);
+    const int k = c * KC + f * 4 * EPF + (lane >> 4) * EPF;
+    u32x4 v = zero16();
+    if (row < rows && k < K) v = ld16(src + row * K + k);
+    *reinterpret_cast<u32x4*>(dst + i * EPF) = v;
+  }
+}
+
+hipError_t launch_pack_tiled(int dtype, const void* src, int rows, int K, void* dst,
+                             hipStream_t st) {
+  if (rows <= 0 || K <= 0) return hipSuccess;
+  const int es = dtype == DFLASH_BF16 ? 2 : 4;
+  if (K % (16 / es)) return hipErrorInvalidValue;  // whole 16-byte source fragments
+  const int64_t n_frags = (int64_t)tiled_bytes(dtype, rows, K) / 16;
+  const int64_t blocks = std::min<int64_t>((n_frags + 255) / 256, 8192);
+  const int nck = tiled_nck(dtype, K);
+  if (dtype == DFLASH_BF16)
+    hipLaunchKernelGGL(pack_tiled_kernel<bf16>, dim3((unsigned)blocks), dim3(256), 0, st,
+                       (const bf16*)src, rows, K, nck, n_frags, (bf16*)dst);
+  else
+    hipLaunchKernelGGL(pack_tiled_kernel<float>, dim3((unsigned)blocks), dim3(256), 0, st,
+                       (const float*)src, rows, K, nck, n_frags, (float*)dst);
+  return hipGetLastError();
 }
 
 }  // namespace dflash

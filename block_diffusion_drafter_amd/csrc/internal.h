@@ -8,38 +8,45 @@
 
 namespace dflash {
 
-constexpr int kMaxASeg = 8;    // K-segments of the GEMM A operand (fused target features)
-constexpr int kMaxWSeg = 32;   // N-segments of the GEMM weight operand (stacked projections)
+constexpr int kMaxASeg = 8;    // K-segments of a row-major GEMM A operand (fused target features)
 constexpr int kKeyBlock = 32;  // V cache position block
 constexpr int kMaxLayers = 16;
 
 enum Epilogue : int {
   EPI_STORE_F32 = 0,  // out (fp32) = acc
   EPI_RESID = 1,      // resid (fp32) += acc
-  EPI_SWIGLU = 2,     // out (model dtype) = SiLU(acc_gate) * acc_up
+  EPI_SWIGLU = 2,     // out (model dtype, tiled) = SiLU(acc_gate) * acc_up
   EPI_ARGMAX = 3,     // per-row (max, argmax) over the tile -> partial keys; optional fp32 logits
 };
 
+// Chunk width (elements) and chunk count of the tiled layout for a dtype.
+inline int tiled_kc(int dtype) { return dtype == DFLASH_BF16 ? 128 : 64; }
+inline int tiled_nck(int dtype, int K) { return (K + tiled_kc(dtype) - 1) / tiled_kc(dtype); }
+// Bytes of a tiled [rows, K] matrix (rows padded to 16, k to the chunk).
+inline size_t tiled_bytes(int dtype, int64_t rows, int K) {
+  return (size_t)((rows + 15) / 16) * 16 * (size_t)tiled_nck(dtype, K) * tiled_kc(dtype) *
+         (dtype == DFLASH_BF16 ? 2 : 4);
+}
+
 // Y[M, N] = A[M, K] · W[N, K]^T with a fused epilogue.
-//  A: row m, column k lives at a[k / a_seg_k] + m * a_stride + k % a_seg_k
-//     (a_nseg > 1 concatenates several [M, a_seg_k] matrices along k).
-//  W: output column n lives in segment s with w_row0[s] <= n < w_row0[s+1],
-//     row n - w_row0[s] of w[s] ([rows, K], row-major). For EPI_SWIGLU, w2
-//     holds the second (up) matrix with the same segmentation.
+//  W (and w2, the up matrix of EPI_SWIGLU): tiled [N, K] (layout in common.h).
+//  A: a_tiled = 1: a[0] is a tiled [M, K] matrix (activations the library
+//     wrote itself); a_tiled = 0: row-major, row m, column k at
+//     a[k / a_seg_k] + m * a_stride + k % a_seg_k (caller inputs; a_nseg > 1
+//     places several [M, a_seg_k] matrices side by side along k).
 struct GemmArgs {
   const void* a[kMaxASeg];
   int64_t a_stride;
   int a_seg_k;
   int a_nseg;
-  const void* w[kMaxWSeg];
-  const void* w2[kMaxWSeg];
-  int w_row0[kMaxWSeg + 1];
-  int w_nseg;
+  int a_tiled;
+  const void* w;
+  const void* w2;
   int M, N, K;
   int k_per_wave;                 // K range per wave (multiple of the chunk)
-  void* out;                      // EPI_STORE_F32 (fp32) / EPI_SWIGLU (model dtype)
+  void* out;                      // EPI_STORE_F32: fp32 [M, out_stride]; EPI_SWIGLU: tiled [M, N]
   int64_t out_stride;
-  float* resid;                   // EPI_RESID
+  float* resid;                   // EPI_RESID: fp32 [M, out_stride]
   unsigned long long* amax;       // EPI_ARGMAX: [M][n_tiles] partial keys
   int64_t amax_stride;
   float* logits;                  // EPI_ARGMAX, optional
@@ -58,6 +65,11 @@ struct GemmPlan {
 GemmPlan plan_gemm(int dtype, int epi, int M, int N, int K, int a_seg_k);
 hipError_t launch_gemm(int dtype, int epi, const GemmArgs& args, hipStream_t st);
 
+// Tiled copy of a row-major [rows, K] matrix (row stride K) into dst, which
+// holds the whole tiled [rows, K] matrix; padding is written as zeros.
+hipError_t launch_pack_tiled(int dtype, const void* src, int rows, int K, void* dst,
+                             hipStream_t st);
+
 struct AttnArgs {
   const void* q;         // [batch][n_heads][16][head_dim] model dtype, rows >= B are zero
   const void* k;         // this layer's K cache base: [cache_batch][Hkv][cap][hd]
@@ -69,8 +81,9 @@ struct AttnArgs {
   float scale_log2;      // log2(e) / sqrt(head_dim)
   float* part_o;         // [batch][Hkv][max_chunks][G][hd][16]
   float* part_ml;        // [batch][Hkv][max_chunks][G][16][2]  (running max in log2 units, sum)
-  void* out;             // [batch*B][n_heads*hd] model dtype; written by the partial kernel
-                         // when a sequence fits in one chunk, else by the combine
+  void* out;             // tiled [batch*B, n_heads*hd] model dtype (out_nck chunks per row);
+  int out_nck;           // written by the partial kernel when a sequence fits in one
+                         // chunk, else by the combine
 };
 
 hipError_t launch_attention(int dtype, const AttnArgs& a, hipStream_t st);
@@ -103,11 +116,13 @@ hipError_t launch_norm_rope_forward(int dtype, const NormRopeArgs& a, hipStream_
 hipError_t launch_norm_rope_append(int dtype, const NormRopeArgs& a, hipStream_t st);
 
 // y[r] = RMSNorm(x[src_row(r)]) * gain, src_row(r) = (r / rpg) * grp_stride + grp_off + r % rpg.
+// y is row-major with y_stride when y_nck == 0, else tiled [rows, d] with y_nck chunks.
 hipError_t launch_rmsnorm(int dtype, const float* x, int64_t x_stride, const void* gain, void* y,
-                          int64_t y_stride, int rows, int d, float eps, int rpg, int grp_stride,
-                          int grp_off, hipStream_t st);
+                          int64_t y_stride, int y_nck, int rows, int d, float eps, int rpg,
+                          int grp_stride, int grp_off, hipStream_t st);
 
-// Block embedding into the fp32 residual x, plus h = RMSNorm(x; gain) for layer 0.
+// Block embedding into the fp32 residual x, plus h = RMSNorm(x; gain) for
+// layer 0, h tiled [batch*block, d].
 hipError_t launch_embed(int dtype, const void* embed, const int32_t* anchor, int batch, int block,
                         int d, int vocab, int mask_id, float* x, const void* gain, float eps,
                         void* h, int32_t* dev_status, hipStream_t st);

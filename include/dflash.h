@@ -12,15 +12,18 @@
  * Conventions shared by every call
  * --------------------------------
  *  - Every tensor argument is CALLER-OWNED DEVICE MEMORY on the current HIP
- *    device. The library never allocates, frees or retains device memory; it
- *    only reads and writes the buffers it is given for the duration of the
- *    call's kernels. Scratch space comes from the caller's workspace.
+ *    device. The library never allocates or frees device memory; it reads
+ *    and writes the buffers it is given, and a handle keeps the weight
+ *    pointers of dflash_create. Scratch space comes from the caller's
+ *    workspace.
  *  - Every compute call takes the caller's stream (a hipStream_t passed as
  *    void*) and is asynchronous on it: it enqueues kernels and returns; it
  *    never synchronises the device. Results are valid once the stream reaches
  *    that point.
- *  - Weights are row-major [out, in] (the Linear layout), all in the model
- *    dtype (DFLASH_BF16 or DFLASH_FP32), norm gains included.
+ *  - Weights are given row-major [out, in] (the Linear layout), all in the
+ *    model dtype (DFLASH_BF16 or DFLASH_FP32), norm gains included; the
+ *    projections are read from a tiled copy the caller has
+ *    dflash_pack_weights write once (see there).
  *  - Every device pointer must be 16-byte aligned.
  *  - Return value: DFLASH_OK (0) or a negative dflash_status. Arguments are
  *    validated on the host before anything is enqueued; a call that returns an
@@ -49,7 +52,7 @@ typedef enum dflash_status {
   DFLASH_ERR_SHAPE = -2,         /* a size is out of range or inconsistent */
   DFLASH_ERR_DTYPE = -3,         /* unknown dtype */
   DFLASH_ERR_ALIGN = -4,         /* a pointer or stride breaks 16-byte alignment */
-  DFLASH_ERR_WORKSPACE = -5,     /* workspace smaller than dflash_workspace_bytes() */
+  DFLASH_ERR_WORKSPACE = -5,     /* workspace or packed buffer smaller than its size query */
   DFLASH_ERR_UNSUPPORTED = -6,   /* a configuration the kernels do not cover */
   DFLASH_ERR_HIP = -7,           /* a HIP launch reported an error */
   DFLASH_ERR_STATE = -8          /* profiler misuse */
@@ -94,10 +97,19 @@ typedef struct dflash_layer_weights {
 
 /* embed, lm_head [vocab, d] (may alias); fc [d, n_target_feats*target_hidden];
  * fc_norm, final_norm [d]; layers: host array of n_layers entries (copied by
- * dflash_create; the device buffers it points to must outlive the handle). */
+ * dflash_create).
+ * packed: the tiled copy of the projection weights that dflash_pack_weights
+ * wrote for this configuration and these weights (packed_bytes: its size,
+ * at least dflash_packed_weight_bytes). Every projection (wq, wk, wv, wo,
+ * w_gate, w_up, w_down, fc, lm_head) is read from it, never from the row-major
+ * matrices; embed, the norm gains and packed are read by every call and must
+ * outlive the handle. dflash_create checks packed's size and alignment, not
+ * its content. */
 typedef struct dflash_weights {
   const void *embed, *lm_head, *fc, *fc_norm, *final_norm;
   const dflash_layer_weights *layers;
+  const void *packed;
+  int64_t packed_bytes;
 } dflash_weights;
 
 /* Per-layer context K/V cache, caller-owned, model dtype.
@@ -119,7 +131,34 @@ typedef struct dflash_kv_cache {
 
 typedef struct dflash_handle dflash_handle;
 
-/* Validate the shape and keep a copy of the weight pointers.
+/* Tiled weight copy. The projections stream their weights from one copy in
+ * the order the matrix-core loop consumes them: rows in tiles of 16, the
+ * input dimension in chunks of 256 bytes, and inside each (row tile, chunk)
+ * four 1 KB fragments, fragment f holding for lane l = r + 16 g the 16 bytes
+ * of row r at element 16*EPF*c + 4*EPF*f + EPF*g (EPF = 8 for bf16, 4 for
+ * fp32), zero-padded to whole tiles and chunks. Every load of a wave then
+ * reads one contiguous kilobyte. The copy holds, per layer, [wq; wk; wv]
+ * stacked, wo, w_gate, w_up, w_down; then fc; then every layer's [wk; wv]
+ * stacked (the context K/V projection); then lm_head.
+ *
+ * dflash_packed_weight_bytes: bytes of the copy for cfg (negative
+ * dflash_status on a bad cfg).
+ * dflash_pack_weights: enqueue on stream the kernels that write the copy of
+ * w's projections into packed (caller-owned device memory of packed_bytes
+ * bytes). Reads lm_head, fc and each layer's wq, wk, wv, wo, w_gate, w_up,
+ * w_down; once stream has passed the call, those row-major matrices are no
+ * longer needed by the library. Errors: DFLASH_ERR_NULL / _ALIGN for a
+ * missing or misaligned matrix or packed, DFLASH_ERR_WORKSPACE when
+ * packed_bytes is too small, config errors as dflash_create. */
+int64_t dflash_packed_weight_bytes(const dflash_config *cfg);
+int32_t dflash_pack_weights(const dflash_config *cfg, const dflash_weights *w, void *packed,
+                            int64_t packed_bytes, void *stream);
+
+/* Validate the shape and keep a copy of the weight pointers (no device work:
+ * packed must already hold dflash_pack_weights' output before the first call
+ * that uses the handle runs). Needs embed, fc_norm, final_norm, packed and
+ * each layer's in_norm, q_norm, k_norm, post_norm; the row-major projection
+ * pointers may be NULL. DFLASH_ERR_WORKSPACE when packed_bytes is too small.
  * Returns DFLASH_OK and *out, or an error with *out = NULL. */
 int32_t dflash_create(const dflash_config *cfg, const dflash_weights *w, dflash_handle **out);
 void dflash_destroy(dflash_handle *h);

@@ -44,7 +44,7 @@ def fake_weights(n_layers):
         for f in B.LAYER_FIELDS:
             setattr(layers[l], f, FAKE)
     w = B.WeightsStruct(FAKE, FAKE, FAKE, FAKE, FAKE,
-                        ctypes.cast(layers, ctypes.POINTER(B.LayerWeights)))
+                        ctypes.cast(layers, ctypes.POINTER(B.LayerWeights)), FAKE, 1 << 40)
     return w, layers
 
 
@@ -82,12 +82,76 @@ def test_create_rejects_bad_config(field, value, code):
 def test_create_rejects_null_and_misaligned_weights():
     c = B.make_config(TINY_FP32)
     w, layers = fake_weights(1)
-    layers[0].wq = None
     h = ctypes.c_void_p()
-    assert B.lib().dflash_create(ctypes.byref(c), ctypes.byref(w), ctypes.byref(h)) == -1
-    layers[0].wq = FAKE + 4
-    assert B.lib().dflash_create(ctypes.byref(c), ctypes.byref(w), ctypes.byref(h)) == -4
+    create_ = lambda: B.lib().dflash_create(ctypes.byref(c), ctypes.byref(w), ctypes.byref(h))
+    layers[0].q_norm = None
+    assert create_() == -1
+    layers[0].q_norm = FAKE + 4
+    assert create_() == -4
+    layers[0].q_norm = FAKE
+    # the row-major projections are only read by dflash_pack_weights
+    layers[0].wq = None
+    w.lm_head = None
+    assert create_() == 0 and h.value
+    B.lib().dflash_destroy(h)
+    w.packed = None
+    assert create_() == -1
+    w.packed = FAKE + 8
+    assert create_() == -4
+    w.packed = FAKE
+    w.packed_bytes = B.lib().dflash_packed_weight_bytes(ctypes.byref(c)) - 1
+    assert create_() == -5
     assert B.lib().dflash_create(ctypes.byref(c), ctypes.byref(w), None) == -1
+
+
+def tiled_bytes(rows, k, es):
+    kc = 256 // es
+    return -(-rows // 16) * 16 * (-(-k // kc) * kc) * es
+
+
+def expected_packed_bytes(cfg):
+    """Sizes of the tiled copies, each on a 256-byte boundary, in the order the
+    header lists them."""
+    es = 2 if cfg.dtype == "bf16" else 4
+    d, q, kv, i = cfg.hidden, cfg.n_heads * cfg.head_dim, cfg.n_kv_heads * cfg.head_dim, cfg.intermediate
+    parts = []
+    for _ in range(cfg.n_layers):
+        parts += [tiled_bytes(q + 2 * kv, d, es), tiled_bytes(d, q, es), tiled_bytes(i, d, es),
+                  tiled_bytes(i, d, es), tiled_bytes(d, i, es)]
+    parts += [tiled_bytes(d, cfg.n_target_feats * cfg.target_hidden, es),
+              tiled_bytes(cfg.n_layers * 2 * kv, d, es), tiled_bytes(cfg.vocab, d, es)]
+    return sum(-(-p // 256) * 256 for p in parts)
+
+
+@pytest.mark.parametrize("cfg", [TINY_FP32, QWEN3_8B_SHAPED], ids=lambda c: c.name)
+def test_packed_weight_bytes(cfg):
+    lib = B.lib()
+    c = B.make_config(cfg)
+    n = lib.dflash_packed_weight_bytes(ctypes.byref(c))
+    assert n == expected_packed_bytes(cfg)
+    assert lib.dflash_packed_weight_bytes(None) == -1
+    c.head_dim = 96
+    assert lib.dflash_packed_weight_bytes(ctypes.byref(c)) == -6
+
+
+def test_pack_weights_rejects_bad_arguments_before_launching():
+    lib = B.lib()
+    c = B.make_config(TINY_FP32)
+    w, layers = fake_weights(1)
+    n = lib.dflash_packed_weight_bytes(ctypes.byref(c))
+    pack = lambda dst=FAKE, nb=n: lib.dflash_pack_weights(ctypes.byref(c), ctypes.byref(w), dst,
+                                                          nb, None)
+    assert pack(dst=None) == -1
+    assert pack(dst=FAKE + 4) == -4
+    assert pack(nb=n - 1) == -5
+    layers[0].w_down = None
+    assert pack() == -1
+    layers[0].w_down = FAKE + 2
+    assert pack() == -4
+    layers[0].w_down = FAKE
+    w.fc = None
+    assert pack() == -1
+    assert lib.dflash_pack_weights(None, ctypes.byref(w), FAKE, n, None) == -1
 
 
 def test_calls_reject_bad_arguments_before_launching():
