@@ -145,7 +145,7 @@ Plan make_plan(const dflash_config& c, int batch, int cap, int max_tokens) {
   const size_t R = (size_t)batch * (B - 1);
   p.y = take(tiled_bytes(dt, (int64_t)R, (int)d));
   // LM head: one (max, argmax) key per row and workgroup column.
-  p.n_vtiles = R > 0 ? plan_gemm(c.dtype, EPI_ARGMAX, (int)R, c.vocab, c.hidden, 0).grid_x : 1;
+  p.n_vtiles = R > 0 ? gemm_amax_cols(c.dtype, (int)R, c.vocab, c.hidden) : 1;
   p.amax = take(R * p.n_vtiles * 8);
   p.fwd_end = off;
   off = 0;

@@ -1,0 +1,367 @@
+// MFMA-bound GEMM for batched drafting: Y = A · W^T with A [M, K] tiled
+// activations (hundreds of rows) and W [N, K] tiled weights, bf16 in, fp32
+// accumulation, the same fused epilogues as the weight-streaming kernel.
+//
+// At a few hundred rows every projection does ~400+ flops per weight byte,
+// above the chip's ridge point, so the kernel is organised around the matrix
+// cores:
+//   * a workgroup owns a BM x BN output block (256x256 with 8 waves, or
+//     128x128 with 4 for narrow projections); each wave a (BM/WGM) x (BN/WGN)
+//     sub-block of 16x16 MFMA tiles held in registers;
+//   * K advances in stages of 32 or 64. A stage of A and W is copied from
+//     the tiled layout into LDS unchanged by direct global->LDS loads
+//     (global_load_lds_dwordx4: one 1 KB fragment per wave instruction, no
+//     registers), and every LDS read of an MFMA operand is 64 lanes x 16
+//     contiguous bytes (no bank conflicts, no shuffles);
+//   * the stages form a ring of NS slots in LDS with NS-1 stages in flight,
+//     so each stage's loads have NS-2 stages of MFMA work to arrive; one
+//     wait + barrier per stage (a register-staged double buffer left the
+//     matrix cores idle on load latency at every stage);
+//   * workgroups that share a column block but differ in row block are
+//     numbered 8 apart, so they run on the same XCD at about the same time
+//     and the second reads the weight block from that XCD's L2.
+#include <algorithm>
+
+#include "common.h"
+#include "internal.h"
+
+namespace dflash {
+
+namespace {
+
+constexpr int kEPF = 8;          // bf16 per 16-byte fragment
+constexpr int kKC = 128;         // k per tiled chunk
+constexpr int kFRAG = 64 * kEPF; // elements of one 1 KB wave-wide fragment
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef const __attribute__((address_space(1))) void* gbl_ptr_t;
+
+// KF fragments per tile per stage (stage k = 32 KF), NS ring slots.
+template <int BM, int BN, int WGM, int WGN, int KF, int NS>
+struct MfmaGeom {
+  static constexpr int NW = WGM * WGN;
+  static constexpr int WM = BM / WGM, WN = BN / WGN;
+  static constexpr int TM = WM / 16, TN = WN / 16;  // 16x16 tiles per wave
+  static constexpr int AT = BM / 16, BT = BN / 16;  // row tiles of A / W in a block
+  static constexpr int SF = (AT + BT) * KF;         // fragments per stage
+  static constexpr int FPW = SF / NW;               // fragments each wave copies per stage
+  static_assert(SF % NW == 0, "stage fragments must split evenly over the waves");
+  static_assert(NS >= 2, "ring needs a slot being read and one arriving");
+};
+
+// Wait until at most N of this wave's global->LDS loads are outstanding and
+// all of its LDS reads have returned, then meet the other waves. The memory
+// clobber keeps the compiler from moving LDS accesses across it.
+template <int N>
+__device__ __forceinline__ void wait_loads_and_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+}  // namespace
+
+// One workgroup per CU (the LDS ring takes most of it): WGM*WGN/4 waves per
+// SIMD, which lets the compiler spend registers on two stages of operands.
+template <int BM, int BN, int WGM, int WGN, int KF, int NS, int EPI>
+__global__ __launch_bounds__(64 * WGM * WGN)
+__attribute__((amdgpu_waves_per_eu(WGM * WGN / 4, WGM * WGN / 4)))
+void gemm_mfma_kernel(GemmArgs p, int n_colblk, int n_rowblk) {
+  using G = MfmaGeom<BM, BN, WGM, WGN, KF, NS>;
+  constexpr bool PF = WGM * WGN == 4;  // one wave per SIMD: prefetch operands in registers
+  constexpr int TM = G::TM, TN = G::TN, AT = G::AT, BT = G::BT, SF = G::SF, FPW = G::FPW;
+  constexpr int NW = G::NW;
+  __shared__ u32x4 lds[NS][SF][64];
+  __shared__ unsigned long long kred[EPI == EPI_ARGMAX ? BM * WGN : 1];
+
+  // Block numbering: ids 8 apart share an XCD; row blocks of one column block
+  // get consecutive multiples of 8.
+  const int id = blockIdx.x;
+  const int xcd = id & 7, q = id >> 3;
+  const int rb = q % n_rowblk;
+  const int cb = (q / n_rowblk) * 8 + xcd;
+  if (cb >= n_colblk) return;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave / WGN, wn = wave % WGN;
+  const int r = lane & 15, grp = lane >> 4;
+  const int nck = (p.K + kKC - 1) / kKC;
+  const int nst = p.K / (32 * KF);  // the host guarantees K % (32 KF) == 0
+  const int m_tiles = (p.M + 15) >> 4, n_tiles = (p.N + 15) >> 4;
+  const int tile_m0 = rb * AT;
+  // SwiGLU: the block's W tiles are BT/2 gate tiles then the same BT/2 up tiles.
+  constexpr bool SW = EPI == EPI_SWIGLU;
+  const int tile_n0 = cb * (SW ? BT / 2 : BT);
+
+  const bf16* A = reinterpret_cast<const bf16*>(p.a[0]);
+  const bf16* W = reinterpret_cast<const bf16*>(p.w);
+  const bf16* W2 = reinterpret_cast<const bf16*>(p.w2);
+
+  // Fragments this wave copies per stage: j = wave + NW * i. Stage slot j:
+  // j < KF*AT: A row tile j / KF, fragment j % KF of the stage; else W tile
+  // (j - KF*AT) / KF. Tiles past the matrix re-read its last tile (valid
+  // memory; those rows and columns are never stored). Bases are wave-uniform.
+  const bf16* src[FPW];
+  int kf[FPW];
+#pragma unroll
+  for (int i = 0; i < FPW; ++i) {
+    const int j = wave + NW * i;
+    kf[i] = j % KF;
+    if (j < KF * AT) {
+      const int t = min(tile_m0 + j / KF, m_tiles - 1);
+      src[i] = A + (int64_t)t * nck * 4 * kFRAG;
+    } else {
+      const int bt = (j - KF * AT) / KF;
+      const bf16* base = W;
+      int t = tile_n0 + bt;
+      if constexpr (SW) {
+        if (bt >= BT / 2) {
+          base = W2;
+          t = tile_n0 + bt - BT / 2;
+        }
+      }
+      t = min(t, n_tiles - 1);
+      src[i] = base + (int64_t)t * nck * 4 * kFRAG;
+    }
+  }
+
+  // Stage s covers fragments KF*s .. KF*s + KF-1 of each tile's K (fragment
+  // g = 4 * chunk + f sits at element g * kFRAG of the tile).
+  auto issue = [&](int s, int slot) {
+#pragma unroll
+    for (int i = 0; i < FPW; ++i) {
+      const bf16* g = src[i] + (int64_t)(KF * s + kf[i]) * kFRAG + lane * kEPF;
+      __builtin_amdgcn_global_load_lds((gbl_ptr_t)g, (lds_ptr_t)&lds[slot][wave + NW * i][0], 16, 0,
+                                       0);
+    }
+  };
+
+  f32x4 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // LDS index of the wave's B tile j (SwiGLU: first TN/2 gate, then up).
+  auto btile = [&](int j) -> int {
+    if constexpr (SW) return j < TN / 2 ? wn * (TN / 2) + j : BT / 2 + wn * (TN / 2) + j - TN / 2;
+    else return wn * TN + j;
+  };
+
+  // One stage's MFMA operands in registers.
+  struct Frags {
+    u32x4 a[KF][TM];
+    u32x4 b[KF][TN];
+  };
+  auto lds_read = [&](Frags& F, int slot) {
+#pragma unroll
+    for (int k2 = 0; k2 < KF; ++k2) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i) F.a[k2][i] = lds[slot][(wm * TM + i) * KF + k2][lane];
+#pragma unroll
+      for (int j = 0; j < TN; ++j) F.b[k2][j] = lds[slot][KF * AT + btile(j) * KF + k2][lane];
+    }
+  };
+  // The stage's MFMAs, with the next stage's LDS reads (if any) interleaved:
+  // one read per MFMA_PER_READ MFMAs, so the reads' latency hides under the
+  // matrix work of this wave instead of stalling it.
+  constexpr int NMFMA = KF * TM * TN, NREAD = KF * (TM + TN);
+  constexpr int MFMA_PER_READ = NMFMA / NREAD > 0 ? NMFMA / NREAD : 1;
+  auto mma = [&](const Frags& F, Frags* next, int next_slot) {
+    if (next) lds_read(*next, next_slot);
+#pragma unroll
+    for (int k2 = 0; k2 < KF; ++k2)
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = mfma_frag<bf16>(F.a[k2][i], F.b[k2][j], acc[i][j]);
+    if (next) {
+#pragma unroll
+      for (int g = 0; g < NREAD; ++g) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);              // one LDS read
+        __builtin_amdgcn_sched_group_barrier(0x008, MFMA_PER_READ, 0);  // then MFMAs
+      }
+    }
+  };
+
+  // Ring of NS slots, all NS filled up front. Iteration s: every wave's LDS
+  // reads of stage s have returned (its operands are in registers) and every
+  // wave passes the barrier, so slot s % NS is free and stage s + NS is issued
+  // into it; stage s + 1 has landed (each wave waited for its own loads
+  // before the barrier). With one wave per SIMD (PF) stage s+1's LDS reads go
+  // out between stage s's MFMAs; with two, the other wave on the SIMD covers
+  // them and the operands of one stage at a time fit the registers.
+#pragma unroll
+  for (int st = 0; st < NS; ++st)
+    if (st < nst) issue(st, st);
+  if (nst >= NS) wait_loads_and_barrier<FPW * (NS - 1)>();
+  else wait_loads_and_barrier<0>();
+  if constexpr (PF) {
+    Frags f0, f1;
+    lds_read(f0, 0);
+    auto step = [&](int s, Frags& cur, Frags& nxt) {
+      const int slot = s % NS;
+      if (s + 1 < nst) {
+        // Issued so far: stages up to min(nst, s + NS) - 1, so stage s+1 has
+        // landed once at most min(NS - 2, nst - 2 - s) later stages are outstanding.
+        if (s + NS <= nst) wait_loads_and_barrier<FPW * (NS - 2)>();
+        else wait_loads_and_barrier<0>();
+        if (s + NS < nst) issue(s + NS, slot);
+        mma(cur, &nxt, (s + 1) % NS);
+      } else {
+        mma(cur, nullptr, 0);
+      }
+    };
+    int s = 0;
+    for (; s + 1 < nst; s += 2) {
+      step(s, f0, f1);
+      step(s + 1, f1, f0);
+    }
+    if (s < nst) step(s, f0, f1);
+  } else {
+    for (int s = 0; s < nst; ++s) {
+      const int slot = s % NS;
+      Frags f;
+      lds_read(f, slot);
+      mma(f, nullptr, 0);
+      if (s + 1 < nst) {
+        // The reads of stage s are done (lgkmcnt) before the barrier frees its slot.
+        if (s + NS <= nst) wait_loads_and_barrier<FPW * (NS - 2)>();
+        else wait_loads_and_barrier<0>();
+        if (s + NS < nst) issue(s + NS, slot);
+      }
+    }
+  }
+  __syncthreads();
+
+  // Epilogue. Lane (r, grp) of tile (i, j) holds rows 4*grp + e of column r.
+  const int row0 = tile_m0 * 16 + wm * (TM * 16);
+  if constexpr (EPI == EPI_ARGMAX) {
+    // Per row: max over this wave's columns, then over the WGN waves via LDS.
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int m = row0 + 16 * i + 4 * grp + e;
+        unsigned long long key = 0ull;
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const int n = (tile_n0 + wn * TN + j) * 16 + r;
+          if (n < p.N) {
+            if (p.logits && m < p.M) p.logits[(int64_t)m * p.logits_stride + n] = acc[i][j][e];
+            const unsigned long long k = argmax_key(acc[i][j][e], (unsigned)n);
+            key = k > key ? k : key;
+          }
+        }
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) {
+          const unsigned long long other = __shfl_xor(key, o);
+          key = other > key ? other : key;
+        }
+        if (r == 0) kred[(wm * TM * 16 + 16 * i + 4 * grp + e) * WGN + wn] = key;
+      }
+    }
+    __syncthreads();
+    for (int row = threadIdx.x; row < BM; row += 64 * NW) {
+      const int m = tile_m0 * 16 + row;
+      if (m < p.M) {
+        unsigned long long best = 0ull;
+#pragma unroll
+        for (int w = 0; w < WGN; ++w) {
+          const unsigned long long k = kred[row * WGN + w];
+          best = k > best ? k : best;
+        }
+        p.amax[(int64_t)m * p.amax_stride + cb] = best;
+      }
+    }
+  } else if constexpr (SW) {
+    bf16* out = reinterpret_cast<bf16*>(p.out);
+    const int out_nck = (p.N + kKC - 1) / kKC;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN / 2; ++j) {
+        const int n = (tile_n0 + wn * (TN / 2) + j) * 16 + r;
+        if (n >= p.N) continue;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int m = row0 + 16 * i + 4 * grp + e;
+          if (m < p.M) {
+            const float gt = acc[i][j][e];
+            const float silu = gt / (1.0f + __expf(-gt));
+            out[tiled_index<bf16>(m, n, out_nck)] = (bf16)(silu * acc[i][j + TN / 2][e]);
+          }
+        }
+      }
+  } else {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int n = (tile_n0 + wn * TN + j) * 16 + r;
+        if (n >= p.N) continue;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int m = row0 + 16 * i + 4 * grp + e;
+          if (m >= p.M) continue;
+          if constexpr (EPI == EPI_STORE_F32)
+            reinterpret_cast<float*>(p.out)[(int64_t)m * p.out_stride + n] = acc[i][j][e];
+          else
+            p.resid[(int64_t)m * p.out_stride + n] += acc[i][j][e];
+        }
+      }
+  }
+}
+
+// Column blocks per launch for an epilogue: SwiGLU blocks hold BN/2 output
+// columns (gate and up tiles side by side).
+static int mfma_colblocks(int epi, int N, int BN) {
+  const int cols = epi == EPI_SWIGLU ? BN / 2 : BN;
+  return (N + cols - 1) / cols;
+}
+
+// Block shape: 256x256 (8 waves of 128x64) reads the fewest operand bytes per
+// flop (1/128 B) and is used when it still gives >= 192 workgroups; narrower
+// projections (QKV, O, down at a few hundred rows) take 128x128 blocks
+// (4 waves of 64x64, twice the operand traffic per flop, four times the
+// workgroups), so that most CUs have a block.
+static int mfma_block(int epi, int M, int N) {
+  const long long big = (long long)((M + 255) / 256) * mfma_colblocks(epi, N, 256);
+  return big >= 192 ? 256 : 128;
+}
+
+int mfma_gemm_colblocks(int epi, int M, int N) {
+  return mfma_colblocks(epi, N, mfma_block(epi, M, N));
+}
+
+template <int BM, int BN, int WGM, int WGN, int KF, int NS, int EPI>
+static hipError_t launch_mfma_t(const GemmArgs& a, hipStream_t st) {
+  const int n_colblk = mfma_colblocks(EPI, a.N, BN);
+  const int n_rowblk = (a.M + BM - 1) / BM;
+  const int groups = (n_colblk + 7) / 8;
+  const dim3 grid(groups * 8 * n_rowblk), block(64 * WGM * WGN);
+  hipLaunchKernelGGL((gemm_mfma_kernel<BM, BN, WGM, WGN, KF, NS, EPI>), grid, block, 0, st, a,
+                     n_colblk, n_rowblk);
+  return hipGetLastError();
+}
+
+template <int EPI>
+static hipError_t launch_mfma_epi(const GemmArgs& a, hipStream_t st) {
+  // 256x256: 8 waves of 128x64, stages of k=64 (64 KB) in 2 slots.
+  // 128x128: 4 waves of 64x64, stages of k=64 (32 KB) in 4 slots.
+  // (Measured best of the block / stage / ring combinations at these shapes.)
+  if (mfma_block(EPI, a.M, a.N) == 256) return launch_mfma_t<256, 256, 2, 4, 2, 2, EPI>(a, st);
+  return launch_mfma_t<128, 128, 2, 2, 2, 4, EPI>(a, st);
+}
+
+hipError_t launch_gemm_mfma(int epi, const GemmArgs& a, hipStream_t st) {
+  if (a.M <= 0 || a.N <= 0 || a.K <= 0) return hipSuccess;
+  if (!a.a_tiled || a.K % 64) return hipErrorInvalidValue;
+  switch (epi) {
+    case EPI_STORE_F32: return launch_mfma_epi<EPI_STORE_F32>(a, st);
+    case EPI_RESID: return launch_mfma_epi<EPI_RESID>(a, st);
+    case EPI_SWIGLU: return launch_mfma_epi<EPI_SWIGLU>(a, st);
+    default: return launch_mfma_epi<EPI_ARGMAX>(a, st);
+  }
+}
+
+}  // namespace dflash

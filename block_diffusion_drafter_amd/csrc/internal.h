@@ -65,6 +65,18 @@ struct GemmPlan {
 GemmPlan plan_gemm(int dtype, int epi, int M, int N, int K, int a_seg_k);
 hipError_t launch_gemm(int dtype, int epi, const GemmArgs& args, hipStream_t st);
 
+// Projections of at least kMfmaMinRows tiled bf16 rows with K a multiple of
+// 64 run on the MFMA-bound LDS-tiled kernel (gemm_mfma.hip), the others on
+// the weight-streaming one.
+constexpr int kMfmaMinRows = 128;
+inline bool gemm_uses_mfma(int dtype, int M, int K, bool a_tiled) {
+  return dtype == DFLASH_BF16 && a_tiled && M >= kMfmaMinRows && K % 64 == 0;
+}
+hipError_t launch_gemm_mfma(int epi, const GemmArgs& a, hipStream_t st);
+int mfma_gemm_colblocks(int epi, int M, int N);
+// Keys per row that the LM-head projection writes (its column blocks).
+int gemm_amax_cols(int dtype, int M, int N, int K);
+
 // Tiled copy of a row-major [rows, K] matrix (row stride K) into dst, which
 // holds the whole tiled [rows, K] matrix; padding is written as zeros.
 hipError_t launch_pack_tiled(int dtype, const void* src, int rows, int K, void* dst,
