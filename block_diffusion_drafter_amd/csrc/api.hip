@@ -102,8 +102,8 @@ PackedLayout packed_layout(const dflash_config& c) {
 
 struct Plan {
   size_t x, h, qkv, q, po, pml, attn, act, y, amax, fwd_end;
-  size_t u, proj_end;
-  size_t kv, app_end;
+  size_t u, ua, proj_end;  // ua: tiled copy of the fused features (MFMA path)
+  size_t kv, ca, app_end;  // ca: tiled copy of the context rows (MFMA path)
   int chunk, max_chunks, n_vtiles;
   size_t total;
 };
@@ -150,9 +150,12 @@ Plan make_plan(const dflash_config& c, int batch, int cap, int max_tokens) {
   p.fwd_end = off;
   off = 0;
   p.u = take((size_t)max_tokens * d * 4);
+  const int fk = c.n_target_feats * c.target_hidden;
+  p.ua = gemm_uses_mfma(dt, max_tokens, fk, true) ? take(tiled_bytes(dt, max_tokens, fk)) : 0;
   p.proj_end = off;
   off = 0;
   p.kv = take((size_t)max_tokens * c.n_layers * 2 * Hkv * hd * 4);
+  p.ca = gemm_uses_mfma(dt, max_tokens, (int)d, true) ? take(tiled_bytes(dt, max_tokens, (int)d)) : 0;
   p.app_end = off;
   p.total = std::max(p.fwd_end, std::max(p.proj_end, p.app_end));
   return p;
@@ -284,8 +287,8 @@ int32_t dflash_pack_weights(const dflash_config* cfg, const dflash_weights* w, v
   // Stacked matrices: each part starts on a 16-row tile boundary (q_dim and
   // kv_dim are multiples of 16), so a part is packed at its rows' byte offset.
   auto pack = [&](const void* src, int rows, int K, size_t off, int64_t row0) {
-    return launch_pack_tiled(dt, src, rows, K, base + off + tiled_bytes(dt, row0, K), st) ==
-           hipSuccess;
+    return launch_pack_tiled(dt, pack_src(src, K), rows, K, base + off + tiled_bytes(dt, row0, K),
+                             st) == hipSuccess;
   };
   bool ok = true;
   for (int l = 0; l < cfg->n_layers && ok; ++l) {
@@ -365,11 +368,27 @@ int32_t dflash_ctx_project(const dflash_handle* h, const void* const* feats,
   hipStream_t st = (hipStream_t)stream;
   float* u = reinterpret_cast<float*>((char*)ws + P.u);
   const char* pk = (const char*)h->w.packed;
-  GemmArgs g = gemm_rows(nullptr, feat_row_stride, pk + h->pl.fc, n_tok, c.hidden,
-                         c.n_target_feats * c.target_hidden);
-  for (int f = 0; f < c.n_target_feats; ++f) g.a[f] = feats[f];
-  g.a_nseg = c.n_target_feats;
-  g.a_seg_k = c.target_hidden;
+  const int K = c.n_target_feats * c.target_hidden;
+  GemmArgs g;
+  if (gemm_uses_mfma(c.dtype, n_tok, K, true)) {
+    // Enough rows for the MFMA-bound kernel: tile the features first.
+    PackSrc src{};
+    for (int f = 0; f < c.n_target_feats; ++f) src.seg[f] = feats[f];
+    src.nseg = c.n_target_feats;
+    src.seg_k = c.target_hidden;
+    src.row_stride = feat_row_stride;
+    void* at = (char*)ws + P.ua;
+    prof_begin(DFLASH_K_SMALL, 0, 0, st);
+    const hipError_t pe = launch_pack_tiled(c.dtype, src, n_tok, K, at, st);
+    prof_end(st);
+    if (pe != hipSuccess) return DFLASH_ERR_HIP;
+    g = gemm_tiled(at, pk + h->pl.fc, n_tok, c.hidden, K);
+  } else {
+    g = gemm_rows(nullptr, feat_row_stride, pk + h->pl.fc, n_tok, c.hidden, K);
+    for (int f = 0; f < c.n_target_feats; ++f) g.a[f] = feats[f];
+    g.a_nseg = c.n_target_feats;
+    g.a_seg_k = c.target_hidden;
+  }
   g.out = u;
   g.out_stride = c.hidden;
   int32_t rc = run_gemm(c.dtype, EPI_STORE_F32, g, st);
@@ -399,7 +418,18 @@ int32_t dflash_ctx_kv_append(const dflash_handle* h, const dflash_kv_cache* cach
   if (n_tok > 0) {
     float* kv = reinterpret_cast<float*>((char*)ws + P.kv);
     const int N = L * 2 * Hkv * hd;
-    GemmArgs g = gemm_rows(ctx, c.hidden, (const char*)h->w.packed + h->pl.kv, n_tok, N, c.hidden);
+    const char* wkv = (const char*)h->w.packed + h->pl.kv;
+    GemmArgs g;
+    if (gemm_uses_mfma(c.dtype, n_tok, c.hidden, true)) {
+      void* at = (char*)ws + P.ca;
+      prof_begin(DFLASH_K_SMALL, 0, 0, st);
+      const hipError_t pe = launch_pack_tiled(c.dtype, pack_src(ctx, c.hidden), n_tok, c.hidden, at, st);
+      prof_end(st);
+      if (pe != hipSuccess) return DFLASH_ERR_HIP;
+      g = gemm_tiled(at, wkv, n_tok, N, c.hidden);
+    } else {
+      g = gemm_rows(ctx, c.hidden, wkv, n_tok, N, c.hidden);
+    }
     g.out = kv;
     g.out_stride = N;
     rc = run_gemm(c.dtype, EPI_STORE_F32, g, st);

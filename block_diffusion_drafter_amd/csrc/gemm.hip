@@ -388,8 +388,8 @@ hipError_t launch_gemm(int dtype, int epi, const GemmArgs& a0, hipStream_t st) {
 
 // One thread per 16-byte fragment of the tiled destination.
 template <typename T>
-__global__ __launch_bounds__(256) void pack_tiled_kernel(const T* __restrict__ src, int rows, int K,
-                                                         int nck, int64_t n_frags, T* __restrict__ dst) {
+__global__ __launch_bounds__(256) void pack_tiled_kernel(PackSrc src, int rows, int K, int nck,
+                                                         int64_t n_frags, T* __restrict__ dst) {
   constexpr int EPF = GemmGeom<T>::EPF;
   constexpr int KC = GemmGeom<T>::KC;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
@@ -403,25 +403,32 @@ __global__ __launch_bounds__(256) void pack_tiled_kernel(const T* __restrict__ s
     const int64_t row = tile * 16 + (lane & 15);
     const int k = c * KC + f * 4 * EPF + (lane >> 4) * EPF;
     u32x4 v = zero16();
-    if (row < rows && k < K) v = ld16(src + row * K + k);
+    if (row < rows && k < K) {
+      const int sg = k / src.seg_k;
+      const T* base = reinterpret_cast<const T*>(src.seg[sg]);
+      v = ld16(base + row * src.row_stride + (k - sg * src.seg_k));
+    }
     *reinterpret_cast<u32x4*>(dst + i * EPF) = v;
   }
 }
 
-hipError_t launch_pack_tiled(int dtype, const void* src, int rows, int K, void* dst,
+hipError_t launch_pack_tiled(int dtype, const PackSrc& src, int rows, int K, void* dst,
                              hipStream_t st) {
   if (rows <= 0 || K <= 0) return hipSuccess;
-  const int es = dtype == DFLASH_BF16 ? 2 : 4;
-  if (K % (16 / es)) return hipErrorInvalidValue;  // whole 16-byte source fragments
+  const int epf = dtype == DFLASH_BF16 ? 8 : 4;
+  // Whole 16-byte source fragments that never straddle a segment.
+  if (src.seg_k % epf || src.row_stride % epf || src.nseg < 1 || src.nseg > kMaxASeg ||
+      (int64_t)src.nseg * src.seg_k < K)
+    return hipErrorInvalidValue;
   const int64_t n_frags = (int64_t)tiled_bytes(dtype, rows, K) / 16;
   const int64_t blocks = std::min<int64_t>((n_frags + 255) / 256, 8192);
   const int nck = tiled_nck(dtype, K);
   if (dtype == DFLASH_BF16)
-    hipLaunchKernelGGL(pack_tiled_kernel<bf16>, dim3((unsigned)blocks), dim3(256), 0, st,
-                       (const bf16*)src, rows, K, nck, n_frags, (bf16*)dst);
+    hipLaunchKernelGGL(pack_tiled_kernel<bf16>, dim3((unsigned)blocks), dim3(256), 0, st, src,
+                       rows, K, nck, n_frags, (bf16*)dst);
   else
-    hipLaunchKernelGGL(pack_tiled_kernel<float>, dim3((unsigned)blocks), dim3(256), 0, st,
-                       (const float*)src, rows, K, nck, n_frags, (float*)dst);
+    hipLaunchKernelGGL(pack_tiled_kernel<float>, dim3((unsigned)blocks), dim3(256), 0, st, src,
+                       rows, K, nck, n_frags, (float*)dst);
   return hipGetLastError();
 }
 

@@ -77,9 +77,26 @@ int mfma_gemm_colblocks(int epi, int M, int N);
 // Keys per row that the LM-head projection writes (its column blocks).
 int gemm_amax_cols(int dtype, int M, int N, int K);
 
-// Tiled copy of a row-major [rows, K] matrix (row stride K) into dst, which
-// holds the whole tiled [rows, K] matrix; padding is written as zeros.
-hipError_t launch_pack_tiled(int dtype, const void* src, int rows, int K, void* dst,
+// A row-major source for the tiled copy: element (row, k) at
+// seg[k / seg_k] + row * row_stride + k % seg_k (seg_k a multiple of the
+// 16-byte fragment, row_stride in elements).
+struct PackSrc {
+  const void* seg[kMaxASeg];
+  int nseg;
+  int seg_k;
+  int64_t row_stride;
+};
+inline PackSrc pack_src(const void* p, int K) {
+  PackSrc s{};
+  s.seg[0] = p;
+  s.nseg = 1;
+  s.seg_k = K;
+  s.row_stride = K;
+  return s;
+}
+// Tiled copy of a row-major [rows, K] matrix into dst, which holds the whole
+// tiled [rows, K] matrix; padding is written as zeros.
+hipError_t launch_pack_tiled(int dtype, const PackSrc& src, int rows, int K, void* dst,
                              hipStream_t st);
 
 struct AttnArgs {
