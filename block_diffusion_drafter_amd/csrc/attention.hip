@@ -7,9 +7,10 @@
 // work is a stream of the K/V cache, split over key chunks:
 //
 //   attn_partial: one workgroup per (sequence, KV head, key chunk), one wave
-//     per query head of the GQA group. The waves of a group read the same K/V
-//     positions, so after the first wave the loads hit the CU's L1: HBM sees
-//     each position once. Scores are computed transposed, S^T = K Q^T (keys as
+//     per query head of the GQA group. In bf16 the group's waves share each
+//     32-key K/V block through an LDS ring filled by direct global->LDS loads
+//     (every position crosses the memory system once, several blocks in
+//     flight); the fp32 path loads per wave into registers. Scores are computed transposed, S^T = K Q^T (keys as
 //     MFMA rows, queries as columns), and the output likewise, O^T = V^T P^T,
 //     so each lane owns one query column: the online-softmax running max/sum
 //     are per-lane values plus a two-step shuffle across the four lane groups.
@@ -104,10 +105,127 @@ __device__ __forceinline__ void load_block(KVBlock<T, HD>& b, const T* K, const 
   }
 }
 
+// Online-softmax update of one wave's state with one 32-key block whose
+// K/V fragments are in registers: S^T = K Q^T, running max / sum per query
+// column (lane), O^T = alpha O^T + V^T P^T.
+template <typename T, int HD>
+struct AttnState {
+  static constexpr int NDT = HD / 16;
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x4 o[NDT];
+};
+
+template <typename T, int HD>
+__device__ __forceinline__ void attn_update(AttnState<T, HD>& S, const KVBlock<T, HD>& b,
+                                            const u32x4* qf, int kb, int k_hi, float scale_log2,
+                                            int grp) {
+  using KB = KVBlock<T, HD>;
+  constexpr int FR = KB::FR, NDT = KB::NDT;
+  f32x4 st[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    st[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int f = 0; f < FR; ++f) st[t] = mfma_frag<T>(b.k[t][f], qf[f], st[t]);
+  }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int key = kb + key_of<T>(t, 4 * grp + i);
+      const float v = key < k_hi ? st[t][i] * scale_log2 : -INFINITY;
+      st[t][i] = v;
+      mx = fmaxf(mx, v);
+    }
+  mx = fmaxf(mx, __shfl_xor(mx, 16));
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  // Every block holds at least one valid key, so m_new is finite.
+  const float m_new = fmaxf(S.m_run, mx);
+  const float alpha = exp2f(S.m_run - m_new);
+  S.m_run = m_new;
+  float psum = 0.f;
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float pv = exp2f(st[t][i] - m_new);
+      st[t][i] = pv;
+      psum += pv;
+    }
+  S.l_run = S.l_run * alpha + psum;
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) S.o[dt] *= alpha;
+  if constexpr (sizeof(T) == 2) {
+    bf16x8 pb;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pb[4 * t + i] = (bf16)st[t][i];
+    const u32x4 pf = __builtin_bit_cast(u32x4, pb);
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) S.o[dt] = mfma_frag<T>(b.v[dt][0], pf, S.o[dt]);
+  } else {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const u32x4 pf = __builtin_bit_cast(u32x4, st[t]);
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) S.o[dt] = mfma_frag<T>(b.v[dt][t], pf, S.o[dt]);
+    }
+  }
+}
+
+// The wave's Q fragments (same channel order as the K fragments).
+template <typename T, int HD>
+__device__ __forceinline__ void load_q(u32x4* qf, const AttnArgs& p, int s, int h, int r, int grp) {
+  using KB = KVBlock<T, HD>;
+  const T* qp = reinterpret_cast<const T*>(p.q) + (((size_t)s * p.n_heads + h) * 16 + r) * HD +
+                grp * KB::EPF;
+#pragma unroll
+  for (int f = 0; f < KB::FR; ++f) qf[f] = ld16(qp + f * 4 * KB::EPF);
+}
+
+// End of a chunk: a sequence that fit in one chunk is normalised and written
+// to the tiled output; otherwise (max, sum, unnormalised O) go to the partials.
+template <typename T, int HD>
+__device__ __forceinline__ void attn_finish(AttnState<T, HD>& S, const AttnArgs& p, int s, int g,
+                                            int c, int j, int G, bool single, int r, int grp) {
+  constexpr int NDT = HD / 16;
+  const int h = g * G + j;
+  S.l_run += __shfl_xor(S.l_run, 16);
+  S.l_run += __shfl_xor(S.l_run, 32);
+  if (single) {
+    if (r < p.block) {
+      // Four consecutive channels per lane and tile: contiguous in the tiled output.
+      const float inv = 1.0f / S.l_run;
+      T* out = reinterpret_cast<T*>(p.out);
+      const int row = s * p.block + r;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        T* dst = out + tiled_index<T>(row, h * HD + 16 * dt + 4 * grp, p.out_nck);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[i] = from_f32<T>(S.o[dt][i] * inv);
+      }
+    }
+    return;
+  }
+  const size_t item = ((size_t)(s * p.n_kv_heads + g) * p.max_chunks + c) * G + j;
+  if (grp == 0) {
+    p.part_ml[(item * 16 + r) * 2 + 0] = S.m_run;
+    p.part_ml[(item * 16 + r) * 2 + 1] = S.l_run;
+  }
+  float* po = p.part_o + item * HD * 16;
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) po[(16 * dt + 4 * grp + i) * 16 + r] = S.o[dt][i];
+}
+
+// fp32 path: each wave loads its K/V fragments straight into registers.
 template <typename T, int HD>
 __global__ __launch_bounds__(512) void attn_partial_kernel(AttnArgs p) {
   using KB = KVBlock<T, HD>;
-  constexpr int EPF = KB::EPF, FR = KB::FR, NDT = KB::NDT;
+  constexpr int FR = KB::FR, NDT = KB::NDT;
   const int lane = threadIdx.x & 63, j = threadIdx.x >> 6;
   const int r = lane & 15, grp = lane >> 4;
   const int c = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
@@ -124,124 +242,144 @@ __global__ __launch_bounds__(512) void attn_partial_kernel(AttnArgs p) {
   const T* K = reinterpret_cast<const T*>(p.k) + kvoff;
   const T* V = reinterpret_cast<const T*>(p.v) + kvoff;
 
-  u32x4 qf[FR];  // same channel order as the K fragments
-  {
-    const T* qp = reinterpret_cast<const T*>(p.q) + (((size_t)s * p.n_heads + h) * 16 + r) * HD +
-                  grp * EPF;
+  u32x4 qf[FR];
+  load_q<T, HD>(qf, p, s, h, r, grp);
+  AttnState<T, HD> S;
 #pragma unroll
-    for (int f = 0; f < FR; ++f) qf[f] = ld16(qp + f * 4 * EPF);
-  }
+  for (int dt = 0; dt < NDT; ++dt) S.o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  float m_run = -INFINITY, l_run = 0.f;
-  f32x4 o[NDT];
-#pragma unroll
-  for (int dt = 0; dt < NDT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  auto process = [&](const KB& b, int kb) {
-    f32x4 st[2];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      st[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int f = 0; f < FR; ++f) st[t] = mfma_frag<T>(b.k[t][f], qf[f], st[t]);
-    }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = kb + key_of<T>(t, 4 * grp + i);
-        const float v = key < k_hi ? st[t][i] * p.scale_log2 : -INFINITY;
-        st[t][i] = v;
-        mx = fmaxf(mx, v);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    // Every block holds at least one valid key, so m_new is finite.
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = exp2f(m_run - m_new);
-    m_run = m_new;
-    float psum = 0.f;
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float pv = exp2f(st[t][i] - m_new);
-        st[t][i] = pv;
-        psum += pv;
-      }
-    l_run = l_run * alpha + psum;
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
-    if constexpr (sizeof(T) == 2) {
-      bf16x8 pb;
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) pb[4 * t + i] = (bf16)st[t][i];
-      const u32x4 pf = __builtin_bit_cast(u32x4, pb);
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) o[dt] = mfma_frag<T>(b.v[dt][0], pf, o[dt]);
-    } else {
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const u32x4 pf = __builtin_bit_cast(u32x4, st[t]);
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) o[dt] = mfma_frag<T>(b.v[dt][t], pf, o[dt]);
-      }
-    }
-  };
-
-  if constexpr (sizeof(T) == 2 || HD == 64) {
+  if constexpr (HD == 64) {
     // Two blocks in flight: the next block's K/V loads while this one is used.
     KB b0, b1;
     load_block<T, HD>(b0, K, V, k_lo, k_hi, r, grp);
     for (int kb = k_lo; kb < k_hi; kb += 64) {
       const bool has1 = kb + 32 < k_hi;
       if (has1) load_block<T, HD>(b1, K, V, kb + 32, k_hi, r, grp);
-      process(b0, kb);
+      attn_update<T, HD>(S, b0, qf, kb, k_hi, p.scale_log2, grp);
       if (has1) {
         if (kb + 64 < k_hi) load_block<T, HD>(b0, K, V, kb + 64, k_hi, r, grp);
-        process(b1, kb + 32);
+        attn_update<T, HD>(S, b1, qf, kb + 32, k_hi, p.scale_log2, grp);
       }
     }
   } else {
-    // fp32 at head_dim 128: one block of fragments already fills the registers.
+    // head_dim 128: one block of fragments already fills the registers.
     for (int kb = k_lo; kb < k_hi; kb += 32) {
       KB b0;
       load_block<T, HD>(b0, K, V, kb, k_hi, r, grp);
-      process(b0, kb);
+      attn_update<T, HD>(S, b0, qf, kb, k_hi, p.scale_log2, grp);
     }
   }
+  attn_finish<T, HD>(S, p, s, g, c, j, G, single, r, grp);
+}
 
-  l_run += __shfl_xor(l_run, 16);
-  l_run += __shfl_xor(l_run, 32);
-  if (single) {
-    // The whole sequence was in this chunk: normalise and write the output.
-    if (r < p.block) {
-      // Four consecutive channels per lane and tile: contiguous in the tiled output.
-      const float inv = 1.0f / l_run;
-      T* out = reinterpret_cast<T*>(p.out);
-      const int row = s * p.block + r;
+typedef __attribute__((address_space(3))) void* attn_lds_ptr;
+typedef const __attribute__((address_space(1))) void* attn_gbl_ptr;
+
+// Wait until at most N of this wave's global->LDS loads are outstanding and
+// its LDS reads have returned, then meet the other waves of the group.
+template <int N>
+__device__ __forceinline__ void attn_wait_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// bf16 path: the G waves of a KV group share each 32-key K/V block through an
+// LDS ring. A block is NI = HD/8 wave-wide 1 KB fragments (2*FR of K, NDT of
+// V), copied by direct global->LDS loads split over the waves; each load's
+// lanes gather exactly the 16-byte pieces the MFMA operand layout wants, so a
+// wave reads every fragment back as 64 lanes x 16 contiguous bytes. NSB ring
+// slots keep NSB-1 blocks in flight per group with no staging registers.
+template <int HD, int G>
+__global__ __launch_bounds__(64 * G) void attn_partial_lds_kernel(AttnArgs p) {
+  using T = bf16;
+  using KB = KVBlock<T, HD>;
+  constexpr int EPF = KB::EPF, FR = KB::FR, NDT = KB::NDT;
+  constexpr int NI = 2 * FR + NDT;  // fragments per block
+  constexpr int IPW = NI / G;       // fragments each wave copies per block
+  static_assert(NI % G == 0, "block fragments must split evenly over the group");
+  constexpr int NSB = 4;
+  __shared__ u32x4 ring[NSB][NI][64];
+
+  const int lane = threadIdx.x & 63;
+  const int j = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = lane & 15, grp = lane >> 4;
+  const int c = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
+  const int h = g * G + j;
+
+  const int n_keys = seq_keys(p, s);
+  const int k_lo = c * p.chunk;
+  if (k_lo >= n_keys) return;
+  const int k_hi = min(n_keys, k_lo + p.chunk);
+  const bool single = n_keys <= p.chunk;
+  const int nblk = (k_hi - k_lo + 31) / 32;
+
+  const size_t kvoff = (size_t)(s * p.n_kv_heads + g) * p.cap * HD;
+  const T* K = reinterpret_cast<const T*>(p.k) + kvoff;
+  const T* V = reinterpret_cast<const T*>(p.v) + kvoff;
+
+  // Fragment i of block n (key base kb, a multiple of 32 below cap, so every
+  // address stays inside the sequence's cache rows): i < 2*FR is K tile i/FR,
+  // fragment i%FR: lane (r, grp) takes key kb + key_of(t, r), channels
+  // [4*EPF*f + EPF*grp, +EPF). Else V channel tile dt = i - 2*FR: lane (r, grp)
+  // takes channel 16 dt + r, keys 8 grp .. 8 grp + 7 of the block.
+  auto issue = [&](int n, int slot) {
+    const int kb = k_lo + 32 * n;
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        T* dst = out + tiled_index<T>(row, h * HD + 16 * dt + 4 * grp, p.out_nck);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) dst[i] = from_f32<T>(o[dt][i] * inv);
+    for (int u = 0; u < IPW; ++u) {
+      const int i = j + G * u;
+      const T* src;
+      if (i < 2 * FR) {
+        const int t = i / FR, f = i % FR;
+        src = K + (size_t)(kb + key_of<T>(t, r)) * HD + f * 4 * EPF + grp * EPF;
+      } else {
+        const int dt = i - 2 * FR;
+        src = V + (size_t)(kb / kKeyBlock) * HD * kKeyBlock + (16 * dt + r) * kKeyBlock + 8 * grp;
       }
+      __builtin_amdgcn_global_load_lds((attn_gbl_ptr)src, (attn_lds_ptr)&ring[slot][i][0], 16, 0, 0);
     }
-    return;
-  }
-  const size_t item = ((size_t)(s * p.n_kv_heads + g) * p.max_chunks + c) * G + j;
-  if (grp == 0) {
-    p.part_ml[(item * 16 + r) * 2 + 0] = m_run;
-    p.part_ml[(item * 16 + r) * 2 + 1] = l_run;
-  }
-  float* po = p.part_o + item * HD * 16;
+  };
+
+  u32x4 qf[FR];
+  load_q<T, HD>(qf, p, s, h, r, grp);
+  // Consume Q here, so the compiler's wait for it happens before the ring's
+  // loads are issued (later, it would have to drain the whole ring).
 #pragma unroll
-  for (int dt = 0; dt < NDT; ++dt)
+  for (int f = 0; f < FR; ++f) asm volatile("" ::"v"(qf[f]));
+  AttnState<T, HD> S;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) po[(16 * dt + 4 * grp + i) * 16 + r] = o[dt][i];
+  for (int dt = 0; dt < NDT; ++dt) S.o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // Ring: before block n is read, every wave has waited for its own loads of
+  // it and passed the barrier; the barrier after block n's reads frees its
+  // slot for block n + NSB.
+#pragma unroll
+  for (int n = 0; n < NSB; ++n)
+    if (n < nblk) issue(n, n);
+  if (nblk >= NSB) attn_wait_barrier<IPW * (NSB - 1)>();
+  else attn_wait_barrier<0>();
+  for (int n = 0; n < nblk; ++n) {
+    const int slot = n % NSB;
+    const int kb = k_lo + 32 * n;
+    KB b;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int f = 0; f < FR; ++f) b.k[t][f] = ring[slot][t * FR + f][lane];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      u32x4 x = ring[slot][2 * FR + dt][lane];
+      // Positions past the last key may hold anything (even NaN bit patterns);
+      // their probabilities are 0, so their values must be 0 too.
+      if (kb + 32 > k_hi) x = keep_first<T>(x, k_hi - (kb + 8 * grp));
+      b.v[dt][0] = x;
+    }
+    attn_update<T, HD>(S, b, qf, kb, k_hi, p.scale_log2, grp);
+    if (n + 1 < nblk) {
+      if (n + NSB <= nblk) attn_wait_barrier<IPW * (NSB - 2)>();
+      else attn_wait_barrier<0>();
+      if (n + NSB < nblk) issue(n + NSB, slot);
+    }
+  }
+  attn_finish<T, HD>(S, p, s, g, c, j, G, single, r, grp);
 }
 
 // Merge of the chunk partials of one (query head, sequence, 16-channel slice).
@@ -307,7 +445,17 @@ template <typename T, int HD>
 static hipError_t launch_hd(const AttnArgs& a, hipStream_t st) {
   const int G = a.n_heads / a.n_kv_heads;
   dim3 grid(a.max_chunks, a.n_kv_heads, a.batch);
-  hipLaunchKernelGGL((attn_partial_kernel<T, HD>), grid, dim3(64 * G), 0, st, a);
+  if constexpr (sizeof(T) == 2) {
+    switch (G) {
+      case 1: hipLaunchKernelGGL((attn_partial_lds_kernel<HD, 1>), grid, dim3(64), 0, st, a); break;
+      case 2: hipLaunchKernelGGL((attn_partial_lds_kernel<HD, 2>), grid, dim3(128), 0, st, a); break;
+      case 4: hipLaunchKernelGGL((attn_partial_lds_kernel<HD, 4>), grid, dim3(256), 0, st, a); break;
+      case 8: hipLaunchKernelGGL((attn_partial_lds_kernel<HD, 8>), grid, dim3(512), 0, st, a); break;
+      default: return hipErrorInvalidValue;
+    }
+  } else {
+    hipLaunchKernelGGL((attn_partial_kernel<T, HD>), grid, dim3(64 * G), 0, st, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.max_chunks <= 1) return e;
   prof_end(st);
