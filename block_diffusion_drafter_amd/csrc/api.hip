@@ -108,16 +108,25 @@ struct Plan {
   size_t total;
 };
 
-// Keys per attention work item (one workgroup of G waves): aim for ~2048
-// waves over the whole cache so every CU has work, within [64, 1024] keys.
-// Small contexts get short chunks (parallelism); long ones long chunks, which
-// keeps the fp32 partials (16 rows x head_dim per wave) a few percent of the
-// K/V stream.
-int choose_chunk(int batch, int hkv, int group, int cap) {
-  long long waves_if_32 = (long long)batch * hkv * group * ((cap + 31) / 32);
-  long long c = 32 * ((waves_if_32 + 2047) / 2048);
-  c = std::max(64LL, std::min(1024LL, c));
-  return (int)c;
+// Keys per attention work item (one workgroup of G waves per sequence, KV
+// head and chunk). The device holds the context lengths, so the split is
+// sized from the capacity. Few (sequence, KV head) pairs: each pair is cut
+// into about 512 / pairs equal chunks, so the items fill ~2 workgroups per CU
+// in one round (a last round with a few items left most of the chip idle:
+// 1056 items over 512 slots ran at 2/3 of the rate of 512 items). Many pairs
+// (ragged batches): 1024-key chunks, several rounds of items. The partials
+// (16 rows x head_dim fp32 per query head) stay a few percent of the K/V
+// stream for chunks of >= 512 keys.
+int choose_chunk(int batch, int hkv, int cap) {
+  const long long pairs = (long long)batch * hkv;
+  long long c;
+  if (pairs >= 128) {
+    c = 1024;
+  } else {
+    const long long per = (512 + pairs - 1) / pairs;
+    c = 32 * (((cap + per - 1) / per + 31) / 32);
+  }
+  return (int)std::max(64LL, std::min(4096LL, c));
 }
 
 Plan make_plan(const dflash_config& c, int batch, int cap, int max_tokens) {
@@ -136,7 +145,7 @@ Plan make_plan(const dflash_config& c, int batch, int cap, int max_tokens) {
   p.h = take(tiled_bytes(dt, (int64_t)M, (int)d));
   p.qkv = take(M * (Hq + 2 * Hkv) * hd * 4);
   p.q = take((size_t)batch * Hq * 16 * hd * es);
-  p.chunk = choose_chunk(batch, (int)Hkv, (int)G, cap);
+  p.chunk = choose_chunk(batch, (int)Hkv, cap);
   p.max_chunks = (cap + p.chunk - 1) / p.chunk;
   p.po = take((size_t)batch * Hkv * p.max_chunks * G * hd * 16 * 4);
   p.pml = take((size_t)batch * Hkv * p.max_chunks * G * 16 * 2 * 4);

@@ -287,8 +287,10 @@ __device__ __forceinline__ void attn_wait_barrier() {
 // V), copied by direct global->LDS loads split over the waves; each load's
 // lanes gather exactly the 16-byte pieces the MFMA operand layout wants, so a
 // wave reads every fragment back as 64 lanes x 16 contiguous bytes. NSB ring
-// slots keep NSB-1 blocks in flight per group with no staging registers.
-template <int HD, int G>
+// slots keep NSB-1 blocks in flight per group with no staging registers; 3
+// slots (48 KB at head_dim 128) leave room for several groups per CU, which
+// measured better than deeper rings with fewer groups.
+template <int HD, int G, int NSB = 3>
 __global__ __launch_bounds__(64 * G) void attn_partial_lds_kernel(AttnArgs p) {
   using T = bf16;
   using KB = KVBlock<T, HD>;
@@ -296,7 +298,6 @@ __global__ __launch_bounds__(64 * G) void attn_partial_lds_kernel(AttnArgs p) {
   constexpr int NI = 2 * FR + NDT;  // fragments per block
   constexpr int IPW = NI / G;       // fragments each wave copies per block
   static_assert(NI % G == 0, "block fragments must split evenly over the group");
-  constexpr int NSB = 4;
   __shared__ u32x4 ring[NSB][NI][64];
 
   const int lane = threadIdx.x & 63;
