@@ -35,6 +35,30 @@ BF16_PEAK_TFLOPS = 2500.0
 METRIC = "drafted block-tokens/sec (5-layer, block 16) + % HBM/MFMA roofline"
 
 
+def measured_traffic(workload: str, kernel_class: str):
+    """HBM bytes per launch from the counter record committed under profiles/
+    for this workload and kernel class (FETCH_SIZE and WRITE_SIZE passes, each
+    scaled by a 1 GiB copy), or None when there is none or when one of the
+    kernel sources it lists has changed since the counters were taken."""
+    import glob
+    import hashlib
+    import re
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
+        for block in re.findall(r"```json\n(.*?)```", open(path).read(), flags=re.S):
+            try:
+                rec = json.loads(block)
+            except ValueError:
+                continue
+            if rec.get("workload") != workload or rec.get("kernel_class") != kernel_class:
+                continue
+            for src, digest in rec.get("sources_sha256", {}).items():
+                fp = os.path.join(ROOT, src)
+                if not os.path.exists(fp) or hashlib.sha256(open(fp, "rb").read()).hexdigest() != digest:
+                    return None
+            return rec.get("traffic_bytes_per_launch")
+    return None
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -188,7 +212,7 @@ def main() -> int:
     else:
         roof = {"bound": "mfma", "achieved": round(tfl, 1), "peak": BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(tfl / BF16_PEAK_TFLOPS, 4)}
-    roof.update({"traffic": None, "kernel_class": dom_name,
+    roof.update({"traffic": measured_traffic(W.name, dom_name), "kernel_class": dom_name,
                  "launches_per_step": dom["launches"] // a.steps,
                  "ms_per_launch": round(dom["ms"] / dom["launches"], 5),
                  "algorithmic_bytes_per_launch": dom["bytes"] / dom["launches"],

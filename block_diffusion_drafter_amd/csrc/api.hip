@@ -101,7 +101,7 @@ PackedLayout packed_layout(const dflash_config& c) {
 }
 
 struct Plan {
-  size_t x, h, qkv, q, po, pml, attn, act, y, amax, fwd_end;
+  size_t x, h, qkv, q, po, pml, attn, act, y, amax, arr, fwd_end;
   size_t u, ua, proj_end;  // ua: tiled copy of the fused features (MFMA path)
   size_t kv, ca, app_end;  // ca: tiled copy of the context rows (MFMA path)
   int chunk, max_chunks, n_vtiles;
@@ -156,6 +156,7 @@ Plan make_plan(const dflash_config& c, int batch, int cap, int max_tokens) {
   // LM head: one (max, argmax) key per row and workgroup column.
   p.n_vtiles = R > 0 ? gemm_amax_cols(c.dtype, (int)R, c.vocab, c.hidden) : 1;
   p.amax = take(R * p.n_vtiles * 8);
+  p.arr = take((size_t)batch * 4);
   p.fwd_end = off;
   off = 0;
   p.u = take((size_t)max_tokens * d * 4);
@@ -516,8 +517,9 @@ int32_t dflash_draft_forward(const dflash_handle* h, const dflash_kv_cache* cach
   const PackedLayout& pl = h->pl;
 
   prof_begin(DFLASH_K_SMALL, 0, 0, st);
+  int32_t* arrivals = reinterpret_cast<int32_t*>(w + P.arr);
   hipError_t e = launch_embed(c.dtype, h->w.embed, anchor, batch, B, d, c.vocab, c.mask_token_id,
-                              x, h->layers[0].in_norm, c.rms_eps, hbuf, dev_status, st);
+                              x, h->layers[0].in_norm, c.rms_eps, hbuf, dev_status, arrivals, st);
   prof_end(st);
   if (e != hipSuccess) return DFLASH_ERR_HIP;
 
@@ -627,7 +629,7 @@ int32_t dflash_draft_forward(const dflash_handle* h, const dflash_kv_cache* cach
     if ((rc = run_gemm(c.dtype, EPI_ARGMAX, g, st))) return rc;
     prof_begin(DFLASH_K_SMALL, 0, 0, st);
     e = launch_argmax_accept(amax, P.n_vtiles, P.n_vtiles, batch, B, draft_tokens, target_tokens,
-                             accept_len, bonus, st);
+                             accept_len, bonus, arrivals, st);
     prof_end(st);
     if (e != hipSuccess) return DFLASH_ERR_HIP;
   } else if (target_tokens) {  // B == 1: nothing drafted, the bonus is the first target

@@ -112,9 +112,10 @@ template <typename T, int VPT>
 __global__ __launch_bounds__(256) void embed_kernel(const T* E, const int32_t* anchor, int block,
                                                     int d, int vocab, int mask_id, float* x,
                                                     const T* gain, float eps, T* h, int nck,
-                                                    int32_t* dev_status) {
+                                                    int32_t* dev_status, int32_t* arrivals) {
   __shared__ float sh[4];
   const int row = blockIdx.x, s = row / block, i = row % block;
+  if (arrivals && i == 0 && threadIdx.x == 0) arrivals[s] = 0;
   int id = i == 0 ? anchor[s] : mask_id;
   if (id < 0 || id >= vocab) {
     if (threadIdx.x == 0 && dev_status) atomicOr(dev_status, DFLASH_DEV_TOKEN);
@@ -133,14 +134,14 @@ __global__ __launch_bounds__(256) void embed_kernel(const T* E, const int32_t* a
 
 hipError_t launch_embed(int dtype, const void* embed, const int32_t* anchor, int batch, int block,
                         int d, int vocab, int mask_id, float* x, const void* gain, float eps,
-                        void* h, int32_t* dev_status, hipStream_t st) {
+                        void* h, int32_t* dev_status, int32_t* arrivals, hipStream_t st) {
   if (d > 8192 || d % 4) return hipErrorInvalidValue;
   const int vpt = (d + 1023) / 1024;
   const int nck = tiled_nck(dtype, d);
   dim3 grid(batch * block), blk(256);
 #define DF_EMBED(T, V)                                                                            \
   hipLaunchKernelGGL((embed_kernel<T, V>), grid, blk, 0, st, (const T*)embed, anchor, block, d,   \
-                     vocab, mask_id, x, (const T*)gain, eps, (T*)h, nck, dev_status)
+                     vocab, mask_id, x, (const T*)gain, eps, (T*)h, nck, dev_status, arrivals)
   if (dtype == DFLASH_BF16) {
     if (vpt <= 1) DF_EMBED(bf16, 1); else if (vpt <= 2) DF_EMBED(bf16, 2);
     else if (vpt <= 4) DF_EMBED(bf16, 4); else DF_EMBED(bf16, 8);
@@ -329,53 +330,65 @@ hipError_t launch_norm_rope_append(int dtype, const NormRopeArgs& a, hipStream_t
   return launch_nr<1>(dtype, a, dim3(a.n_layers * 2 * a.n_kv_heads, a.n_tok), st);
 }
 
-// Per sequence: wave i reduces row i's per-workgroup (max, argmax) keys into
-// draft token i; then, when targets are given, one thread applies the greedy
-// accept rule to the sequence's drafts.
-__global__ __launch_bounds__(1024) void argmax_accept_kernel(const unsigned long long* amax,
-                                                             int64_t stride, int n_cols, int block,
-                                                             int32_t* drafts,
-                                                             const int32_t* targets,
-                                                             int32_t* accept_len, int32_t* bonus) {
-  __shared__ int32_t dsh[16];
-  const int s = blockIdx.x, m = block - 1;
+// One workgroup per draft row: its 1024 threads reduce the row's per-column
+// (max, argmax) keys from the LM head (thousands of columns at batch 1) into
+// the draft token. With targets, the last row of a sequence to finish (a
+// per-sequence arrival counter, zeroed by the embedding kernel at the start
+// of the forward) applies the greedy accept rule to the sequence's drafts.
+__global__ __launch_bounds__(1024) void argmax_rows_kernel(const unsigned long long* amax,
+                                                           int64_t stride, int n_cols, int block,
+                                                           int32_t* drafts, const int32_t* targets,
+                                                           int32_t* accept_len, int32_t* bonus,
+                                                           int32_t* arrivals) {
+  __shared__ unsigned long long red[16];
+  __shared__ int is_last;
+  const int row = blockIdx.x, m = block - 1, s = row / m;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  if (wave < m) {
-    const int row = s * m + wave;
-    const unsigned long long* keys = amax + (int64_t)row * stride;
-    unsigned long long best = 0ull;
-#pragma unroll 8
-    for (int c = lane; c < n_cols; c += 64) {
-      const unsigned long long k = keys[c];
-      best = k > best ? k : best;
-    }
+  const unsigned long long* keys = amax + (int64_t)row * stride;
+  unsigned long long best = 0ull;
+#pragma unroll 4
+  for (int c = threadIdx.x; c < n_cols; c += 1024) {
+    const unsigned long long k = keys[c];
+    best = k > best ? k : best;
+  }
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const unsigned long long other = __shfl_xor(best, o);
-      best = other > best ? other : best;
-    }
-    if (lane == 0) {
-      const int32_t tok = (int32_t)argmax_index(best);
-      drafts[row] = tok;
-      dsh[wave] = tok;
+  for (int o = 32; o > 0; o >>= 1) {
+    const unsigned long long other = __shfl_xor(best, o);
+    best = other > best ? other : best;
+  }
+  if (lane == 0) red[wave] = best;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < 16; ++w) best = red[w] > best ? red[w] : best;
+    best = red[0] > best ? red[0] : best;
+    drafts[row] = (int32_t)argmax_index(best);
+    is_last = 0;
+    if (targets) {
+      __threadfence();  // the draft is visible before the arrival is counted
+      is_last = atomicAdd(&arrivals[s], 1) == m - 1;
     }
   }
   __syncthreads();
-  if (targets && threadIdx.x == 0) {
+  if (is_last && threadIdx.x == 0) {
+    __threadfence();  // see every row's draft
+    const volatile int32_t* d = drafts + (int64_t)s * m;
     const int32_t* t = targets + (int64_t)s * block;
     int a = 0;
-    while (a < m && dsh[a] == t[a]) ++a;
+    while (a < m && d[a] == t[a]) ++a;
     accept_len[s] = a;
     bonus[s] = t[a];
+    arrivals[s] = 0;
   }
 }
 
 hipError_t launch_argmax_accept(const unsigned long long* amax, int64_t stride, int n_cols,
                                 int batch, int block, int32_t* drafts, const int32_t* targets,
-                                int32_t* accept_len, int32_t* bonus, hipStream_t st) {
+                                int32_t* accept_len, int32_t* bonus, int32_t* arrivals,
+                                hipStream_t st) {
   if (batch <= 0 || block < 2 || block > 17) return block == 1 ? hipSuccess : hipErrorInvalidValue;
-  hipLaunchKernelGGL(argmax_accept_kernel, dim3(batch), dim3(1024), 0, st, amax, stride, n_cols,
-                     block, drafts, targets, accept_len, bonus);
+  if (targets && !arrivals) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(argmax_rows_kernel, dim3(batch * (block - 1)), dim3(1024), 0, st, amax, stride,
+                     n_cols, block, drafts, targets, accept_len, bonus, arrivals);
   return hipGetLastError();
 }
 

@@ -151,16 +151,18 @@ hipError_t launch_rmsnorm(int dtype, const float* x, int64_t x_stride, const voi
                           int grp_stride, int grp_off, hipStream_t st);
 
 // Block embedding into the fp32 residual x, plus h = RMSNorm(x; gain) for
-// layer 0, h tiled [batch*block, d].
+// layer 0, h tiled [batch*block, d]; zeroes arrivals[0..batch) when non-null.
 hipError_t launch_embed(int dtype, const void* embed, const int32_t* anchor, int batch, int block,
                         int d, int vocab, int mask_id, float* x, const void* gain, float eps,
-                        void* h, int32_t* dev_status, hipStream_t st);
+                        void* h, int32_t* dev_status, int32_t* arrivals, hipStream_t st);
 
 // Draft tokens from the LM head's per-workgroup keys ([batch*(B-1)][n_cols]),
-// plus the greedy accept rule when targets is non-null.
+// plus the greedy accept rule when targets is non-null (arrivals: per-sequence
+// counters, zero on entry, left zero).
 hipError_t launch_argmax_accept(const unsigned long long* amax, int64_t stride, int n_cols,
                                 int batch, int block, int32_t* drafts, const int32_t* targets,
-                                int32_t* accept_len, int32_t* bonus, hipStream_t st);
+                                int32_t* accept_len, int32_t* bonus, int32_t* arrivals,
+                                hipStream_t st);
 
 hipError_t launch_accept(const int32_t* drafts, const int32_t* targets, int batch, int block,
                          int32_t* accept_len, int32_t* bonus, int32_t* anchor_out,
