@@ -101,9 +101,10 @@ PackedLayout packed_layout(const dflash_config& c) {
 }
 
 struct Plan {
-  size_t x, h, qkv, q, po, pml, attn, act, y, amax, arr, fwd_end;
-  size_t u, ua, proj_end;  // ua: tiled copy of the fused features (MFMA path)
-  size_t kv, ca, app_end;  // ca: tiled copy of the context rows (MFMA path)
+  size_t x, h, qkv, q, po, pml, attn, act, y, amax, arr, part, fwd_end;
+  size_t u, ua, upart, proj_end;  // ua: tiled copy of the fused features (MFMA path)
+  size_t kv, ca, kvpart, app_end;  // ca: tiled copy of the context rows (MFMA path)
+  int64_t part_elems, upart_elems, kvpart_elems;  // split-K partials (floats)
   int chunk, max_chunks, n_vtiles;
   size_t total;
 };
@@ -127,6 +128,13 @@ int choose_chunk(int batch, int hkv, int cap) {
     c = 32 * (((cap + per - 1) / per + 31) / 32);
   }
   return (int)std::max(64LL, std::min(4096LL, c));
+}
+
+// Floats of split-K partials a tiled-A projection needs on the MFMA path (0 if none).
+int64_t splitk_elems(int dtype, int epi, int M, int N, int K) {
+  if (!gemm_uses_mfma(dtype, M, K, true)) return 0;
+  const int ks = mfma_gemm_ksplit(epi, M, N, K);
+  return ks > 1 ? (int64_t)ks * M * N : 0;
 }
 
 Plan make_plan(const dflash_config& c, int batch, int cap, int max_tokens) {
@@ -157,15 +165,26 @@ Plan make_plan(const dflash_config& c, int batch, int cap, int max_tokens) {
   p.n_vtiles = R > 0 ? gemm_amax_cols(c.dtype, (int)R, c.vocab, c.hidden) : 1;
   p.amax = take(R * p.n_vtiles * 8);
   p.arr = take((size_t)batch * 4);
+  {
+    const int Mi = (int)M, Nqkv = (int)((Hq + 2 * Hkv) * hd), qd = (int)(Hq * hd);
+    p.part_elems = std::max({splitk_elems(dt, EPI_STORE_F32, Mi, Nqkv, (int)d),
+                             splitk_elems(dt, EPI_RESID, Mi, (int)d, qd),
+                             splitk_elems(dt, EPI_RESID, Mi, (int)d, (int)I)});
+    p.part = take((size_t)p.part_elems * 4);
+  }
   p.fwd_end = off;
   off = 0;
   p.u = take((size_t)max_tokens * d * 4);
   const int fk = c.n_target_feats * c.target_hidden;
   p.ua = gemm_uses_mfma(dt, max_tokens, fk, true) ? take(tiled_bytes(dt, max_tokens, fk)) : 0;
+  p.upart_elems = splitk_elems(dt, EPI_STORE_F32, max_tokens, (int)d, fk);
+  p.upart = take((size_t)p.upart_elems * 4);
   p.proj_end = off;
   off = 0;
   p.kv = take((size_t)max_tokens * c.n_layers * 2 * Hkv * hd * 4);
   p.ca = gemm_uses_mfma(dt, max_tokens, (int)d, true) ? take(tiled_bytes(dt, max_tokens, (int)d)) : 0;
+  p.kvpart_elems = splitk_elems(dt, EPI_STORE_F32, max_tokens, (int)(c.n_layers * 2 * Hkv * hd), (int)d);
+  p.kvpart = take((size_t)p.kvpart_elems * 4);
   p.app_end = off;
   p.total = std::max(p.fwd_end, std::max(p.proj_end, p.app_end));
   return p;
@@ -393,6 +412,8 @@ int32_t dflash_ctx_project(const dflash_handle* h, const void* const* feats,
     prof_end(st);
     if (pe != hipSuccess) return DFLASH_ERR_HIP;
     g = gemm_tiled(at, pk + h->pl.fc, n_tok, c.hidden, K);
+    g.part = reinterpret_cast<float*>((char*)ws + P.upart);
+    g.part_elems = P.upart_elems;
   } else {
     g = gemm_rows(nullptr, feat_row_stride, pk + h->pl.fc, n_tok, c.hidden, K);
     for (int f = 0; f < c.n_target_feats; ++f) g.a[f] = feats[f];
@@ -437,6 +458,8 @@ int32_t dflash_ctx_kv_append(const dflash_handle* h, const dflash_kv_cache* cach
       prof_end(st);
       if (pe != hipSuccess) return DFLASH_ERR_HIP;
       g = gemm_tiled(at, wkv, n_tok, N, c.hidden);
+      g.part = reinterpret_cast<float*>((char*)ws + P.kvpart);
+      g.part_elems = P.kvpart_elems;
     } else {
       g = gemm_rows(ctx, c.hidden, wkv, n_tok, N, c.hidden);
     }
@@ -533,7 +556,10 @@ int32_t dflash_draft_forward(const dflash_handle* h, const dflash_kv_cache* cach
     }
 
     const int Nqkv = (Hq + 2 * Hkv) * hd;
+    float* part = reinterpret_cast<float*>(w + P.part);
     GemmArgs g = gemm_tiled(hbuf, pk + pl.qkv[l], M, Nqkv, d);
+    g.part = part;
+    g.part_elems = P.part_elems;
     g.out = qkv;
     g.out_stride = Nqkv;
     if ((rc = run_gemm(c.dtype, EPI_STORE_F32, g, st))) return rc;
@@ -589,6 +615,8 @@ int32_t dflash_draft_forward(const dflash_handle* h, const dflash_kv_cache* cach
     if (e != hipSuccess) return DFLASH_ERR_HIP;
 
     g = gemm_tiled(attn, pk + pl.wo[l], M, d, Hq * hd);
+    g.part = part;
+    g.part_elems = P.part_elems;
     g.resid = x;
     g.out_stride = d;
     if ((rc = run_gemm(c.dtype, EPI_RESID, g, st))) return rc;
@@ -603,6 +631,8 @@ int32_t dflash_draft_forward(const dflash_handle* h, const dflash_kv_cache* cach
     if ((rc = run_gemm(c.dtype, EPI_SWIGLU, g, st))) return rc;
 
     g = gemm_tiled(act, pk + pl.down[l], M, d, I);
+    g.part = part;
+    g.part_elems = P.part_elems;
     g.resid = x;
     g.out_stride = d;
     if ((rc = run_gemm(c.dtype, EPI_RESID, g, st))) return rc;

@@ -49,6 +49,8 @@ struct MfmaGeom {
   static_assert(NS >= 2, "ring needs a slot being read and one arriving");
 };
 
+__device__ __forceinline__ int p_ksplit(const GemmArgs& p) { return p.ksplit > 1 ? p.ksplit : 1; }
+
 // Wait until at most N of this wave's global->LDS loads are outstanding and
 // all of its LDS reads have returned, then meet the other waves. The memory
 // clobber keeps the compiler from moving LDS accesses across it.
@@ -73,8 +75,11 @@ void gemm_mfma_kernel(GemmArgs p, int n_colblk, int n_rowblk) {
   __shared__ unsigned long long kred[EPI == EPI_ARGMAX ? BM * WGN : 1];
 
   // Block numbering: ids 8 apart share an XCD; row blocks of one column block
-  // get consecutive multiples of 8.
-  const int id = blockIdx.x;
+  // get consecutive multiples of 8. With a K split, the slice index is the
+  // slowest-varying part of the id.
+  const int per_split = gridDim.x / p_ksplit(p);
+  const int z = blockIdx.x / per_split;
+  const int id = blockIdx.x - z * per_split;
   const int xcd = id & 7, q = id >> 3;
   const int rb = q % n_rowblk;
   const int cb = (q / n_rowblk) * 8 + xcd;
@@ -85,7 +90,11 @@ void gemm_mfma_kernel(GemmArgs p, int n_colblk, int n_rowblk) {
   const int wm = wave / WGN, wn = wave % WGN;
   const int r = lane & 15, grp = lane >> 4;
   const int nck = (p.K + kKC - 1) / kKC;
-  const int nst = p.K / (32 * KF);  // the host guarantees K % (32 KF) == 0
+  // The host guarantees K % (32 KF) == 0; slice z takes stages [s0, s0 + nst).
+  const int nst_all = p.K / (32 * KF);
+  const int per_slice = (nst_all + p_ksplit(p) - 1) / p_ksplit(p);
+  const int s0 = z * per_slice;
+  const int nst = max(0, min(per_slice, nst_all - s0));
   const int m_tiles = (p.M + 15) >> 4, n_tiles = (p.N + 15) >> 4;
   const int tile_m0 = rb * AT;
   // SwiGLU: the block's W tiles are BT/2 gate tiles then the same BT/2 up tiles.
@@ -129,7 +138,7 @@ void gemm_mfma_kernel(GemmArgs p, int n_colblk, int n_rowblk) {
   auto issue = [&](int s, int slot) {
 #pragma unroll
     for (int i = 0; i < FPW; ++i) {
-      const bf16* g = src[i] + (int64_t)(KF * s + kf[i]) * kFRAG + lane * kEPF;
+      const bf16* g = src[i] + (int64_t)(KF * (s0 + s) + kf[i]) * kFRAG + lane * kEPF;
       __builtin_amdgcn_global_load_lds((gbl_ptr_t)g, (lds_ptr_t)&lds[slot][wave + NW * i][0], 16, 0,
                                        0);
     }
@@ -235,6 +244,25 @@ void gemm_mfma_kernel(GemmArgs p, int n_colblk, int n_rowblk) {
 
   // Epilogue. Lane (r, grp) of tile (i, j) holds rows 4*grp + e of column r.
   const int row0 = tile_m0 * 16 + wm * (TM * 16);
+  if constexpr (EPI == EPI_STORE_F32 || EPI == EPI_RESID) {
+    if (p_ksplit(p) > 1) {
+      // K slice z: fp32 partial tile, summed in slice order by splitk_reduce_kernel.
+      float* part = p.part + (int64_t)z * p.M * p.N;
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const int n = (tile_n0 + wn * TN + j) * 16 + r;
+          if (n >= p.N) continue;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int m = row0 + 16 * i + 4 * grp + e;
+            if (m < p.M) part[(int64_t)m * p.N + n] = acc[i][j][e];
+          }
+        }
+      return;
+    }
+  }
   if constexpr (EPI == EPI_ARGMAX) {
     // Per row: max over this wave's columns, then over the WGN waves via LDS.
 #pragma unroll
@@ -333,14 +361,75 @@ int mfma_gemm_colblocks(int epi, int M, int N) {
   return mfma_colblocks(epi, N, mfma_block(epi, M, N));
 }
 
+// K slices for a projection: only 128x128-block fp32-store / residual
+// projections that leave most CUs without a block (<= 128 blocks: O, down and
+// the fusion at a few hundred rows, QKV at 256) are split, into as many
+// slices as fit 256 blocks, each keeping >= 8 stages of K. The partial tiles
+// cost one extra fp32 pass (M x N x 4 B per slice, written and read once).
+int mfma_gemm_ksplit(int epi, int M, int N, int K) {
+  if (epi != EPI_STORE_F32 && epi != EPI_RESID) return 1;
+  if (mfma_block(epi, M, N) != 128) return 1;
+  const long long blocks = (long long)((M + 127) / 128) * ((N + 127) / 128);
+  if (blocks > 128) return 1;
+  int ks = 1;
+  while (ks < 4 && blocks * ks * 2 <= 256 && K / (64 * ks * 2) >= 8) ks *= 2;
+  return ks;
+}
+
+// Sum of the K-slice partials in slice order, then the projection's epilogue:
+// out = sum (EPI_STORE_F32) or resid += sum (EPI_RESID). Four columns per thread.
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part, int ks,
+                                                            int M, int N, float* out,
+                                                            int64_t out_stride, int resid) {
+  const int64_t n4 = (int64_t)M * N / 4;
+  const int64_t MN = (int64_t)M * N;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    float4 acc = reinterpret_cast<const float4*>(part)[i];
+    for (int z = 1; z < ks; ++z) {
+      const float4 v = reinterpret_cast<const float4*>(part + z * MN)[i];
+      acc.x += v.x;
+      acc.y += v.y;
+      acc.z += v.z;
+      acc.w += v.w;
+    }
+    const int64_t e = 4 * i;
+    const int m = (int)(e / N), n = (int)(e % N);
+    float4* dst = reinterpret_cast<float4*>(out + (int64_t)m * out_stride + n);
+    if (resid) {
+      const float4 x = *dst;
+      acc.x += x.x;
+      acc.y += x.y;
+      acc.z += x.z;
+      acc.w += x.w;
+    }
+    *dst = acc;
+  }
+}
+
 template <int BM, int BN, int WGM, int WGN, int KF, int NS, int EPI>
-static hipError_t launch_mfma_t(const GemmArgs& a, hipStream_t st) {
+static hipError_t launch_mfma_t(const GemmArgs& a0, hipStream_t st) {
+  GemmArgs a = a0;
+  a.ksplit = 1;
+  if constexpr (EPI == EPI_STORE_F32 || EPI == EPI_RESID) {
+    const int ks = mfma_gemm_ksplit(EPI, a.M, a.N, a.K);
+    if (ks > 1 && a.part && a.part_elems >= (int64_t)ks * a.M * a.N && a.N % 4 == 0 &&
+        a.out_stride % 4 == 0)
+      a.ksplit = ks;
+  }
   const int n_colblk = mfma_colblocks(EPI, a.N, BN);
   const int n_rowblk = (a.M + BM - 1) / BM;
   const int groups = (n_colblk + 7) / 8;
-  const dim3 grid(groups * 8 * n_rowblk), block(64 * WGM * WGN);
+  const dim3 grid(groups * 8 * n_rowblk * a.ksplit), block(64 * WGM * WGN);
   hipLaunchKernelGGL((gemm_mfma_kernel<BM, BN, WGM, WGN, KF, NS, EPI>), grid, block, 0, st, a,
                      n_colblk, n_rowblk);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.ksplit == 1) return e;
+  float* dst = EPI == EPI_RESID ? a.resid : reinterpret_cast<float*>(a.out);
+  const int64_t n4 = (int64_t)a.M * a.N / 4;
+  const int blocks = (int)std::min<int64_t>((n4 + 255) / 256, 4096);
+  hipLaunchKernelGGL(splitk_reduce_kernel, dim3(blocks), dim3(256), 0, st, a.part, a.ksplit, a.M,
+                     a.N, dst, a.out_stride, EPI == EPI_RESID ? 1 : 0);
   return hipGetLastError();
 }
 

@@ -51,6 +51,11 @@ struct GemmArgs {
   int64_t amax_stride;
   float* logits;                  // EPI_ARGMAX, optional
   int64_t logits_stride;
+  // Split-K scratch of the MFMA kernel (EPI_STORE_F32 / EPI_RESID only):
+  // fp32 [ksplit][M][N], part_elems floats available; nullptr: never split.
+  float* part;
+  int64_t part_elems;
+  int ksplit;                     // K slices of an MFMA launch (set by its launcher)
 };
 
 // Launch geometry of one weight-streaming GEMM (also used to size LM-head partials).
@@ -74,6 +79,9 @@ inline bool gemm_uses_mfma(int dtype, int M, int K, bool a_tiled) {
 }
 hipError_t launch_gemm_mfma(int epi, const GemmArgs& a, hipStream_t st);
 int mfma_gemm_colblocks(int epi, int M, int N);
+// K slices the MFMA kernel splits a projection into (1 = no split); the
+// partial buffer it then needs is ksplit * M * N floats.
+int mfma_gemm_ksplit(int epi, int M, int N, int K);
 // Keys per row that the LM-head projection writes (its column blocks).
 int gemm_amax_cols(int dtype, int M, int N, int K);
 
