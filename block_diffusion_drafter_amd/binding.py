@@ -19,7 +19,7 @@ _lib = None
 DFLASH_FP32, DFLASH_BF16 = 0, 1
 DEV_CAPACITY, DEV_TOKEN, DEV_OFFSETS = 1, 2, 4
 KERNEL_CLASSES = ["gemm_f32out", "gemm_resid", "gemm_swiglu", "lm_head", "attention",
-                  "attention_combine", "norm_rope", "rmsnorm", "small"]
+                  "attention_combine", "norm_rope", "rmsnorm", "small", "sampling"]
 
 LAYER_FIELDS = ["in_norm", "wq", "wk", "wv", "q_norm", "k_norm", "wo", "post_norm",
                 "w_gate", "w_up", "w_down"]
@@ -84,6 +84,14 @@ def lib() -> ctypes.CDLL:
                                            vp, vp, vp, vp, vp, vp, i64, vp]
         L.dflash_accept.restype = i32
         L.dflash_accept.argtypes = [vp, vp, i32, i32, vp, vp, vp, vp]
+        L.dflash_sampling_workspace_bytes.restype = i64
+        L.dflash_sampling_workspace_bytes.argtypes = [i32, i32, i32]
+        L.dflash_sample_drafts.restype = i32
+        L.dflash_sample_drafts.argtypes = [vp, i64, i32, i32, ctypes.c_float, ctypes.c_uint64, i32,
+                                           vp, vp, vp, i64, vp]
+        L.dflash_verify_sampled.restype = i32
+        L.dflash_verify_sampled.argtypes = [vp, vp, vp, i32, i32, i32, ctypes.c_float,
+                                            ctypes.c_uint64, i32, vp, vp, vp, vp, i64, vp]
         L.dflash_profiler_start.restype = i32
         L.dflash_profiler_start.argtypes = [i32, ctypes.c_uint32]
         L.dflash_profiler_stop.restype = i32
@@ -269,6 +277,38 @@ def accept(draft_tokens: torch.Tensor, target_tokens: torch.Tensor, block_size: 
     _check(lib().dflash_accept(_ptr(draft_tokens), _ptr(target_tokens), target_tokens.shape[0],
                                block_size, _ptr(accept_len), _ptr(bonus), _ptr(anchor_out),
                                _stream()), "dflash_accept")
+
+
+def sampling_workspace(batch: int, block_size: int, vocab: int) -> torch.Tensor:
+    n = lib().dflash_sampling_workspace_bytes(batch, block_size, vocab)
+    if n < 0:
+        _check(int(n), "dflash_sampling_workspace_bytes")
+    return torch.empty(int(n), dtype=torch.uint8, device="cuda")
+
+
+def sample_drafts(logits: torch.Tensor, temperature: float, seed: int, rnd: int,
+                  tokens: torch.Tensor, ws: torch.Tensor,
+                  logq: Optional[torch.Tensor] = None) -> None:
+    """tokens[r] ~ softmax(logits[r] / T) (fp32 logits [rows, >= vocab])."""
+    rows, vocab = logits.shape
+    if logits.dtype != torch.float32 or logits.stride(1) != 1:
+        raise DFlashError("logits must be fp32 with unit column stride")
+    _check(lib().dflash_sample_drafts(logits.data_ptr(), logits.stride(0), rows, vocab,
+                                      float(temperature), int(seed), int(rnd), _ptr(tokens),
+                                      _ptr(logq), _ptr(ws), ws.numel(), _stream()),
+           "dflash_sample_drafts")
+
+
+def verify_sampled(drafts: torch.Tensor, draft_logits: torch.Tensor,
+                   target_logits: torch.Tensor, temperature: float, seed: int, rnd: int,
+                   accept_len: torch.Tensor, out_token: torch.Tensor, ws: torch.Tensor,
+                   anchor_out: Optional[torch.Tensor] = None) -> None:
+    """drafts [b, B-1], draft logits [b, B-1, V], target logits [b, B, V]."""
+    b, Bk, vocab = target_logits.shape
+    _check(lib().dflash_verify_sampled(_ptr(drafts), _ptr(draft_logits), _ptr(target_logits), b,
+                                       Bk, vocab, float(temperature), int(seed), int(rnd),
+                                       _ptr(accept_len), _ptr(out_token), _ptr(anchor_out),
+                                       _ptr(ws), ws.numel(), _stream()), "dflash_verify_sampled")
 
 
 def profiler_start(max_launches: int = 100000, classes: Optional[List[str]] = None) -> None:

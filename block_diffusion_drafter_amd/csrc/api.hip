@@ -671,6 +671,58 @@ int32_t dflash_draft_forward(const dflash_handle* h, const dflash_kv_cache* cach
   return DFLASH_OK;
 }
 
+int64_t dflash_sampling_workspace_bytes(int32_t batch, int32_t block_size, int32_t vocab) {
+  if (batch < 0 || block_size < 2 || block_size > 17 || vocab < 2) return DFLASH_ERR_SHAPE;
+  const int b = std::max(batch, 1);
+  return std::max(sample_ws_bytes(b * (block_size - 1), vocab), verify_ws_bytes(b, block_size, vocab));
+}
+
+int32_t dflash_sample_drafts(const float* logits, int64_t row_stride, int32_t rows, int32_t vocab,
+                             float temperature, uint64_t seed, int32_t round, int32_t* tokens,
+                             float* logq, void* ws, int64_t ws_bytes, void* stream) {
+  if (rows < 0 || vocab < 2 || row_stride < vocab || !(temperature > 0.f) ||
+      !std::isfinite(temperature))
+    return DFLASH_ERR_SHAPE;
+  if (rows == 0) return DFLASH_OK;
+  if (!logits || !tokens || !ws) return DFLASH_ERR_NULL;
+  if (!al16(logits) || !al16(tokens) || !al16(ws) || (logq && !al16(logq))) return DFLASH_ERR_ALIGN;
+  if (ws_bytes < sample_ws_bytes(rows, vocab)) return DFLASH_ERR_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  prof_begin(DFLASH_K_SAMPLING, (double)rows * row_stride * 4, 0.0, st);
+  const hipError_t e = launch_sample_drafts(logits, row_stride, rows, vocab, temperature, seed,
+                                            round, tokens, logq, ws, st);
+  prof_end(st);
+  return e == hipSuccess ? DFLASH_OK : DFLASH_ERR_HIP;
+}
+
+int32_t dflash_verify_sampled(const int32_t* drafts, const float* draft_logits,
+                              const float* target_logits, int32_t batch, int32_t block_size,
+                              int32_t vocab, float temperature, uint64_t seed, int32_t round,
+                              int32_t* accept_len, int32_t* out_token, int32_t* anchor_out,
+                              void* ws, int64_t ws_bytes, void* stream) {
+  if (batch < 0 || block_size < 2 || block_size > 17 || vocab < 2 || !(temperature > 0.f) ||
+      !std::isfinite(temperature))
+    return DFLASH_ERR_SHAPE;
+  if (batch == 0) return DFLASH_OK;
+  if (!drafts || !draft_logits || !target_logits || !accept_len || !out_token || !ws)
+    return DFLASH_ERR_NULL;
+  const void* ps[] = {drafts, draft_logits, target_logits, accept_len, out_token, ws};
+  for (const void* q : ps)
+    if (!al16(q)) return DFLASH_ERR_ALIGN;
+  if (anchor_out && !al16(anchor_out)) return DFLASH_ERR_ALIGN;
+  if (ws_bytes < verify_ws_bytes(batch, block_size, vocab)) return DFLASH_ERR_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  // bytes: every target and draft row is read once for its normaliser, the
+  // emitted row twice more (stats, residual)
+  const double rows = (double)batch * block_size + (double)batch * (block_size - 1) + 2.0 * batch;
+  prof_begin(DFLASH_K_SAMPLING, rows * vocab * 4, 0.0, st);
+  const hipError_t e = launch_verify_sampled(drafts, draft_logits, target_logits, batch, block_size,
+                                             vocab, temperature, seed, round, accept_len,
+                                             out_token, anchor_out, ws, st);
+  prof_end(st);
+  return e == hipSuccess ? DFLASH_OK : DFLASH_ERR_HIP;
+}
+
 int32_t dflash_accept(const int32_t* draft_tokens, const int32_t* target_tokens, int32_t batch,
                       int32_t block_size, int32_t* accept_len, int32_t* bonus,
                       int32_t* anchor_out, void* stream) {

@@ -179,6 +179,19 @@ hipError_t launch_accept(const int32_t* drafts, const int32_t* targets, int batc
 hipError_t launch_ctx_len_add(int32_t* ctx_len, const int32_t* cu_new, int batch, int n_tok,
                               int cap, int32_t* dev_status, hipStream_t st);
 
+// Temperature > 0 drafting and verification (sampling.hip).
+int sampling_splits(int vocab);
+int64_t sample_ws_bytes(int rows, int vocab);
+int64_t verify_ws_bytes(int batch, int block, int vocab);
+hipError_t launch_sample_drafts(const float* logits, int64_t ld, int rows, int vocab, float temp,
+                                uint64_t seed, int rnd, int32_t* tokens, float* logq, void* ws,
+                                hipStream_t st);
+hipError_t launch_verify_sampled(const int32_t* drafts, const float* draft_logits,
+                                 const float* target_logits, int batch, int block, int vocab,
+                                 float temp, uint64_t seed, int rnd, int32_t* accept_len,
+                                 int32_t* out_token, int32_t* anchor_out, void* ws,
+                                 hipStream_t st);
+
 // Profiler hooks (api.hip).
 void prof_begin(int kind, double bytes, double flops, hipStream_t st);
 void prof_end(hipStream_t st);

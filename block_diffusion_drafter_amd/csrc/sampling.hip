@@ -1,0 +1,367 @@
+// Temperature > 0: drafting by sampling and speculative verification with
+// residual resampling ("DFlash: Why a Diffusion Drafter Can Accelerate an
+// Autoregressive Model", sec. 4.2, eqs. 6-8 and Algorithm 1).
+//
+// Random numbers: Philox4x64-10 (Salmon, Moraes, Dror, Shaw, "Parallel random
+// numbers: as easy as 1, 2, 3", SC 2011). Element i of (row, round, stream)
+// is word i % 4 of the block at counter (i / 4, row, round, stream) under key
+// (seed, 0); a uniform is ((w >> 41) + 0.5) * 2^-23 (24 significant bits:
+// exact in fp32, never 0 or 1). A
+// categorical draw is a Gumbel-max: the argmax of log-probability +
+// (-log(-log u)) over the support, lowest index on ties.
+//
+// Every reduction over the vocabulary is split over workgroups of 8192
+// logits (4 per thread, one Philox block per thread), so a batch of a few
+// rows still spreads over many CUs; small kernels merge the splits.
+#include <cmath>
+
+#include "common.h"
+#include "internal.h"
+
+namespace dflash {
+
+namespace {
+
+constexpr int kSplit = 8192;  // logits per workgroup
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ void philox4x64(uint64_t c[4], uint64_t k0, uint64_t k1) {
+  const uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
+  const uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t hi0 = __umul64hi(M0, c[0]), lo0 = M0 * c[0];
+    const uint64_t hi1 = __umul64hi(M1, c[2]), lo1 = M1 * c[2];
+    const uint64_t n0 = hi1 ^ c[1] ^ k0, n2 = hi0 ^ c[3] ^ k1;
+    c[0] = n0;
+    c[1] = lo1;
+    c[2] = n2;
+    c[3] = lo0;
+    k0 += W0;
+    k1 += W1;
+  }
+}
+
+// The four uniforms of elements 4q .. 4q+3 of (row, round, stream).
+__device__ __forceinline__ void uniforms4(uint64_t seed, uint64_t q, uint64_t row, uint64_t rnd,
+                                          uint64_t stream, float u[4]) {
+  uint64_t c[4] = {q, row, rnd, stream};
+  philox4x64(c, seed, 0ull);
+#pragma unroll
+  for (int w = 0; w < 4; ++w) u[w] = ((float)(c[w] >> 41) + 0.5f) * 0x1p-23f;
+}
+
+__device__ __forceinline__ float gumbel(float u) { return -logf(-logf(u)); }
+
+// Order-preserving key of (score, index): larger score wins, lower index on ties.
+__device__ __forceinline__ unsigned long long okey(float v, unsigned idx) {
+  return argmax_key(v, idx);
+}
+
+// Online log-sum-exp state (max, sum of exp(x - max)).
+struct Lse {
+  float m = -INFINITY, s = 0.f;
+  __device__ void add(float x) {
+    if (x > m) {
+      s = s * __expf(m - x) + 1.f;
+      m = x;
+    } else {
+      s += __expf(x - m);
+    }
+  }
+  __device__ void merge(float m2, float s2) {
+    if (m2 == -INFINITY) return;
+    if (m2 > m) {
+      s = s * __expf(m - m2) + s2;
+      m = m2;
+    } else {
+      s += s2 * __expf(m2 - m);
+    }
+  }
+  __device__ float value() const { return m + logf(s); }
+};
+
+__device__ __forceinline__ unsigned long long block_max_key(unsigned long long k,
+                                                            unsigned long long* sh) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const unsigned long long x = __shfl_xor(k, o);
+    k = x > k ? x : k;
+  }
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) sh[w] = k;
+  __syncthreads();
+  unsigned long long r = 0ull;
+  for (int i = 0; i < (int)(blockDim.x >> 6); ++i) r = sh[i] > r ? sh[i] : r;
+  __syncthreads();
+  return r;
+}
+
+__device__ __forceinline__ void block_lse(Lse& l, float* shm, float* shs) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) l.merge(__shfl_xor(l.m, o), __shfl_xor(l.s, o));
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    shm[w] = l.m;
+    shs[w] = l.s;
+  }
+  __syncthreads();
+  Lse r;
+  for (int i = 0; i < (int)(blockDim.x >> 6); ++i) r.merge(shm[i], shs[i]);
+  __syncthreads();
+  l = r;
+}
+
+struct SplitStat {        // per (row, split)
+  unsigned long long key;  // Gumbel-max key (sampling) or unused
+  float m, s;              // log-sum-exp partial of logits / T
+};
+
+// ---- drafting -----------------------------------------------------------
+
+__global__ __launch_bounds__(kThreads) void sample_split_kernel(const float* logits, int64_t ld,
+                                                                 int V, float inv_t, uint64_t seed,
+                                                                 int rnd, SplitStat* part,
+                                                                 int nsplit) {
+  __shared__ unsigned long long shk[kThreads / 64];
+  __shared__ float shm[kThreads / 64], shs[kThreads / 64];
+  const int split = blockIdx.x, row = blockIdx.y;
+  const float* l = logits + (int64_t)row * ld;
+  const int v0 = split * kSplit + 4 * threadIdx.x;
+  unsigned long long key = 0ull;
+  Lse lse;
+  for (int v = v0; v < min(V, (split + 1) * kSplit); v += 4 * kThreads) {
+    float u[4];
+    uniforms4(seed, (uint64_t)(v >> 2), (uint64_t)row, (uint64_t)rnd, 0ull, u);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      if (v + w < V) {
+        const float x = l[v + w] * inv_t;
+        lse.add(x);
+        const unsigned long long k = okey(x + gumbel(u[w]), (unsigned)(v + w));
+        key = k > key ? k : key;
+      }
+    }
+  }
+  key = block_max_key(key, shk);
+  block_lse(lse, shm, shs);
+  if (threadIdx.x == 0) part[(int64_t)row * nsplit + split] = SplitStat{key, lse.m, lse.s};
+}
+
+__global__ void sample_finish_kernel(const float* logits, int64_t ld, float inv_t,
+                                     const SplitStat* part, int nsplit, int rows, int32_t* tokens,
+                                     float* logq) {
+  const int row = blockIdx.x * blockDim.x + threadIdx.x;
+  if (row >= rows) return;
+  unsigned long long key = 0ull;
+  Lse lse;
+  for (int i = 0; i < nsplit; ++i) {
+    const SplitStat& p = part[(int64_t)row * nsplit + i];
+    key = p.key > key ? p.key : key;
+    lse.merge(p.m, p.s);
+  }
+  const int tok = (int)argmax_index(key);
+  tokens[row] = tok;
+  if (logq) logq[row] = logits[(int64_t)row * ld + tok] * inv_t - lse.value();
+}
+
+// ---- verification -------------------------------------------------------
+
+// Log-sum-exp partials of every target row (b x B) and draft row (b x m),
+// draft rows stored after the target rows.
+__global__ __launch_bounds__(kThreads) void verify_stats_kernel(const float* draft_logits,
+                                                                 const float* target_logits,
+                                                                 int batch, int B, int V,
+                                                                 float inv_t, SplitStat* part,
+                                                                 int nsplit) {
+  __shared__ float shm[kThreads / 64], shs[kThreads / 64];
+  const int split = blockIdx.x, r = blockIdx.y;  // r < batch*B: target; else draft
+  const float* l = r < batch * B ? target_logits + (int64_t)r * V
+                                 : draft_logits + (int64_t)(r - batch * B) * V;
+  Lse lse;
+  const int end = min(V, (split + 1) * kSplit);
+  for (int v = split * kSplit + threadIdx.x; v < end; v += kThreads) lse.add(l[v] * inv_t);
+  block_lse(lse, shm, shs);
+  if (threadIdx.x == 0) part[(int64_t)r * nsplit + split] = SplitStat{0ull, lse.m, lse.s};
+}
+
+// Per row: log-sum-exp of logits / T from its split partials.
+__global__ void verify_lse_kernel(const SplitStat* part, int nsplit, int rows, float* lse) {
+  const int r = blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= rows) return;
+  Lse l;
+  for (int i = 0; i < nsplit; ++i) l.merge(part[(int64_t)r * nsplit + i].m, part[(int64_t)r * nsplit + i].s);
+  lse[r] = l.value();
+}
+
+// Per sequence and split: the accept test of every position (eq. 6, one
+// thread per position) and the left-to-right scan for the first rejection,
+// repeated by every split of the sequence (identical inputs, identical
+// result); then the Gumbel-max partial over this split of the emitted law:
+// the residual [p - q]_+ at the first rejected position (eq. 7), with the
+// target law as fallback when the residual support is empty, or the target's
+// next law when every candidate survived (bonus).
+__global__ __launch_bounds__(kThreads) void verify_residual_kernel(
+    const int32_t* drafts, const float* draft_logits, const float* target_logits, int batch, int B,
+    int V, float inv_t, uint64_t seed, int rnd, const float* lse, int nsplit,
+    unsigned long long* keys, int32_t* accept_out) {
+  __shared__ unsigned long long shk[kThreads / 64];
+  __shared__ int sh_ok[64];
+  __shared__ int sh_a;
+  const int split = blockIdx.x, s = blockIdx.y;
+  const int m = B - 1;  // m <= 16 < kThreads
+  if ((int)threadIdx.x < m) {
+    const int i = threadIdx.x;
+    float u4[4];
+    uniforms4(seed, (uint64_t)(i >> 2), (uint64_t)s, (uint64_t)rnd, 1ull, u4);
+    int y = drafts[(int64_t)s * m + i];
+    y = y < 0 ? 0 : (y >= V ? V - 1 : y);  // ids outside the vocabulary are clamped
+    const float lp = target_logits[((int64_t)s * B + i) * V + y] * inv_t - lse[s * B + i];
+    const float lq = draft_logits[((int64_t)s * m + i) * V + y] * inv_t - lse[batch * B + s * m + i];
+    const float alpha = fminf(1.f, expf(lp - lq));
+    sh_ok[i] = u4[i & 3] < alpha;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int a = 0;
+    while (a < m && sh_ok[a]) ++a;
+    sh_a = a;
+    if (split == 0) accept_out[s] = a;
+  }
+  __syncthreads();
+  const int a = sh_a;
+  const float lse_p = lse[s * B + a];
+  const float lse_q = a < m ? lse[batch * B + s * m + a] : 0.f;
+  const float* lp_row = target_logits + ((int64_t)s * B + a) * V;
+  const float* lq_row = a < m ? draft_logits + ((int64_t)s * m + a) * V : nullptr;
+  const uint64_t grow = (uint64_t)s * B + a;
+  unsigned long long kres = 0ull, kfb = 0ull;
+  const int v0 = split * kSplit + 4 * threadIdx.x;
+  for (int v = v0; v < min(V, (split + 1) * kSplit); v += 4 * kThreads) {
+    float u[4];
+    uniforms4(seed, (uint64_t)(v >> 2), grow, (uint64_t)rnd, 2ull, u);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const int vv = v + w;
+      if (vv >= V) continue;
+      const float g = gumbel(u[w]);
+      const float lp = lp_row[vv] * inv_t - lse_p;
+      const unsigned long long kf = okey(lp + g, (unsigned)vv);
+      kfb = kf > kfb ? kf : kfb;
+      if (lq_row) {
+        const float d = expf(lp) - expf(lq_row[vv] * inv_t - lse_q);
+        if (d > 0.f) {
+          const unsigned long long kr = okey(logf(d) + g, (unsigned)vv);
+          kres = kr > kres ? kr : kres;
+        }
+      }
+    }
+  }
+  kres = block_max_key(kres, shk);
+  kfb = block_max_key(kfb, shk);
+  if (threadIdx.x == 0) {
+    keys[((int64_t)s * nsplit + split) * 2 + 0] = kres;
+    keys[((int64_t)s * nsplit + split) * 2 + 1] = kfb;
+  }
+}
+
+__global__ void verify_finish_kernel(const unsigned long long* keys, int nsplit, int batch, int B,
+                                     const int32_t* accept_in, int32_t* accept_len,
+                                     int32_t* out_token, int32_t* anchor_out) {
+  const int s = blockIdx.x * blockDim.x + threadIdx.x;
+  if (s >= batch) return;
+  unsigned long long kr = 0ull, kf = 0ull;
+  for (int i = 0; i < nsplit; ++i) {
+    const unsigned long long a = keys[((int64_t)s * nsplit + i) * 2 + 0];
+    const unsigned long long b = keys[((int64_t)s * nsplit + i) * 2 + 1];
+    kr = a > kr ? a : kr;
+    kf = b > kf ? b : kf;
+  }
+  const int a = accept_in[s];
+  // residual draw when the rejected position's residual support is non-empty,
+  // else (bonus position, or empty support) the target-law draw
+  const unsigned long long key = (a < B - 1 && kr != 0ull) ? kr : kf;
+  const int32_t tok = (int32_t)argmax_index(key);
+  accept_len[s] = a;
+  out_token[s] = tok;
+  if (anchor_out) anchor_out[s] = tok;
+}
+
+}  // namespace
+
+int sampling_splits(int vocab) { return (vocab + kSplit - 1) / kSplit; }
+
+int64_t sample_ws_bytes(int rows, int vocab) {
+  return (int64_t)rows * sampling_splits(vocab) * (int64_t)sizeof(SplitStat);
+}
+
+namespace {
+struct VerifyWs {
+  int64_t stats, keys, lse, acc, total;
+};
+VerifyWs verify_ws(int batch, int block, int vocab) {
+  const int64_t ns = sampling_splits(vocab);
+  const int64_t rows = (int64_t)batch * block + (int64_t)batch * (block - 1);
+  auto al = [](int64_t x) { return ((x + 255) / 256) * 256; };
+  VerifyWs w{};
+  w.stats = 0;
+  w.keys = al(rows * ns * (int64_t)sizeof(SplitStat));
+  w.lse = w.keys + al((int64_t)batch * ns * 16);
+  w.acc = w.lse + al(rows * 4);
+  w.total = w.acc + al((int64_t)batch * 4);
+  return w;
+}
+}  // namespace
+
+int64_t verify_ws_bytes(int batch, int block, int vocab) { return verify_ws(batch, block, vocab).total; }
+
+hipError_t launch_sample_drafts(const float* logits, int64_t ld, int rows, int vocab, float temp,
+                                uint64_t seed, int rnd, int32_t* tokens, float* logq, void* ws,
+                                hipStream_t st) {
+  if (rows <= 0) return hipSuccess;
+  const int ns = sampling_splits(vocab);
+  SplitStat* part = reinterpret_cast<SplitStat*>(ws);
+  const float inv_t = 1.0f / temp;
+  hipLaunchKernelGGL(sample_split_kernel, dim3(ns, rows), dim3(kThreads), 0, st, logits, ld, vocab,
+                     inv_t, seed, rnd, part, ns);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(sample_finish_kernel, dim3((rows + 63) / 64), dim3(64), 0, st, logits, ld,
+                     inv_t, part, ns, rows, tokens, logq);
+  return hipGetLastError();
+}
+
+hipError_t launch_verify_sampled(const int32_t* drafts, const float* draft_logits,
+                                 const float* target_logits, int batch, int block, int vocab,
+                                 float temp, uint64_t seed, int rnd, int32_t* accept_len,
+                                 int32_t* out_token, int32_t* anchor_out, void* ws,
+                                 hipStream_t st) {
+  if (batch <= 0) return hipSuccess;
+  const int ns = sampling_splits(vocab);
+  const float inv_t = 1.0f / temp;
+  char* w = reinterpret_cast<char*>(ws);
+  const VerifyWs L = verify_ws(batch, block, vocab);
+  const int64_t stats_rows = (int64_t)batch * block + (int64_t)batch * (block - 1);
+  SplitStat* stats = reinterpret_cast<SplitStat*>(w + L.stats);
+  unsigned long long* keys = reinterpret_cast<unsigned long long*>(w + L.keys);
+  float* lse = reinterpret_cast<float*>(w + L.lse);
+  int32_t* acc = reinterpret_cast<int32_t*>(w + L.acc);
+  hipLaunchKernelGGL(verify_stats_kernel, dim3(ns, (unsigned)stats_rows), dim3(kThreads), 0, st,
+                     draft_logits, target_logits, batch, block, vocab, inv_t, stats, ns);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(verify_lse_kernel, dim3((unsigned)((stats_rows + 63) / 64)), dim3(64), 0, st,
+                     stats, ns, (int)stats_rows, lse);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(verify_residual_kernel, dim3(ns, batch), dim3(kThreads), 0, st, drafts,
+                     draft_logits, target_logits, batch, block, vocab, inv_t, seed, rnd, lse, ns,
+                     keys, acc);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(verify_finish_kernel, dim3((batch + 63) / 64), dim3(64), 0, st, keys, ns,
+                     batch, block, acc, accept_len, out_token, anchor_out);
+  return hipGetLastError();
+}
+
+}  // namespace dflash

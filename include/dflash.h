@@ -222,6 +222,56 @@ int32_t dflash_accept(const int32_t *draft_tokens, const int32_t *target_tokens,
                       int32_t block_size, int32_t *accept_len, int32_t *bonus,
                       int32_t *anchor_out, void *stream);
 
+/* Temperature > 0: drafting by sampling and speculative verification with
+ * residual resampling [R sec. 4.2 eqs. 6-8 and its Algorithm 1; W "Paper vs
+ * code": above temperature 0 the reference code verifies by rejection
+ * sampling with residual resampling]. p and q are softmax(logits / T) of the
+ * target's and the draft's logits at the same temperature T > 0 (no top-p /
+ * top-k filtering).
+ *
+ * Random numbers: Philox4x64-10 (Salmon et al., "Parallel random numbers: as
+ * easy as 1, 2, 3", SC 2011) with key (seed, 0). Element i of a (row, round,
+ * stream) triple is word i % 4 of the block at counter (i / 4, row, round,
+ * stream); a uniform is ((w >> 41) + 0.5) * 2^-23. Streams: 0 drafting (row =
+ * the logits row), 1 acceptance tests (row = sequence, element = position),
+ * 2 correction / bonus draws (row = sequence * block_size + position).
+ * A categorical draw is the Gumbel-max argmax of log-probability +
+ * (-log(-log u)) over the support, lowest index on ties.
+ *
+ * dflash_sampling_workspace_bytes: workspace bytes that both calls below need
+ * for up to `batch` sequences of `block_size` (dflash_sample_drafts with
+ * rows <= batch * (block_size - 1)). Negative dflash_status on bad sizes.
+ *
+ * dflash_sample_drafts: tokens[r] ~ softmax(logits[r] / T) for r < rows
+ * (stream 0, row r); logq[r] (optional) = log q(tokens[r]).
+ * logits: fp32 device [rows, row_stride >= vocab] -- for the drafter's
+ * candidates, dflash_draft_forward's logits output ([batch * (B-1), vocab]).
+ *
+ * dflash_verify_sampled: per sequence s, candidates drafts[s][0..B-2] are
+ * scanned left to right; candidate i is accepted when u_i < min(1,
+ * p_i(y) / q_i(y)) (eq. 6). accept_len[s] = the number accepted before the
+ * first rejection; out_token[s] = a draw from the residual [p - q]_+ at the
+ * first rejected position (eq. 7; from p if that support is empty), or, when
+ * all B-1 are accepted, the bonus token drawn from the target's law at
+ * position B-1. anchor_out (optional) receives out_token (the next anchor).
+ * drafts: int32 [batch, B-1]; draft_logits: fp32 [batch, B-1, vocab] (the
+ * logits the candidates were drawn from); target_logits: fp32
+ * [batch, B, vocab] (the target's logits at the B-1 candidate positions and
+ * the position after them). round separates the random numbers of
+ * successive rounds. Candidate ids outside [0, vocab) are clamped.
+ * Errors (before anything is enqueued): DFLASH_ERR_NULL, DFLASH_ERR_ALIGN,
+ * DFLASH_ERR_SHAPE (T not finite and > 0, vocab < 2, block_size outside
+ * 2..17, negative sizes, row_stride < vocab), DFLASH_ERR_WORKSPACE. */
+int64_t dflash_sampling_workspace_bytes(int32_t batch, int32_t block_size, int32_t vocab);
+int32_t dflash_sample_drafts(const float *logits, int64_t row_stride, int32_t rows, int32_t vocab,
+                             float temperature, uint64_t seed, int32_t round, int32_t *tokens,
+                             float *logq, void *ws, int64_t ws_bytes, void *stream);
+int32_t dflash_verify_sampled(const int32_t *drafts, const float *draft_logits,
+                              const float *target_logits, int32_t batch, int32_t block_size,
+                              int32_t vocab, float temperature, uint64_t seed, int32_t round,
+                              int32_t *accept_len, int32_t *out_token, int32_t *anchor_out,
+                              void *ws, int64_t ws_bytes, void *stream);
+
 /* Static text for a dflash_status code. */
 const char *dflash_status_string(int32_t code);
 
@@ -244,7 +294,8 @@ typedef enum dflash_kernel_class {
   DFLASH_K_NORM_ROPE = 6,    /* per-head q/k RMSNorm + RoPE + cache scatter */
   DFLASH_K_RMSNORM = 7,
   DFLASH_K_SMALL = 8,        /* embedding, argmax reduce, accept, ctx_len update */
-  DFLASH_K_NCLASSES = 9
+  DFLASH_K_SAMPLING = 9,     /* temperature > 0 drafting and verification */
+  DFLASH_K_NCLASSES = 10
 } dflash_kernel_class;
 
 int32_t dflash_profiler_start(int32_t max_launches, uint32_t class_mask);

@@ -28,8 +28,8 @@ Readings taken where the pages are silent (each repeated at its use):
     generator of Salmon, Moraes, Dror and Shaw, "Parallel random numbers: as
     easy as 1, 2, 3", SC 2011), so the GPU side can draw the same numbers from
     the same published definition: key (seed, 0); counter (i // 4, row, round,
-    stream) with word i % 4; a uniform is ((w >> 40) + 0.5) / 2^24, exact in
-    fp32 and fp64. Streams: 0 drafting (row = draft row), 1 acceptance
+    stream) with word i % 4; a uniform is ((w >> 41) + 0.5) / 2^23, exact in
+    fp32 and fp64 (24 significant bits). Streams: 0 drafting (row = draft row), 1 acceptance
     uniforms (row = sequence, i = position), 2 residual / bonus draws
     (row = sequence * B + position).
   * a categorical sample uses the Gumbel-max construction: the argmax of
@@ -93,14 +93,25 @@ def philox4x64(c0, c1, c2, c3, k0, k1):
 def uniforms(seed: int, idx, row, rnd: int, stream: int) -> np.ndarray:
     """u in (0, 1) for element indices idx of (row, round, stream): word
     idx % 4 of Philox at counter (idx // 4, row, round, stream), key (seed, 0);
-    u = ((w >> 40) + 0.5) / 2^24."""
+    u = ((w >> 41) + 0.5) / 2^23."""
     idx = np.asarray(idx, dtype=np.uint64)
     row = np.asarray(row, dtype=np.uint64)
     words = philox4x64(idx >> np.uint64(2), row, np.uint64(rnd), np.uint64(stream),
                        np.uint64(seed), np.uint64(0))
     sel = (idx & np.uint64(3)).astype(np.int64)
     w = np.choose(sel, words)
-    return ((w >> np.uint64(40)).astype(np.float64) + 0.5) / float(1 << 24)
+    return ((w >> np.uint64(41)).astype(np.float64) + 0.5) / float(1 << 23)
+
+
+def row_uniforms(seed: int, V: int, rows, rnd: int, stream: int) -> np.ndarray:
+    """uniforms(seed, arange(V), row, rnd, stream) for every row in rows
+    ([len(rows), V]), computing each Philox block once for its four elements."""
+    rows = np.asarray(rows, dtype=np.uint64).reshape(-1, 1)
+    nb = (V + 3) // 4
+    words = philox4x64(np.arange(nb, dtype=np.uint64)[None, :], rows, np.uint64(rnd),
+                       np.uint64(stream), np.uint64(seed), np.uint64(0))
+    w = np.stack(words, axis=-1).reshape(rows.shape[0], nb * 4)[:, :V]
+    return ((w >> np.uint64(41)).astype(np.float64) + 0.5) / float(1 << 23)
 
 
 def gumbel(u: np.ndarray) -> np.ndarray:
@@ -119,12 +130,13 @@ def gumbel_argmax(scores: np.ndarray, g: np.ndarray):
     """argmax of scores + g over the last axis (lowest index on ties), and the
     margin between the best and second-best perturbed score."""
     s = scores + g
-    order = np.argsort(-s, axis=-1, kind="stable")
-    top = order[..., 0]
-    best = np.take_along_axis(s, order[..., :1], axis=-1)[..., 0]
-    second = np.take_along_axis(s, order[..., 1:2], axis=-1)[..., 0] if s.shape[-1] > 1 \
-        else np.full(best.shape, -np.inf)
-    return top.astype(np.int64), best - second
+    top = np.argmax(s, axis=-1)  # first occurrence: lowest index on ties
+    best = np.take_along_axis(s, top[..., None], axis=-1)[..., 0]
+    if s.shape[-1] == 1:
+        return top.astype(np.int64), np.full(best.shape, np.inf)
+    rest = s.copy()
+    np.put_along_axis(rest, top[..., None], -np.inf, axis=-1)
+    return top.astype(np.int64), best - np.max(rest, axis=-1)
 
 
 @dataclass
@@ -140,7 +152,7 @@ def sample_drafts(logits: np.ndarray, temperature: float, seed: int, rnd: int) -
     logits = np.asarray(logits, dtype=np.float64)
     rows, V = logits.shape
     lq = log_softmax(logits, temperature)
-    g = gumbel(uniforms(seed, np.arange(V)[None, :], np.arange(rows)[:, None], rnd, 0))
+    g = gumbel(row_uniforms(seed, V, np.arange(rows), rnd, 0))
     tok, margin = gumbel_argmax(lq, g)
     return Drafted(tok, lq[np.arange(rows), tok], margin)
 
@@ -178,7 +190,7 @@ def verify(drafts: np.ndarray, draft_logits: np.ndarray, target_logits: np.ndarr
     # a = first rejected position, m if every candidate survived
     a = np.where(rejected.any(1), np.argmax(rejected, 1), m)
     um = np.where(np.arange(m)[None, :] <= a[:, None], np.abs(u - alpha), np.inf)
-    g = gumbel(uniforms(seed, np.arange(V)[None, :], (sidx * B + a)[:, None], rnd, 2))
+    g = gumbel(row_uniforms(seed, V, sidx * B + a, rnd, 2))
     lp_a = lp[sidx, a]                                  # target law at the emitted position
     lq_a = lq[sidx, np.minimum(a, m - 1)]
     d = np.exp(lp_a) - np.exp(lq_a)

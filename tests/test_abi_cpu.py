@@ -202,3 +202,31 @@ def test_profiler_state_machine():
     assert lib.dflash_profiler_read(0, ctypes.byref(n), ctypes.byref(d), ctypes.byref(d),
                                     ctypes.byref(d)) == 0
     assert n.value == 0
+
+
+def test_sampling_calls_reject_bad_arguments_before_launching():
+    lib = B.lib()
+    assert lib.dflash_sampling_workspace_bytes(4, 16, 1000) > 0
+    assert lib.dflash_sampling_workspace_bytes(4, 1, 1000) == -2
+    assert lib.dflash_sampling_workspace_bytes(4, 16, 1) == -2
+    need = lib.dflash_sampling_workspace_bytes(2, 16, 1000)
+    samp = lambda logits=FAKE, stride=1000, rows=30, T=0.8, tokens=FAKE, ws=FAKE, wsb=need: \
+        lib.dflash_sample_drafts(logits, stride, rows, 1000, T, 7, 0, tokens, None, ws, wsb, None)
+    assert samp(T=0.0) == -2
+    assert samp(T=float("nan")) == -2
+    assert samp(T=float("inf")) == -2
+    assert samp(stride=999) == -2
+    assert samp(rows=-1) == -2
+    assert samp(rows=0, logits=None) == 0  # no-op
+    assert samp(logits=None) == -1
+    assert samp(tokens=FAKE + 4) == -4
+    assert samp(wsb=16) == -5
+    ver = lambda block=16, T=1.0, drafts=FAKE, ws=FAKE, wsb=need, batch=2: lib.dflash_verify_sampled(
+        drafts, FAKE, FAKE, batch, block, 1000, T, 1, 0, FAKE, FAKE, None, ws, wsb, None)
+    assert ver(block=1) == -2
+    assert ver(block=18) == -2
+    assert ver(T=-1.0) == -2
+    assert ver(batch=0, drafts=None) == 0
+    assert ver(drafts=None) == -1
+    assert ver(ws=FAKE + 8) == -4
+    assert ver(wsb=need // 4) == -5

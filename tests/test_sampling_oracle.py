@@ -60,8 +60,17 @@ def test_philox_vectorised_matches_numpy_many():
 def test_uniforms_lattice():
     u = S.uniforms(3, np.arange(10000), 5, 2, 0)
     assert np.all(u > 0) and np.all(u < 1)
-    assert np.all(((u * (1 << 24)) - 0.5) % 1 == 0)  # on the 24-bit lattice, exact
+    assert np.array_equal(u.astype(np.float32).astype(np.float64), u)
+    assert np.all(((u * (1 << 23)) - 0.5) % 1 == 0)  # on the 23-bit lattice, exact in fp32
     assert abs(u.mean() - 0.5) < 0.01 and abs(u.var() - 1 / 12) < 0.005
+
+
+def test_row_uniforms_equal_elementwise_definition():
+    V = 37
+    rows = np.array([0, 3, 1 << 40])
+    a = S.row_uniforms(9, V, rows, 5, 2)
+    b = S.uniforms(9, np.arange(V)[None, :], rows[:, None], 5, 2)
+    assert np.array_equal(a, b)
 
 
 def chi2_ok(counts, probs, n):
