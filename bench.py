@@ -1,13 +1,17 @@
 #!/usr/bin/env python3
 """Benchmark of one DFlash drafting round on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload q1]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload q1] [--temperature T]
 
 A step is one pass of the whole hot path over one batch: fuse the target
 features of the rows accepted last round (1-16 rows per sequence, a seeded
 schedule), inject them into every layer's context K/V, run the drafter forward
 on [anchor, MASK x 15] with the fused argmax and greedy accept against seeded
 target tokens, and take the bonus token as the next anchor (written in place).
+With --temperature T > 0 the round drafts by sampling instead: the forward
+writes the draft's fp32 logits, the candidates are drawn from softmax(logits/T)
+and verified against seeded target logits by speculative rejection sampling
+(residual resampling on rejection); the emitted token becomes the anchor.
 Inputs are resident in HBM before the timed region. The context grows by the
 appended rows every step, as in decoding; the reported context range covers
 the whole run.
@@ -65,6 +69,12 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="q1", choices=["q1", "q32", "q4l", "l16"])
+    ap.add_argument("--temperature", type=float, default=0.0,
+                    help="> 0: draft by sampling softmax(logits / T) and verify by speculative "
+                         "rejection sampling against seeded target logits (0: greedy)")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the device-resident round (accept, fuse the block, inject "
+                         "the accepted rows, draft) eagerly and as one replayed HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="approximate CPU time budget of the oracle sample")
@@ -95,7 +105,7 @@ def main() -> int:
     ctx_lens = I.ctx_lengths(W)
     max_new = 16
     n_prof = max(3, min(10, a.steps))
-    total_steps = a.warmup + n_prof + a.steps
+    total_steps = a.warmup + n_prof + a.steps + (2 * (a.warmup + a.steps) if a.graph else 0)
     cap = int(((int(ctx_lens.max()) + max_new * total_steps + Bk + 31) // 32) * 32)
     print(f"[bench] workload {W.name}: batch {b}, ctx {int(ctx_lens.min())}-{int(ctx_lens.max())}, "
           f"capacity {cap}", file=sys.stderr, flush=True)
@@ -137,10 +147,31 @@ def main() -> int:
     drafts = torch.empty((b, Bk - 1), dtype=torch.int32, device="cuda")
     acc = torch.empty(b, dtype=torch.int32, device="cuda")
     status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    T = a.temperature
+    if T > 0:
+        # the draft's logits at the masked slots, the target's at the B block
+        # positions (seeded stand-ins for the target's verify pass)
+        V, m = cfg.vocab, Bk - 1
+        logits = torch.empty((b, m, V), dtype=torch.float32, device="cuda")
+        t_logits = torch.from_numpy(
+            I.normal(W.seeds["targets"], "bench.target_logits", (b, Bk, V), 2.0, False)
+            .reshape(b, Bk, V)).cuda()
+        samp_ws = B.sampling_workspace(b, Bk, V)
+        out_tok = torch.empty(b, dtype=torch.int32, device="cuda")
+    rnd = [0]
 
     def step():
         model.ctx_project(feats_d, ctx_new, ws)
         model.ctx_kv_append(cache, ctx_new, cu_new, ws, status)
+        if T > 0:
+            # sample the candidates from the draft's laws, verify them against
+            # the target's; the emitted token is written over the anchor
+            model.draft_forward(cache, anchor, drafts, ws, logits=logits, dev_status=status)
+            B.sample_drafts(logits.view(b * m, V), T, 1234, rnd[0], drafts.view(-1), samp_ws)
+            B.verify_sampled(drafts, logits, t_logits, T, 1234, rnd[0], acc, out_tok, samp_ws,
+                             anchor_out=anchor)
+            rnd[0] += 1
+            return
         # the bonus token is written over the anchor: next round's anchor
         model.draft_forward(cache, anchor, drafts, ws, target_tokens=targets, accept_len=acc,
                             bonus=anchor, dev_status=status)
@@ -236,6 +267,7 @@ def main() -> int:
                    "ctx_len": [int(ctx_lens.min()), int(ctx_end.max())],
                    "new_rows_per_round": int(n_tok), "hidden": d, "heads": [Hq, Hkv],
                    "intermediate": cfg.intermediate, "vocab": cfg.vocab,
+                   "decoding": f"sampled, temperature {T}" if T > 0 else "greedy",
                    "parallelism": "none (1 GPU)"},
         "roofline": roof,
         "step_roofline": {"t_roof_ms": round(t_roof * 1e3, 5),
@@ -245,11 +277,56 @@ def main() -> int:
         "wall_s_timed": round(wall, 4),
     }
 
+    if a.graph:
+        out["round_graph"] = time_round_graph(a, B, I, torch_io, W, model, cache, ws, anchor,
+                                              drafts, acc, status)
+
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(W, host, ctx_lens, n_new, feats, a.cpu_seconds)
 
     print(json.dumps(out), flush=True)
     return 0
+
+
+def time_round_graph(a, B, I, torch_io, W, model, cache, ws, anchor, drafts, acc, status):
+    """The device-resident round (accept the verified block, fuse the features
+    of all its B positions, inject the accepted rows, draft the next block):
+    the four calls made one by one, then the same round captured once as a HIP
+    graph and replayed. The synthetic target tokens are fixed, so the accept
+    lengths (and with them the rows injected) come from the device."""
+    import torch
+    cfg = W.model
+    b, Bk = W.batch, cfg.block_size
+    feats = [torch_io.to_device(f) for f in
+             I.target_hiddens(cfg, b * Bk, seed=W.seeds["round_base"], tag="block")]
+    targets = torch.from_numpy(I.uniform_tokens(cfg, (b, Bk), W.seeds["targets"], "graph")).cuda()
+    ctx = torch.empty((b * Bk, cfg.hidden), dtype=model.dtype, device="cuda")
+
+    def eager():
+        B.accept(drafts, targets, Bk, acc, anchor)
+        model.ctx_project(feats, ctx, ws)
+        model.ctx_kv_append_accepted(cache, ctx, acc, ws, status)
+        model.draft_forward(cache, anchor, drafts, ws, dev_status=status)
+
+    g = B.RoundGraph(model, cache, feats, targets, drafts, acc, anchor, ctx, ws, None, status)
+    res = {}
+    for name, fn in (("eager", eager), ("graph", g.replay)):
+        for _ in range(a.warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(a.steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        res[f"ms_per_round_{name}"] = round(e0.elapsed_time(e1) / a.steps, 5)
+    g.close()
+    assert status.item() == 0, f"device status {status.item()}"
+    res["block_tokens_per_s_graph"] = round(b * Bk / (res["ms_per_round_graph"] / 1e3), 1)
+    res["rows_fused_per_round"] = b * Bk
+    return res
 
 
 def cpu_baseline(W, host, ctx_lens, n_new, feats, budget_s):

@@ -48,6 +48,15 @@ class KVCacheStruct(ctypes.Structure):
                 ("batch", ctypes.c_int32), ("capacity", ctypes.c_int32)]
 
 
+class RoundIOStruct(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("feats", ctypes.POINTER(ctypes.c_void_p)),
+                ("feat_row_stride", ctypes.c_int64), ("target_tokens", ctypes.c_void_p),
+                ("draft_tokens", ctypes.c_void_p), ("accept_len", ctypes.c_void_p),
+                ("anchor", ctypes.c_void_p), ("ctx", ctypes.c_void_p), ("logits", ctypes.c_void_p),
+                ("dev_status", ctypes.c_void_p), ("ws", ctypes.c_void_p),
+                ("ws_bytes", ctypes.c_int64)]
+
+
 class DFlashError(RuntimeError):
     pass
 
@@ -79,6 +88,17 @@ def lib() -> ctypes.CDLL:
         L.dflash_ctx_kv_append.restype = i32
         L.dflash_ctx_kv_append.argtypes = [vp, ctypes.POINTER(KVCacheStruct), vp, vp, i32, vp,
                                            vp, i64, vp]
+        L.dflash_ctx_kv_append_accepted.restype = i32
+        L.dflash_ctx_kv_append_accepted.argtypes = [vp, ctypes.POINTER(KVCacheStruct), vp, vp, vp,
+                                                    vp, i64, vp]
+        L.dflash_round_graph_create.restype = i32
+        L.dflash_round_graph_create.argtypes = [vp, ctypes.POINTER(KVCacheStruct),
+                                                ctypes.POINTER(RoundIOStruct), vp,
+                                                ctypes.POINTER(vp)]
+        L.dflash_round_graph_launch.restype = i32
+        L.dflash_round_graph_launch.argtypes = [vp, vp]
+        L.dflash_round_graph_destroy.restype = None
+        L.dflash_round_graph_destroy.argtypes = [vp]
         L.dflash_draft_forward.restype = i32
         L.dflash_draft_forward.argtypes = [vp, ctypes.POINTER(KVCacheStruct), vp, i32, vp, vp,
                                            vp, vp, vp, vp, vp, vp, i64, vp]
@@ -257,6 +277,18 @@ class DraftModel:
                                           ctx.shape[0], _ptr(dev_status), _ptr(ws), ws.numel(),
                                           _stream()), "dflash_ctx_kv_append")
 
+    def ctx_kv_append_accepted(self, cache: KVCache, ctx: torch.Tensor, accept_len: torch.Tensor,
+                               ws: torch.Tensor, dev_status: Optional[torch.Tensor] = None) -> None:
+        """ctx: the block positions of every sequence [batch * B, hidden];
+        rows 0..accept_len[s] of sequence s join its context."""
+        if ctx.shape[0] != cache.batch * self.cfg.block_size:
+            raise DFlashError("ctx must hold batch * block_size rows")
+        st = cache.struct()
+        _check(lib().dflash_ctx_kv_append_accepted(self.handle, ctypes.byref(st), _ptr(ctx),
+                                                   _ptr(accept_len), _ptr(dev_status), _ptr(ws),
+                                                   ws.numel(), _stream()),
+               "dflash_ctx_kv_append_accepted")
+
     def draft_forward(self, cache: KVCache, anchor: torch.Tensor, draft_tokens: torch.Tensor,
                       ws: torch.Tensor, logits: Optional[torch.Tensor] = None,
                       hidden_out: Optional[torch.Tensor] = None,
@@ -269,6 +301,52 @@ class DraftModel:
             self.handle, ctypes.byref(st), _ptr(anchor), anchor.shape[0], _ptr(draft_tokens),
             _ptr(logits), _ptr(hidden_out), _ptr(target_tokens), _ptr(accept_len), _ptr(bonus),
             _ptr(dev_status), _ptr(ws), ws.numel(), _stream()), "dflash_draft_forward")
+
+
+class RoundGraph:
+    """A decoding round captured once by dflash_round_graph_create and replayed
+    with dflash_round_graph_launch: accept the verified block, fuse its
+    features, inject the accepted rows, draft the next block. The tensors are
+    the graph's fixed buffers: refill feats and target_tokens between replays.
+    Capture runs on a side stream (the default stream cannot be captured)."""
+
+    def __init__(self, model: DraftModel, cache: KVCache, feats: Sequence[torch.Tensor],
+                 target_tokens: torch.Tensor, draft_tokens: torch.Tensor,
+                 accept_len: torch.Tensor, anchor: torch.Tensor, ctx: torch.Tensor,
+                 ws: torch.Tensor, logits: Optional[torch.Tensor] = None,
+                 dev_status: Optional[torch.Tensor] = None):
+        stride = feats[0].stride(0)
+        for f in feats:
+            if f.stride(0) != stride or f.stride(1) != 1 or not f.is_cuda:
+                raise DFlashError("features must be row-major device tensors with one row stride")
+        # keep every buffer the graph points at alive as long as the graph
+        self._keep = (model, cache, list(feats), target_tokens, draft_tokens, accept_len, anchor,
+                      ctx, ws, logits, dev_status)
+        self._cache = cache.struct()
+        self._feat_ptrs = (ctypes.c_void_p * len(feats))(*[f.data_ptr() for f in feats])
+        self._io = RoundIOStruct(cache.batch, ctypes.cast(self._feat_ptrs,
+                                                          ctypes.POINTER(ctypes.c_void_p)),
+                                 stride, _ptr(target_tokens), _ptr(draft_tokens), _ptr(accept_len),
+                                 _ptr(anchor), _ptr(ctx), _ptr(logits), _ptr(dev_status), _ptr(ws),
+                                 ws.numel())
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        g = ctypes.c_void_p()
+        _check(lib().dflash_round_graph_create(model.handle, ctypes.byref(self._cache),
+                                               ctypes.byref(self._io), side.cuda_stream,
+                                               ctypes.byref(g)), "dflash_round_graph_create")
+        self.graph = g
+
+    def replay(self) -> None:
+        _check(lib().dflash_round_graph_launch(self.graph, _stream()), "dflash_round_graph_launch")
+
+    def close(self) -> None:
+        if getattr(self, "graph", None) is not None and _lib is not None:
+            _lib.dflash_round_graph_destroy(self.graph)
+            self.graph = None
+
+    def __del__(self):
+        self.close()
 
 
 def accept(draft_tokens: torch.Tensor, target_tokens: torch.Tensor, block_size: int,

@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <new>
 #include <vector>
 
 #include "internal.h"
@@ -61,6 +62,12 @@ void prof_end(hipStream_t st) {
 }  // namespace dflash
 
 using namespace dflash;
+
+// A captured decoding round: the graph and its executable instance.
+struct dflash_round_graph {
+  hipGraph_t graph;
+  hipGraphExec_t exec;
+};
 
 namespace {
 
@@ -280,7 +287,7 @@ const char* dflash_status_string(int32_t code) {
     case DFLASH_ERR_WORKSPACE: return "workspace or packed buffer is smaller than its size query";
     case DFLASH_ERR_UNSUPPORTED: return "configuration not covered by the kernels";
     case DFLASH_ERR_HIP: return "a HIP launch reported an error";
-    case DFLASH_ERR_STATE: return "profiler misuse";
+    case DFLASH_ERR_STATE: return "profiler misuse, or graph capture while the profiler records";
     default: return "unknown status";
   }
 }
@@ -431,15 +438,17 @@ int32_t dflash_ctx_project(const dflash_handle* h, const void* const* feats,
   return e == hipSuccess ? DFLASH_OK : DFLASH_ERR_HIP;
 }
 
-int32_t dflash_ctx_kv_append(const dflash_handle* h, const dflash_kv_cache* cache, const void* ctx,
-                             const int32_t* cu_new, int32_t n_tok, int32_t* dev_status, void* ws,
-                             int64_t ws_bytes, void* stream) {
-  if (!h) return DFLASH_ERR_NULL;
+// Context K/V injection of n_tok rows; a row's sequence and position come from
+// the prefix offsets cu_new, or, when accept_len is given, from the block
+// layout (row s*B + i, kept for i <= accept_len[s]).
+static int32_t append_rows(const dflash_handle* h, const dflash_kv_cache* cache, const void* ctx,
+                           const int32_t* cu_new, const int32_t* accept_len, int32_t n_tok,
+                           int32_t* dev_status, void* ws, int64_t ws_bytes, void* stream) {
   const dflash_config& c = h->cfg;
   int32_t rc = check_cache(h, cache);
   if (rc) return rc;
   if (n_tok < 0) return DFLASH_ERR_SHAPE;
-  if (!cu_new) return DFLASH_ERR_NULL;
+  if (!cu_new && !accept_len) return DFLASH_ERR_NULL;
   if (n_tok > 0 && (!ctx || !ws)) return DFLASH_ERR_NULL;
   if ((ctx && !al16(ctx)) || (ws && !al16(ws))) return DFLASH_ERR_ALIGN;
   const Plan P = make_plan(c, 1, cache->capacity, n_tok);
@@ -476,6 +485,7 @@ int32_t dflash_ctx_kv_append(const dflash_handle* h, const dflash_kv_cache* cach
     for (int l = 0; l < L; ++l) a.k_norm[l] = h->layers[l].k_norm;
     a.ctx_len = cache->ctx_len;
     a.cu_new = cu_new;
+    a.accept_len = accept_len;
     a.dev_status = dev_status;
     a.batch = cache->batch;
     a.cache_batch = cache->batch;
@@ -494,10 +504,31 @@ int32_t dflash_ctx_kv_append(const dflash_handle* h, const dflash_kv_cache* cach
     if (e != hipSuccess) return DFLASH_ERR_HIP;
   }
   prof_begin(DFLASH_K_SMALL, 0, 0, st);
-  hipError_t e = launch_ctx_len_add(cache->ctx_len, cu_new, cache->batch, n_tok, cache->capacity,
-                                    dev_status, st);
+  hipError_t e = launch_ctx_len_add(cache->ctx_len, cu_new, accept_len, c.block_size,
+                                    cache->batch, n_tok, cache->capacity, dev_status, st);
   prof_end(st);
   return e == hipSuccess ? DFLASH_OK : DFLASH_ERR_HIP;
+}
+
+int32_t dflash_ctx_kv_append(const dflash_handle* h, const dflash_kv_cache* cache, const void* ctx,
+                             const int32_t* cu_new, int32_t n_tok, int32_t* dev_status, void* ws,
+                             int64_t ws_bytes, void* stream) {
+  if (!h) return DFLASH_ERR_NULL;
+  if (!cu_new) return DFLASH_ERR_NULL;
+  return append_rows(h, cache, ctx, cu_new, nullptr, n_tok, dev_status, ws, ws_bytes, stream);
+}
+
+int32_t dflash_ctx_kv_append_accepted(const dflash_handle* h, const dflash_kv_cache* cache,
+                                      const void* ctx, const int32_t* accept_len,
+                                      int32_t* dev_status, void* ws, int64_t ws_bytes,
+                                      void* stream) {
+  if (!h || !cache) return DFLASH_ERR_NULL;
+  if (!accept_len) return DFLASH_ERR_NULL;
+  if (!al16(accept_len)) return DFLASH_ERR_ALIGN;
+  if (cache->batch < 0 || (int64_t)cache->batch * h->cfg.block_size > INT32_MAX)
+    return DFLASH_ERR_SHAPE;
+  return append_rows(h, cache, ctx, nullptr, accept_len, cache->batch * h->cfg.block_size,
+                     dev_status, ws, ws_bytes, stream);
 }
 
 int32_t dflash_draft_forward(const dflash_handle* h, const dflash_kv_cache* cache,
@@ -688,7 +719,7 @@ int32_t dflash_sample_drafts(const float* logits, int64_t row_stride, int32_t ro
   if (!al16(logits) || !al16(tokens) || !al16(ws) || (logq && !al16(logq))) return DFLASH_ERR_ALIGN;
   if (ws_bytes < sample_ws_bytes(rows, vocab)) return DFLASH_ERR_WORKSPACE;
   hipStream_t st = (hipStream_t)stream;
-  prof_begin(DFLASH_K_SAMPLING, (double)rows * row_stride * 4, 0.0, st);
+  prof_begin(DFLASH_K_SAMPLING, (double)rows * vocab * 4, 0.0, st);
   const hipError_t e = launch_sample_drafts(logits, row_stride, rows, vocab, temperature, seed,
                                             round, tokens, logq, ws, st);
   prof_end(st);
@@ -736,6 +767,66 @@ int32_t dflash_accept(const int32_t* draft_tokens, const int32_t* target_tokens,
                                anchor_out, st);
   prof_end(st);
   return e == hipSuccess ? DFLASH_OK : DFLASH_ERR_HIP;
+}
+
+int32_t dflash_round_graph_create(const dflash_handle* h, const dflash_kv_cache* cache,
+                                  const dflash_round_io* io, void* stream,
+                                  dflash_round_graph** out) {
+  if (!out) return DFLASH_ERR_NULL;
+  *out = nullptr;
+  if (!h || !cache || !io || !stream) return DFLASH_ERR_NULL;
+  if (g_prof_on) return DFLASH_ERR_STATE;  // its event records would be baked into the graph
+  if (io->batch <= 0 || io->batch != cache->batch) return DFLASH_ERR_SHAPE;
+  const int B = h->cfg.block_size;
+  if ((int64_t)io->batch * B > INT32_MAX) return DFLASH_ERR_SHAPE;
+  hipStream_t st = (hipStream_t)stream;
+  if (hipStreamBeginCapture(st, hipStreamCaptureModeThreadLocal) != hipSuccess)
+    return DFLASH_ERR_HIP;
+  // Each call validates its arguments before enqueuing anything; the first
+  // error ends the capture and discards what it holds.
+  int32_t rc = dflash_accept(io->draft_tokens, io->target_tokens, io->batch, B, io->accept_len,
+                             io->anchor, nullptr, stream);
+  if (!rc)
+    rc = dflash_ctx_project(h, io->feats, io->feat_row_stride, io->batch * B, io->ctx, io->ws,
+                            io->ws_bytes, stream);
+  if (!rc)
+    rc = dflash_ctx_kv_append_accepted(h, cache, io->ctx, io->accept_len, io->dev_status, io->ws,
+                                       io->ws_bytes, stream);
+  if (!rc)
+    rc = dflash_draft_forward(h, cache, io->anchor, io->batch, io->draft_tokens, io->logits,
+                              nullptr, nullptr, nullptr, nullptr, io->dev_status, io->ws,
+                              io->ws_bytes, stream);
+  hipGraph_t graph = nullptr;
+  const hipError_t ec = hipStreamEndCapture(st, &graph);
+  if (rc || ec != hipSuccess || !graph) {
+    if (graph) (void)hipGraphDestroy(graph);
+    return rc ? rc : DFLASH_ERR_HIP;
+  }
+  hipGraphExec_t exec = nullptr;
+  if (hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0) != hipSuccess) {
+    (void)hipGraphDestroy(graph);
+    return DFLASH_ERR_HIP;
+  }
+  dflash_round_graph* g = new (std::nothrow) dflash_round_graph{graph, exec};
+  if (!g) {
+    (void)hipGraphExecDestroy(exec);
+    (void)hipGraphDestroy(graph);
+    return DFLASH_ERR_HIP;
+  }
+  *out = g;
+  return DFLASH_OK;
+}
+
+int32_t dflash_round_graph_launch(dflash_round_graph* g, void* stream) {
+  if (!g) return DFLASH_ERR_NULL;
+  return hipGraphLaunch(g->exec, (hipStream_t)stream) == hipSuccess ? DFLASH_OK : DFLASH_ERR_HIP;
+}
+
+void dflash_round_graph_destroy(dflash_round_graph* g) {
+  if (!g) return;
+  (void)hipGraphExecDestroy(g->exec);
+  (void)hipGraphDestroy(g->graph);
+  delete g;
 }
 
 int32_t dflash_profiler_start(int32_t max_launches, uint32_t class_mask) {

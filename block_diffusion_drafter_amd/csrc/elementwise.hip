@@ -8,6 +8,12 @@
 
 namespace dflash {
 
+// Rows of a verified block that enter the context: the anchor and the accepted
+// candidates, accept length + 1, with the length clamped to [0, block).
+__device__ __forceinline__ int accepted_rows(int a, int block) {
+  return (a < 0 ? 0 : (a >= block ? block - 1 : a)) + 1;
+}
+
 __device__ __forceinline__ float block_sum(float v, float* sh) {
   v = wave_sum(v);
   const int w = threadIdx.x >> 6;
@@ -258,20 +264,28 @@ __global__ __launch_bounds__(64) void norm_rope_append_kernel(NormRopeArgs p) {
   const int col = blockIdx.x, row = blockIdx.y, lane = threadIdx.x;
   const int Hkv = p.n_kv_heads;
   const int l = col / (2 * Hkv), hh = col % (2 * Hkv);
-  int s = -1;
-  for (int t = 0; t < p.batch; ++t) {
-    if (p.cu_new[t] <= row && row < p.cu_new[t + 1]) {
-      s = t;
-      break;
+  int s = -1, i = 0;
+  if (p.accept_len) {
+    // block rows: position i of sequence s, kept for i <= accept length
+    s = row / p.block;
+    i = row - s * p.block;
+    if (i > accepted_rows(p.accept_len[s], p.block) - 1) return;
+  } else {
+    for (int t = 0; t < p.batch; ++t) {
+      if (p.cu_new[t] <= row && row < p.cu_new[t + 1]) {
+        s = t;
+        break;
+      }
     }
-  }
-  if (s < 0) {
-    if (lane == 0 && p.dev_status) atomicOr(p.dev_status, DFLASH_DEV_OFFSETS);
-    return;
+    if (s < 0) {
+      if (lane == 0 && p.dev_status) atomicOr(p.dev_status, DFLASH_DEV_OFFSETS);
+      return;
+    }
+    i = row - p.cu_new[s];
   }
   int cl = p.ctx_len[s];
   cl = cl < 0 ? 0 : cl;
-  const int pos = cl + (row - p.cu_new[s]);
+  const int pos = cl + i;
   if (pos >= p.cap) {
     if (lane == 0 && p.dev_status) atomicOr(p.dev_status, DFLASH_DEV_CAPACITY);
     return;
@@ -415,16 +429,24 @@ hipError_t launch_accept(const int32_t* drafts, const int32_t* targets, int batc
   return hipGetLastError();
 }
 
-__global__ void ctx_len_add_kernel(int32_t* ctx_len, const int32_t* cu_new, int batch, int n_tok,
+__global__ void ctx_len_add_kernel(int32_t* ctx_len, const int32_t* cu_new,
+                                   const int32_t* accept_len, int block, int batch, int n_tok,
                                    int cap, int32_t* dev_status) {
   const int s = blockIdx.x * blockDim.x + threadIdx.x;
-  if (s == 0 && (cu_new[0] != 0 || cu_new[batch] != n_tok) && dev_status)
+  if (!accept_len && s == 0 && (cu_new[0] != 0 || cu_new[batch] != n_tok) && dev_status)
     atomicOr(dev_status, DFLASH_DEV_OFFSETS);
   if (s >= batch) return;
-  int n = cu_new[s + 1] - cu_new[s];
-  if (n < 0) {
-    if (dev_status) atomicOr(dev_status, DFLASH_DEV_OFFSETS);
-    n = 0;
+  int n;
+  if (accept_len) {
+    const int a = accept_len[s];
+    if ((a < 0 || a >= block) && dev_status) atomicOr(dev_status, DFLASH_DEV_OFFSETS);
+    n = accepted_rows(a, block);
+  } else {
+    n = cu_new[s + 1] - cu_new[s];
+    if (n < 0) {
+      if (dev_status) atomicOr(dev_status, DFLASH_DEV_OFFSETS);
+      n = 0;
+    }
   }
   int cl = ctx_len[s];
   cl = cl < 0 ? 0 : cl;
@@ -436,10 +458,11 @@ __global__ void ctx_len_add_kernel(int32_t* ctx_len, const int32_t* cu_new, int 
   ctx_len[s] = nl;
 }
 
-hipError_t launch_ctx_len_add(int32_t* ctx_len, const int32_t* cu_new, int batch, int n_tok,
-                              int cap, int32_t* dev_status, hipStream_t st) {
+hipError_t launch_ctx_len_add(int32_t* ctx_len, const int32_t* cu_new, const int32_t* accept_len,
+                              int block, int batch, int n_tok, int cap, int32_t* dev_status,
+                              hipStream_t st) {
   hipLaunchKernelGGL(ctx_len_add_kernel, dim3((batch + 63) / 64), dim3(64), 0, st, ctx_len, cu_new,
-                     batch, n_tok, cap, dev_status);
+                     accept_len, block, batch, n_tok, cap, dev_status);
   return hipGetLastError();
 }
 

@@ -141,7 +141,9 @@ struct NormRopeArgs {
   const void* q_norm[kMaxLayers];   // per-layer gains [hd] (forward mode: only [0])
   const void* k_norm[kMaxLayers];
   const int32_t* ctx_len;
-  const int32_t* cu_new;  // append mode only
+  const int32_t* cu_new;  // append mode: row offsets of each sequence's new rows
+  const int32_t* accept_len;  // append mode, block rows: when non-null, row s*block + i of
+                              // sequence s is appended iff i <= accept_len[s] (cu_new unused)
   int32_t* dev_status;
   int batch, cache_batch, n_heads, n_kv_heads, head_dim, block, cap, n_layers;
   int n_tok;              // append mode
@@ -176,8 +178,12 @@ hipError_t launch_accept(const int32_t* drafts, const int32_t* targets, int batc
                          int32_t* accept_len, int32_t* bonus, int32_t* anchor_out,
                          hipStream_t st);
 
-hipError_t launch_ctx_len_add(int32_t* ctx_len, const int32_t* cu_new, int batch, int n_tok,
-                              int cap, int32_t* dev_status, hipStream_t st);
+// ctx_len[s] += cu_new[s+1] - cu_new[s], or, when accept_len is non-null,
+// ctx_len[s] += accept_len[s] + 1 (accept lengths outside [0, block) are
+// clamped and flagged); clamped to cap.
+hipError_t launch_ctx_len_add(int32_t* ctx_len, const int32_t* cu_new, const int32_t* accept_len,
+                              int block, int batch, int n_tok, int cap, int32_t* dev_status,
+                              hipStream_t st);
 
 // Temperature > 0 drafting and verification (sampling.hip).
 int sampling_splits(int vocab);

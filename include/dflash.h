@@ -55,7 +55,7 @@ typedef enum dflash_status {
   DFLASH_ERR_WORKSPACE = -5,     /* workspace or packed buffer smaller than its size query */
   DFLASH_ERR_UNSUPPORTED = -6,   /* a configuration the kernels do not cover */
   DFLASH_ERR_HIP = -7,           /* a HIP launch reported an error */
-  DFLASH_ERR_STATE = -8          /* profiler misuse */
+  DFLASH_ERR_STATE = -8          /* profiler misuse, or graph capture while it records */
 } dflash_status;
 
 typedef enum dflash_dtype { DFLASH_FP32 = 0, DFLASH_BF16 = 1 } dflash_dtype;
@@ -190,6 +190,22 @@ int32_t dflash_ctx_kv_append(const dflash_handle *h, const dflash_kv_cache *cach
                              const void *ctx, const int32_t *cu_new, int32_t n_tok,
                              int32_t *dev_status, void *ws, int64_t ws_bytes, void *stream);
 
+/* The same injection for the rows of a verified block, with the row count
+ * taken on the device [W decoding-loop pseudocode: the accepted tokens' target
+ * features join the context before the next round; R sec. 4.1]: for every
+ * sequence s < cache->batch, rows s*B + i of ctx with i <= accept_len[s] (the
+ * anchor and the accepted candidates) are stored at pos = ctx_len[s] + i, then
+ * ctx_len[s] += accept_len[s] + 1. No host-side count, so a round built on it
+ * has fixed shapes (it can be captured in a HIP graph).
+ * ctx: [cache->batch * B, hidden] model dtype: the block positions of every
+ *      sequence (dflash_ctx_project over cache->batch * B rows);
+ * accept_len: DEVICE int32 [cache->batch], values in [0, B-1] (dflash_accept's
+ *      output); a value outside is clamped and flags DFLASH_DEV_OFFSETS. */
+int32_t dflash_ctx_kv_append_accepted(const dflash_handle *h, const dflash_kv_cache *cache,
+                                      const void *ctx, const int32_t *accept_len,
+                                      int32_t *dev_status, void *ws, int64_t ws_bytes,
+                                      void *stream);
+
 /* One parallel drafter pass over batch sequences [W decoding-loop and
  * draft-layer pseudocode; "Method" steps 2-3]:
  *   block = [anchor[s], MASK x (B-1)] embedded with `embed`;
@@ -271,6 +287,56 @@ int32_t dflash_verify_sampled(const int32_t *drafts, const float *draft_logits,
                               int32_t vocab, float temperature, uint64_t seed, int32_t round,
                               int32_t *accept_len, int32_t *out_token, int32_t *anchor_out,
                               void *ws, int64_t ws_bytes, void *stream);
+
+/* A whole decoding round with device-resident state, captured once as a HIP
+ * graph and replayed [W decoding-loop pseudocode; R sec. 3.1 eq. 4, whose
+ * T_o term is the per-round orchestration and cache overhead this removes]. Between two replays the caller's target pass writes
+ * its tokens and features for the block the previous replay drafted; one
+ * replay then runs, on the stream it is launched on:
+ *   1. dflash_accept(draft_tokens, target_tokens) -> accept_len, and the
+ *      bonus written over anchor;
+ *   2. dflash_ctx_project(feats, batch * B rows) -> ctx;
+ *   3. dflash_ctx_kv_append_accepted(ctx, accept_len): the anchor and the
+ *      accepted candidates join the context, ctx_len advances on the device;
+ *   4. dflash_draft_forward(anchor) -> draft_tokens (and logits when given)
+ *      for the next block.
+ * Every pointer in io and *cache, and the values of the sizes, are fixed at
+ * creation; the buffers' contents may change between replays. The first
+ * block's drafts come from an ordinary dflash_draft_forward call.
+ * The workspace and ctx belong to the graph while replays may run; replays
+ * of one graph, and other calls on the same buffers, must not overlap.
+ *
+ * dflash_round_graph_create: captures the four steps on `stream`, which must
+ * be a stream that can be captured (not the legacy NULL stream), and
+ * instantiates the graph. Arguments are validated as by the four calls;
+ * DFLASH_ERR_STATE while the profiler records, DFLASH_ERR_HIP when capture or
+ * instantiation fails. Nothing is enqueued on `stream`.
+ * dflash_round_graph_launch: enqueues one replay on `stream` (any stream).
+ * dflash_round_graph_destroy: frees the graph (host and driver objects only). */
+typedef struct dflash_round_io {
+  int32_t batch;                /* sequences; must equal cache->batch */
+  const void *const *feats;     /* HOST array of n_target_feats device pointers, each
+                                   [batch * B, target_hidden]: the target's features at
+                                   every block position (row s*B + i) */
+  int64_t feat_row_stride;      /* elements */
+  const int32_t *target_tokens; /* device [batch, B]: the target's tokens for the block */
+  int32_t *draft_tokens;        /* device [batch, B-1]: read (the verified block), then
+                                   overwritten with the next block's drafts */
+  int32_t *accept_len;          /* device [batch], written */
+  int32_t *anchor;              /* device [batch]: set to the bonus token, then drafted from */
+  void *ctx;                    /* device [batch * B, hidden], model dtype (scratch) */
+  float *logits;                /* optional fp32 [batch, B-1, vocab] */
+  int32_t *dev_status;          /* optional */
+  void *ws;                     /* workspace of dflash_workspace_bytes(h, batch,
+                                   cache->capacity, batch * B) bytes */
+  int64_t ws_bytes;
+} dflash_round_io;
+typedef struct dflash_round_graph dflash_round_graph;
+int32_t dflash_round_graph_create(const dflash_handle *h, const dflash_kv_cache *cache,
+                                  const dflash_round_io *io, void *stream,
+                                  dflash_round_graph **out);
+int32_t dflash_round_graph_launch(dflash_round_graph *g, void *stream);
+void dflash_round_graph_destroy(dflash_round_graph *g);
 
 /* Static text for a dflash_status code. */
 const char *dflash_status_string(int32_t code);

@@ -230,3 +230,40 @@ def test_sampling_calls_reject_bad_arguments_before_launching():
     assert ver(drafts=None) == -1
     assert ver(ws=FAKE + 8) == -4
     assert ver(wsb=need // 4) == -5
+
+
+def test_block_append_and_round_graph_reject_bad_arguments_before_launching():
+    lib = B.lib()
+    rc, h = create(B.make_config(TINY_FP32))
+    assert rc == 0
+    cache = B.KVCacheStruct(FAKE, FAKE, FAKE, 2, 64)
+    need = lib.dflash_workspace_bytes(h, 2, 64, 2 * TINY_FP32.block_size)
+    app = lambda ctx=FAKE, acc=FAKE, ws=FAKE, wsb=need, c=cache: \
+        lib.dflash_ctx_kv_append_accepted(h, ctypes.byref(c), ctx, acc, None, ws, wsb, None)
+    assert app(acc=None) == -1
+    assert app(acc=FAKE + 4) == -4
+    assert app(ctx=None) == -1
+    assert app(ctx=FAKE + 2) == -4
+    assert app(wsb=16) == -5
+    assert app(c=B.KVCacheStruct(FAKE, FAKE, FAKE, 2, 48)) == -2
+    assert lib.dflash_ctx_kv_append_accepted(None, ctypes.byref(cache), FAKE, FAKE, None, FAKE,
+                                             need, None) == -1
+
+    feats = (ctypes.c_void_p * 3)(FAKE, FAKE, FAKE)
+    io = B.RoundIOStruct(2, ctypes.cast(feats, ctypes.POINTER(ctypes.c_void_p)), 256, FAKE, FAKE,
+                         FAKE, FAKE, FAKE, None, None, FAKE, need)
+    g = ctypes.c_void_p(FAKE)
+    create_g = lambda stream=FAKE, io_=io: lib.dflash_round_graph_create(
+        h, ctypes.byref(cache), ctypes.byref(io_), stream, ctypes.byref(g))
+    # the NULL stream cannot be captured: refused before any HIP call
+    assert create_g(stream=None) == -1
+    assert g.value is None  # *out cleared on failure
+    io.batch = 3  # must match the cache's batch
+    assert create_g() == -2
+    io.batch = 2
+    assert lib.dflash_round_graph_create(h, ctypes.byref(cache), None, FAKE, ctypes.byref(g)) == -1
+    assert lib.dflash_round_graph_create(h, ctypes.byref(cache), ctypes.byref(io), FAKE,
+                                         None) == -1
+    assert lib.dflash_round_graph_launch(None, None) == -1
+    lib.dflash_round_graph_destroy(None)  # no-op
+    lib.dflash_destroy(h)
