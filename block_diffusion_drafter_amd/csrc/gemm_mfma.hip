@@ -5,9 +5,10 @@
 // At a few hundred rows every projection does ~400+ flops per weight byte,
 // above the chip's ridge point, so the kernel is organised around the matrix
 // cores:
-//   * a workgroup owns a BM x BN output block (256x256 with 8 waves, or
-//     128x128 with 4 for narrow projections); each wave a (BM/WGM) x (BN/WGN)
-//     sub-block of 16x16 MFMA tiles held in registers;
+//   * a workgroup owns a BM x BN output block (256x256 or 256x192 with 8
+//     waves, 128x128 or 128x96 with 4, whichever fills the 256 CUs best for
+//     the least work); each wave a (BM/WGM) x (BN/WGN) sub-block of 16x16
+//     MFMA tiles held in registers;
 //   * K advances in stages of 32 or 64. A stage of A and W is copied from
 //     the tiled layout into LDS unchanged by direct global->LDS loads
 //     (global_load_lds_dwordx4: one 1 KB fragment per wave instruction, no
@@ -59,11 +60,16 @@ __device__ __forceinline__ void wait_loads_and_barrier() {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
+// Wait for this wave's LDS reads, then meet the other waves.
+__device__ __forceinline__ void wait_lds_and_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 }  // namespace
 
 // One workgroup per CU (the LDS ring takes most of it): WGM*WGN/4 waves per
 // SIMD, which lets the compiler spend registers on two stages of operands.
-template <int BM, int BN, int WGM, int WGN, int KF, int NS, int EPI>
+template <int BM, int BN, int WGM, int WGN, int KF, int NS, int EPI, bool EARLY>
 __global__ __launch_bounds__(64 * WGM * WGN)
 __attribute__((amdgpu_waves_per_eu(WGM * WGN / 4, WGM * WGN / 4)))
 void gemm_mfma_kernel(GemmArgs p, int n_colblk, int n_rowblk) {
@@ -226,6 +232,28 @@ void gemm_mfma_kernel(GemmArgs p, int n_colblk, int n_rowblk) {
       step(s + 1, f1, f0);
     }
     if (s < nst) step(s, f0, f1);
+  } else if constexpr (EARLY) {
+    // Early issue: once every wave holds stage s in registers (second
+    // barrier), its slot takes stage s + NS before the MFMAs of stage s, so a
+    // stage's loads have NS stages of matrix work to arrive instead of NS - 1.
+    // Pays where the loads' latency, not the matrix core, sets the pace (the
+    // LM head streams each weight block once); the extra barrier costs
+    // elsewhere.
+    for (int s = 0; s < nst; ++s) {
+      const int slot = s % NS;
+      if (s > 0) {
+        // Issued: stages up to min(s - 1 + NS, nst - 1); stage s must have landed.
+        if (nst - 1 - s >= NS - 1) wait_loads_and_barrier<FPW * (NS - 1)>();
+        else wait_loads_and_barrier<0>();
+      }
+      Frags f;
+      lds_read(f, slot);
+      if (s + NS < nst) {
+        wait_lds_and_barrier();
+        issue(s + NS, slot);
+      }
+      mma(f, nullptr, 0);
+    }
   } else {
     for (int s = 0; s < nst; ++s) {
       const int slot = s % NS;
@@ -347,33 +375,62 @@ static int mfma_colblocks(int epi, int N, int BN) {
   return (N + cols - 1) / cols;
 }
 
-// Block shape: 256x256 (8 waves of 128x64) reads the fewest operand bytes per
-// flop (1/128 B) and is used when it still gives >= 192 workgroups; narrower
-// projections (QKV, O, down at a few hundred rows) take 128x128 blocks
-// (4 waves of 64x64, twice the operand traffic per flop, four times the
-// workgroups), so that most CUs have a block.
-static int mfma_block(int epi, int M, int N) {
-  const long long big = (long long)((M + 255) / 256) * mfma_colblocks(epi, N, 256);
-  return big >= 192 ? 256 : 128;
-}
+// Block shapes, largest first: 256x256 (8 waves of 128x64), 256x192 (8 waves
+// of 64x96), 128x128 (4 waves of 64x64), 128x96 (4 waves of 64x48). Bigger
+// blocks read fewer operand bytes per flop; smaller ones fill the 256 CUs at
+// fewer rows or columns. `eff` is each shape's measured throughput per busy CU
+// relative to 256x256 (gate/up and QKV at 512 rows on MI355X).
+struct MfmaShape {
+  int bm, bn;
+  double eff;
+};
+static const MfmaShape kShapes[4] = {{256, 256, 1.0}, {256, 192, 0.92}, {128, 128, 0.75},
+                                     {128, 96, 0.70}};
 
-int mfma_gemm_colblocks(int epi, int M, int N) {
-  return mfma_colblocks(epi, N, mfma_block(epi, M, N));
-}
-
-// K slices for a projection: only 128x128-block fp32-store / residual
-// projections that leave most CUs without a block (<= 128 blocks: O, down and
-// the fusion at a few hundred rows, QKV at 256) are split, into as many
-// slices as fit 256 blocks, each keeping >= 8 stages of K. The partial tiles
-// cost one extra fp32 pass (M x N x 4 B per slice, written and read once).
-int mfma_gemm_ksplit(int epi, int M, int N, int K) {
+// K slices for a 128x128 fp32-store / residual projection that leaves most
+// CUs without a block (<= 128 blocks: O, down and the fusion at a few hundred
+// rows, QKV at 256): as many slices as fit 256 blocks, each keeping >= 8
+// stages of K. The partial tiles cost one extra fp32 pass (M x N x 4 B per
+// slice, written and read once).
+static int ksplit_128(int epi, int M, int N, int K) {
   if (epi != EPI_STORE_F32 && epi != EPI_RESID) return 1;
-  if (mfma_block(epi, M, N) != 128) return 1;
   const long long blocks = (long long)((M + 127) / 128) * ((N + 127) / 128);
   if (blocks > 128) return 1;
   int ks = 1;
   while (ks < 4 && blocks * ks * 2 <= 256 && K / (64 * ks * 2) >= 8) ks *= 2;
   return ks;
+}
+
+// The shape with the least estimated time: whole rounds of 256 workgroups
+// times the work of one block (a K slice of it when 128x128 is split) over its
+// efficiency. SwiGLU needs an even number of column tiles per wave (not
+// 128x96); the LM-head argmax keeps square blocks. Ties go to the larger block.
+static int mfma_shape(int epi, int M, int N, int K) {
+  int best = 0;
+  double best_t = 1e300;
+  for (int i = 0; i < 4; ++i) {
+    const MfmaShape& sh = kShapes[i];
+    if (epi == EPI_SWIGLU && sh.bn == 96) continue;
+    if (epi == EPI_ARGMAX && sh.bm != sh.bn) continue;
+    const int ks = (sh.bm == 128 && sh.bn == 128) ? ksplit_128(epi, M, N, K) : 1;
+    const long long wgs =
+        (long long)((M + sh.bm - 1) / sh.bm) * mfma_colblocks(epi, N, sh.bn) * ks;
+    const double t = (double)((wgs + 255) / 256) * sh.bm * sh.bn / (ks * sh.eff);
+    if (t < best_t * 0.999) {
+      best_t = t;
+      best = i;
+    }
+  }
+  return best;
+}
+
+int mfma_gemm_colblocks(int epi, int M, int N, int K) {
+  return mfma_colblocks(epi, N, kShapes[mfma_shape(epi, M, N, K)].bn);
+}
+
+int mfma_gemm_ksplit(int epi, int M, int N, int K) {
+  const MfmaShape& sh = kShapes[mfma_shape(epi, M, N, K)];
+  return (sh.bm == 128 && sh.bn == 128) ? ksplit_128(epi, M, N, K) : 1;
 }
 
 // Sum of the K-slice partials in slice order, then the projection's epilogue:
@@ -407,7 +464,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
   }
 }
 
-template <int BM, int BN, int WGM, int WGN, int KF, int NS, int EPI>
+template <int BM, int BN, int WGM, int WGN, int KF, int NS, int EPI, bool EARLY = false>
 static hipError_t launch_mfma_t(const GemmArgs& a0, hipStream_t st) {
   GemmArgs a = a0;
   a.ksplit = 1;
@@ -421,8 +478,8 @@ static hipError_t launch_mfma_t(const GemmArgs& a0, hipStream_t st) {
   const int n_rowblk = (a.M + BM - 1) / BM;
   const int groups = (n_colblk + 7) / 8;
   const dim3 grid(groups * 8 * n_rowblk * a.ksplit), block(64 * WGM * WGN);
-  hipLaunchKernelGGL((gemm_mfma_kernel<BM, BN, WGM, WGN, KF, NS, EPI>), grid, block, 0, st, a,
-                     n_colblk, n_rowblk);
+  hipLaunchKernelGGL((gemm_mfma_kernel<BM, BN, WGM, WGN, KF, NS, EPI, EARLY>), grid, block, 0, st,
+                     a, n_colblk, n_rowblk);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.ksplit == 1) return e;
   float* dst = EPI == EPI_RESID ? a.resid : reinterpret_cast<float*>(a.out);
@@ -435,11 +492,20 @@ static hipError_t launch_mfma_t(const GemmArgs& a0, hipStream_t st) {
 
 template <int EPI>
 static hipError_t launch_mfma_epi(const GemmArgs& a, hipStream_t st) {
-  // 256x256: 8 waves of 128x64, stages of k=64 (64 KB) in 2 slots.
-  // 128x128: 4 waves of 64x64, stages of k=64 (32 KB) in 4 slots.
-  // (Measured best of the block / stage / ring combinations at these shapes.)
-  if (mfma_block(EPI, a.M, a.N) == 256) return launch_mfma_t<256, 256, 2, 4, 2, 2, EPI>(a, st);
-  return launch_mfma_t<128, 128, 2, 2, 2, 4, EPI>(a, st);
+  // Stages of k = 64 in 2 slots for the 8-wave shapes (64 / 56 KB each), in
+  // 4 slots for the 4-wave ones (32 / 28 KB): measured best at these shapes.
+  switch (mfma_shape(EPI, a.M, a.N, a.K)) {
+    case 0:
+      if constexpr (EPI == EPI_ARGMAX) return launch_mfma_t<256, 256, 2, 4, 2, 2, EPI, true>(a, st);
+      else return launch_mfma_t<256, 256, 2, 4, 2, 2, EPI>(a, st);
+    case 1:
+      if constexpr (EPI == EPI_ARGMAX) return hipErrorInvalidValue;
+      else return launch_mfma_t<256, 192, 4, 2, 2, 2, EPI>(a, st);
+    case 2: return launch_mfma_t<128, 128, 2, 2, 2, 4, EPI>(a, st);
+    default:
+      if constexpr (EPI == EPI_ARGMAX || EPI == EPI_SWIGLU) return hipErrorInvalidValue;
+      else return launch_mfma_t<128, 96, 2, 2, 2, 4, EPI>(a, st);
+  }
 }
 
 hipError_t launch_gemm_mfma(int epi, const GemmArgs& a, hipStream_t st) {

@@ -78,7 +78,7 @@ inline bool gemm_uses_mfma(int dtype, int M, int K, bool a_tiled) {
   return dtype == DFLASH_BF16 && a_tiled && M >= kMfmaMinRows && K % 64 == 0;
 }
 hipError_t launch_gemm_mfma(int epi, const GemmArgs& a, hipStream_t st);
-int mfma_gemm_colblocks(int epi, int M, int N);
+int mfma_gemm_colblocks(int epi, int M, int N, int K);
 // K slices the MFMA kernel splits a projection into (1 = no split); the
 // partial buffer it then needs is ksplit * M * N floats.
 int mfma_gemm_ksplit(int epi, int M, int N, int K);
