@@ -112,30 +112,19 @@ struct Plan {
   size_t u, ua, upart, proj_end;  // ua: tiled copy of the fused features (MFMA path)
   size_t kv, ca, kvpart, app_end;  // ca: tiled copy of the context rows (MFMA path)
   int64_t part_elems, upart_elems, kvpart_elems;  // split-K partials (floats)
-  int chunk, max_chunks, n_vtiles;
+  int attn_wg, n_vtiles;  // attention workgroups per KV head; LM-head keys per row
   size_t total;
 };
 
-// Keys per attention work item (one workgroup of G waves per sequence, KV
-// head and chunk). The device holds the context lengths, so the split is
-// sized from the capacity. Few (sequence, KV head) pairs: each pair is cut
-// into about 512 / pairs equal chunks, so the items fill ~2 workgroups per CU
-// in one round (a last round with a few items left most of the chip idle:
-// 1056 items over 512 slots ran at 2/3 of the rate of 512 items). Many pairs
-// (ragged batches): 1024-key chunks, several rounds of items. The partials
-// (16 rows x head_dim fp32 per query head) stay a few percent of the K/V
-// stream for chunks of >= 512 keys.
-int choose_chunk(int batch, int hkv, int cap) {
-  const long long pairs = (long long)batch * hkv;
-  long long c;
-  if (pairs >= 128) {
-    c = 1024;
-  } else {
-    const long long per = (512 + pairs - 1) / pairs;
-    c = 32 * (((cap + per - 1) / per + 31) / 32);
-  }
-  return (int)std::max(64LL, std::min(4096LL, c));
-}
+// Attention split: each KV head's keys (all sequences, end to end) are cut
+// into equal ranges over up to 512 / Hkv workgroups, one round over the chip
+// at 2 workgroups of a KV group per CU, each range at least 2 blocks of 32
+// keys; the device sizes the split from ctx_len, the host only bounds it.
+// (Per-sequence chunks left a ragged batch with a part-filled last round:
+// batch 32 at 512-8192 keys ran 1.6 rounds of 1024-key chunks.)
+constexpr int kAttnSlots = 512;
+constexpr int kAttnMinBlocks = 2;
+int attn_wg_per_head(int hkv) { return std::max(1, kAttnSlots / std::max(1, hkv)); }
 
 // Floats of split-K partials a tiled-A projection needs on the MFMA path (0 if none).
 int64_t splitk_elems(int dtype, int epi, int M, int N, int K) {
@@ -160,10 +149,11 @@ Plan make_plan(const dflash_config& c, int batch, int cap, int max_tokens) {
   p.h = take(tiled_bytes(dt, (int64_t)M, (int)d));
   p.qkv = take(M * (Hq + 2 * Hkv) * hd * 4);
   p.q = take((size_t)batch * Hq * 16 * hd * es);
-  p.chunk = choose_chunk(batch, (int)Hkv, cap);
-  p.max_chunks = (cap + p.chunk - 1) / p.chunk;
-  p.po = take((size_t)batch * Hkv * p.max_chunks * G * hd * 16 * 4);
-  p.pml = take((size_t)batch * Hkv * p.max_chunks * G * 16 * 2 * 4);
+  p.attn_wg = attn_wg_per_head((int)Hkv);
+  // one partial entry per (KV head, workgroup or sequence boundary)
+  const size_t entries = Hkv * (size_t)(p.attn_wg + batch);
+  p.po = take(entries * G * hd * 16 * 4);
+  p.pml = take(entries * G * 16 * 2 * 4);
   p.attn = take(tiled_bytes(dt, (int64_t)M, (int)(Hq * hd)));
   p.act = take(tiled_bytes(dt, (int64_t)M, (int)I));
   const size_t R = (size_t)batch * (B - 1);
@@ -633,8 +623,8 @@ int32_t dflash_draft_forward(const dflash_handle* h, const dflash_kv_cache* cach
     at.head_dim = hd;
     at.block = B;
     at.cap = cap;
-    at.chunk = P.chunk;
-    at.max_chunks = P.max_chunks;
+    at.wg_per_head = P.attn_wg;
+    at.min_blocks = kAttnMinBlocks;
     at.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)hd));
     at.part_o = reinterpret_cast<float*>(w + P.po);
     at.part_ml = reinterpret_cast<float*>(w + P.pml);

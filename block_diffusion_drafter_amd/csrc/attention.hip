@@ -6,8 +6,11 @@
 // [ctx_len, ctx_len + B). With 16 queries per head over thousands of keys the
 // work is a stream of the K/V cache, split over key chunks:
 //
-//   attn_partial: one workgroup per (sequence, KV head, key chunk), one wave
-//     per query head of the GQA group. In bf16 the group's waves share each
+//   attn_partial: per KV head, the keys of all sequences are laid end to end
+//     in 32-key blocks (sequence order) and split into equal ranges, one per
+//     workgroup, so ragged batches keep every workgroup equally busy; a
+//     workgroup runs each sequence segment of its range in turn, one wave per
+//     query head of the GQA group. In bf16 the group's waves share each
 //     32-key K/V block through an LDS ring filled by direct global->LDS loads
 //     (every position crosses the memory system once, several blocks in
 //     flight); the fp32 path loads per wave into registers. Scores are computed transposed, S^T = K Q^T (keys as
@@ -18,10 +21,11 @@
 //     operand needs (the key order inside a 32-key block is permuted to make
 //     that so). V is stored channel-major inside 32-position blocks, so each
 //     lane's V fragment is one 16-byte load. The next block's K/V is loaded
-//     while the current one is multiplied. A sequence that fits in one chunk
-//     is normalised and written directly; otherwise the chunk's (max, sum,
-//     unnormalised O) go to a partial buffer.
-//   attn_combine: merges the chunks of the sequences that needed several.
+//     while the current one is multiplied. A sequence that lies within one
+//     workgroup's range is normalised and written directly; otherwise each
+//     segment's (max, sum, unnormalised O) goes to a partial buffer.
+//   attn_combine: merges the segments of the sequences that span several
+//     workgroups.
 #include "common.h"
 #include "internal.h"
 
@@ -64,6 +68,54 @@ __device__ __forceinline__ int seq_keys(const AttnArgs& p, int s) {
   int cl = p.ctx_len[s];
   cl = cl < 0 ? 0 : cl;
   return min(cl + p.block, p.cap);
+}
+
+// First 32-key block of every sequence when one KV head's keys are laid end
+// to end: pre[s] = sum over t < s of ceil(keys(t) / 32), pre[batch] = the
+// total. Built in LDS by wave 0 (one load per lane and sequence, a wave scan
+// per 64 sequences); every thread returns after the barrier that publishes it.
+__device__ __forceinline__ void seq_block_prefix(const AttnArgs& p, int* pre) {
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    int carry = 0;
+    for (int base = 0; base < p.batch; base += 64) {
+      const int s = base + lane;
+      int v = s < p.batch ? (seq_keys(p, s) + 31) >> 5 : 0;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int u = __shfl_up(v, o);
+        if (lane >= o) v += u;
+      }
+      if (lane == 0) pre[base] = carry;
+      if (s < p.batch) pre[s + 1] = carry + v;
+      carry += __shfl(v, 63);
+    }
+    if (p.batch == 0 && lane == 0) pre[0] = 0;
+  }
+  __syncthreads();
+}
+
+// The equal split of one KV head's keys: tb 32-key blocks in total, of which
+// workgroup w < nw takes [begin(w), begin(w + 1)). nw is the number of
+// workgroups per head, capped so that each gets >= min_blocks blocks; both
+// attention kernels derive the same split from ctx_len.
+struct KeySplit {
+  int tb, nw;
+  __device__ int begin(int w) const { return (int)(((long long)w * tb) / nw); }
+  // The workgroup whose range holds block b.
+  __device__ int owner(int b) const { return (int)(((long long)(b + 1) * nw - 1) / tb); }
+};
+
+__device__ __forceinline__ KeySplit key_split(const AttnArgs& p, const int* pre) {
+  const int tb = pre[p.batch];
+  const int want = (tb + p.min_blocks - 1) / p.min_blocks;
+  return KeySplit{tb, max(1, min(p.wg_per_head, want))};
+}
+
+// Partial entry of sequence s's segment in workgroup w (KV head g): w + s is
+// unique over the (s, w) pairs that overlap, and below wg_per_head + batch.
+__device__ __forceinline__ size_t part_entry(const AttnArgs& p, int g, int w, int s) {
+  return (size_t)g * (p.wg_per_head + p.batch) + w + s;
 }
 
 template <typename T, int HD>
@@ -185,11 +237,13 @@ __device__ __forceinline__ void load_q(u32x4* qf, const AttnArgs& p, int s, int 
   for (int f = 0; f < KB::FR; ++f) qf[f] = ld16(qp + f * 4 * KB::EPF);
 }
 
-// End of a chunk: a sequence that fit in one chunk is normalised and written
-// to the tiled output; otherwise (max, sum, unnormalised O) go to the partials.
+// End of a segment: a sequence that lies in one workgroup's range is
+// normalised and written to the tiled output; otherwise (max, sum,
+// unnormalised O) go to the segment's partial entry.
 template <typename T, int HD>
 __device__ __forceinline__ void attn_finish(AttnState<T, HD>& S, const AttnArgs& p, int s, int g,
-                                            int c, int j, int G, bool single, int r, int grp) {
+                                            size_t entry, int j, int G, bool single, int r,
+                                            int grp) {
   constexpr int NDT = HD / 16;
   const int h = g * G + j;
   S.l_run += __shfl_xor(S.l_run, 16);
@@ -209,7 +263,7 @@ __device__ __forceinline__ void attn_finish(AttnState<T, HD>& S, const AttnArgs&
     }
     return;
   }
-  const size_t item = ((size_t)(s * p.n_kv_heads + g) * p.max_chunks + c) * G + j;
+  const size_t item = entry * G + j;
   if (grp == 0) {
     p.part_ml[(item * 16 + r) * 2 + 0] = S.m_run;
     p.part_ml[(item * 16 + r) * 2 + 1] = S.l_run;
@@ -221,6 +275,28 @@ __device__ __forceinline__ void attn_finish(AttnState<T, HD>& S, const AttnArgs&
     for (int i = 0; i < 4; ++i) po[(16 * dt + 4 * grp + i) * 16 + r] = S.o[dt][i];
 }
 
+// seg(s, k_lo, k_hi, single) for every sequence segment of workgroup w's
+// range, in sequence order: keys [k_lo, k_hi) of sequence s; single when the
+// segment is the whole sequence. The first sequence is found by binary search
+// in the block prefix.
+template <typename F>
+__device__ __forceinline__ void for_each_segment(const AttnArgs& p, const int* pre,
+                                                 const KeySplit& ks, int w, F&& seg) {
+  const int b0 = ks.begin(w), b1 = ks.begin(w + 1);
+  int lo = 0, hi = p.batch - 1;  // last s with pre[s] <= b0
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (pre[mid] <= b0) lo = mid;
+    else hi = mid - 1;
+  }
+  for (int s = lo; s < p.batch && pre[s] < b1; ++s) {
+    const int bs = pre[s], be = pre[s + 1];
+    const int n_keys = seq_keys(p, s);
+    const int a = max(b0, bs), b = min(b1, be);
+    if (a < b) seg(s, 32 * (a - bs), min(n_keys, 32 * (b - bs)), a == bs && b == be);
+  }
+}
+
 // fp32 path: each wave loads its K/V fragments straight into registers.
 template <typename T, int HD>
 __global__ __launch_bounds__(512) void attn_partial_kernel(AttnArgs p) {
@@ -228,16 +304,14 @@ __global__ __launch_bounds__(512) void attn_partial_kernel(AttnArgs p) {
   constexpr int FR = KB::FR, NDT = KB::NDT;
   const int lane = threadIdx.x & 63, j = threadIdx.x >> 6;
   const int r = lane & 15, grp = lane >> 4;
-  const int c = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
+  const int w = blockIdx.x, g = blockIdx.y;
   const int G = p.n_heads / p.n_kv_heads;
   const int h = g * G + j;
-
-  const int n_keys = seq_keys(p, s);
-  const int k_lo = c * p.chunk;
-  if (k_lo >= n_keys) return;
-  const int k_hi = min(n_keys, k_lo + p.chunk);
-  const bool single = n_keys <= p.chunk;
-
+  extern __shared__ int pre[];
+  seq_block_prefix(p, pre);
+  const KeySplit ks = key_split(p, pre);
+  if (w >= ks.nw) return;
+  for_each_segment(p, pre, ks, w, [&](int s, int k_lo, int k_hi, bool single) {
   const size_t kvoff = (size_t)(s * p.n_kv_heads + g) * p.cap * HD;
   const T* K = reinterpret_cast<const T*>(p.k) + kvoff;
   const T* V = reinterpret_cast<const T*>(p.v) + kvoff;
@@ -269,7 +343,8 @@ __global__ __launch_bounds__(512) void attn_partial_kernel(AttnArgs p) {
       attn_update<T, HD>(S, b0, qf, kb, k_hi, p.scale_log2, grp);
     }
   }
-  attn_finish<T, HD>(S, p, s, g, c, j, G, single, r, grp);
+  attn_finish<T, HD>(S, p, s, g, part_entry(p, g, w, s), j, G, single, r, grp);
+  });
 }
 
 typedef __attribute__((address_space(3))) void* attn_lds_ptr;
@@ -303,14 +378,18 @@ __global__ __launch_bounds__(64 * G) void attn_partial_lds_kernel(AttnArgs p) {
   const int lane = threadIdx.x & 63;
   const int j = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 15, grp = lane >> 4;
-  const int c = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
+  const int w = blockIdx.x, g = blockIdx.y;
   const int h = g * G + j;
-
-  const int n_keys = seq_keys(p, s);
-  const int k_lo = c * p.chunk;
-  if (k_lo >= n_keys) return;
-  const int k_hi = min(n_keys, k_lo + p.chunk);
-  const bool single = n_keys <= p.chunk;
+  extern __shared__ int pre[];
+  seq_block_prefix(p, pre);
+  const KeySplit ks = key_split(p, pre);
+  if (w >= ks.nw) return;
+  bool first = true;
+  for_each_segment(p, pre, ks, w, [&](int s, int k_lo, int k_hi, bool single) {
+  // The previous segment's last ring reads are done in every wave before its
+  // slots are refilled.
+  if (!first) __syncthreads();
+  first = false;
   const int nblk = (k_hi - k_lo + 31) / 32;
 
   const size_t kvoff = (size_t)(s * p.n_kv_heads + g) * p.cap * HD;
@@ -380,15 +459,16 @@ __global__ __launch_bounds__(64 * G) void attn_partial_lds_kernel(AttnArgs p) {
       if (n + NSB < nblk) issue(n + NSB, slot);
     }
   }
-  attn_finish<T, HD>(S, p, s, g, c, j, G, single, r, grp);
+  attn_finish<T, HD>(S, p, s, g, part_entry(p, g, w, s), j, G, single, r, grp);
+  });
 }
 
-// Merge of the chunk partials of one (query head, sequence, 16-channel slice).
-// Thread (q, cg) owns query row q and the chunks c = cg, cg + 16, ...: it
-// reduces the row's running max and sum over its chunks, the 16 threads of a
-// row combine them through LDS, then each thread accumulates its chunks'
-// weighted partial outputs for the slice's 16 channels and LDS sums the 16
-// chunk groups. Every thread's loads are independent of each other.
+// Merge of the segment partials of one (query head, sequence, 16-channel
+// slice). Thread (q, cg) owns query row q and the segments c = cg, cg + 16,
+// ...: it reduces the row's running max and sum over its segments, the 16
+// threads of a row combine them through LDS, then each thread accumulates its
+// segments' weighted partial outputs for the slice's 16 channels and LDS sums
+// the 16 segment groups. Every thread's loads are independent of each other.
 template <typename T, int HD>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs p) {
   __shared__ float red_m[16][17], red_l[16][17];
@@ -396,11 +476,16 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs p) {
   const int h = blockIdx.x, s = blockIdx.y, slice = blockIdx.z;
   const int G = p.n_heads / p.n_kv_heads;
   const int g = h / G, j = h % G;
-  const int n_keys = seq_keys(p, s);
-  const int nch = (n_keys + p.chunk - 1) / p.chunk;
-  if (nch <= 1) return;  // written by the partial kernel
+  extern __shared__ int pre[];
+  seq_block_prefix(p, pre);
+  const KeySplit ks = key_split(p, pre);
+  const int w0 = ks.owner(pre[s]), w1 = ks.owner(pre[s + 1] - 1);
+  if (w0 == w1) return;  // one segment: written by the partial kernel
+  // Segments c = 0 .. nch-1 come from workgroups w0 + c (every one in between
+  // has a non-empty range since nw <= tb), at entries w0 + c + s.
+  const int nch = w1 - w0 + 1;
   const int t = threadIdx.x, q = t & 15, cg = t >> 4;
-  const size_t item0 = (size_t)(s * p.n_kv_heads + g) * p.max_chunks * G + j;
+  const size_t item0 = part_entry(p, g, w0, s) * G + j;
   float m = -INFINITY;
   for (int c = cg; c < nch; c += 16) m = fmaxf(m, p.part_ml[((item0 + (size_t)c * G) * 16 + q) * 2]);
   red_m[q][cg] = m;
@@ -445,24 +530,25 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs p) {
 template <typename T, int HD>
 static hipError_t launch_hd(const AttnArgs& a, hipStream_t st) {
   const int G = a.n_heads / a.n_kv_heads;
-  dim3 grid(a.max_chunks, a.n_kv_heads, a.batch);
+  dim3 grid(a.wg_per_head, a.n_kv_heads, 1);
+  const size_t pre_bytes = (size_t)(a.batch + 1) * sizeof(int);  // block prefix in LDS
   if constexpr (sizeof(T) == 2) {
     switch (G) {
-      case 1: hipLaunchKernelGGL((attn_partial_lds_kernel<HD, 1>), grid, dim3(64), 0, st, a); break;
-      case 2: hipLaunchKernelGGL((attn_partial_lds_kernel<HD, 2>), grid, dim3(128), 0, st, a); break;
-      case 4: hipLaunchKernelGGL((attn_partial_lds_kernel<HD, 4>), grid, dim3(256), 0, st, a); break;
-      case 8: hipLaunchKernelGGL((attn_partial_lds_kernel<HD, 8>), grid, dim3(512), 0, st, a); break;
+      case 1: hipLaunchKernelGGL((attn_partial_lds_kernel<HD, 1>), grid, dim3(64), pre_bytes, st, a); break;
+      case 2: hipLaunchKernelGGL((attn_partial_lds_kernel<HD, 2>), grid, dim3(128), pre_bytes, st, a); break;
+      case 4: hipLaunchKernelGGL((attn_partial_lds_kernel<HD, 4>), grid, dim3(256), pre_bytes, st, a); break;
+      case 8: hipLaunchKernelGGL((attn_partial_lds_kernel<HD, 8>), grid, dim3(512), pre_bytes, st, a); break;
       default: return hipErrorInvalidValue;
     }
   } else {
-    hipLaunchKernelGGL((attn_partial_kernel<T, HD>), grid, dim3(64 * G), 0, st, a);
+    hipLaunchKernelGGL((attn_partial_kernel<T, HD>), grid, dim3(64 * G), pre_bytes, st, a);
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.max_chunks <= 1) return e;
+  if (e != hipSuccess || a.wg_per_head <= 1) return e;
   prof_end(st);
   prof_begin(DFLASH_K_ATTN_COMBINE, 0.0, 0.0, st);
-  hipLaunchKernelGGL((attn_combine_kernel<T, HD>), dim3(a.n_heads, a.batch, HD / 16), dim3(256), 0,
-                     st, a);
+  hipLaunchKernelGGL((attn_combine_kernel<T, HD>), dim3(a.n_heads, a.batch, HD / 16), dim3(256),
+                     pre_bytes, st, a);
   return hipGetLastError();
 }
 

@@ -113,14 +113,14 @@ struct AttnArgs {
   const void* v;         // this layer's V cache base: [cache_batch][Hkv][cap/32][hd][32]
   const int32_t* ctx_len;
   int batch, n_heads, n_kv_heads, head_dim, block, cap;
-  int chunk;             // keys per work item (multiple of 32)
-  int max_chunks;        // ceil(cap / chunk)
+  int wg_per_head;       // workgroups per KV head that split its keys (grid x)
+  int min_blocks;        // fewest 32-key blocks a workgroup is given
   float scale_log2;      // log2(e) / sqrt(head_dim)
-  float* part_o;         // [batch][Hkv][max_chunks][G][hd][16]
-  float* part_ml;        // [batch][Hkv][max_chunks][G][16][2]  (running max in log2 units, sum)
+  float* part_o;         // [Hkv][wg_per_head + batch][G][hd][16]
+  float* part_ml;        // [Hkv][wg_per_head + batch][G][16][2]  (running max in log2 units, sum)
   void* out;             // tiled [batch*B, n_heads*hd] model dtype (out_nck chunks per row);
-  int out_nck;           // written by the partial kernel when a sequence fits in one
-                         // chunk, else by the combine
+  int out_nck;           // written by the partial kernel when a sequence lies in one
+                         // workgroup's range, else by the combine
 };
 
 hipError_t launch_attention(int dtype, const AttnArgs& a, hipStream_t st);
