@@ -30,6 +30,9 @@ Readings taken where the pages are silent (each is repeated at its use):
     at ctx_len + i; context rows keep their absolute positions.
   * attention scale 1/sqrt(head_dim), no mask; query head j reads KV head
     j // (n_heads / n_kv_heads); no biases anywhere.
+  * sliding-window layers (listed in the config): query i of the block, at
+    position ctx_len + i, sees the keys at positions p with
+    ctx_len + i - p < window, and no causal mask.
   * context rows are not normed again per layer (they are already RMS-normed
     by the fusion step).
   * argmax ties break to the lowest token id.
@@ -192,7 +195,8 @@ def embed_block(anchor: int, weights, cfg) -> np.ndarray:
     return _f64(np.asarray(weights["embed"])[ids])
 
 
-def kv_injected_attention(q, k_blk, v_blk, k_ctx, v_ctx, group: int) -> np.ndarray:
+def kv_injected_attention(q, k_blk, v_blk, k_ctx, v_ctx, group: int,
+                          window: Optional[int] = None) -> np.ndarray:
     """Non-causal attention of the block queries over [context ; block] keys.
 
     q [B, Hq, hd]; k_blk, v_blk [B, Hkv, hd]; k_ctx, v_ctx [Hkv, c, hd].
@@ -200,20 +204,38 @@ def kv_injected_attention(q, k_blk, v_blk, k_ctx, v_ctx, group: int) -> np.ndarr
     concatenated with the block's own along the sequence; queries come from the
     block only; [W "Paper vs code"]: full-attention layers are non-causal.
     Reading: scale 1/sqrt(hd), no mask, query head j uses KV head j // group.
+
+    window: a sliding-window layer ([W "Paper vs code", attention-pattern
+    bullet: the code supports per-layer sliding-window attention, which the
+    paper does not describe]). Reading: with context positions 0..c-1 and
+    block position i at c + i, query i sees key position p iff
+    (c + i) - p < window; no causal part (the drafter is non-causal).
     """
     B, hq, hd = q.shape
+    c = k_ctx.shape[1]
+    qpos = np.arange(c, c + B)[:, None]
+    kpos = np.arange(c + B)[None, :]
+    visible = np.ones((B, c + B), dtype=bool) if window is None else (qpos - kpos < window)
     out = np.empty((B, hq, hd), dtype=F64)
     for j in range(hq):
         g = j // group
         keys = np.concatenate([_f64(k_ctx[g]), _f64(k_blk[:, g, :])], axis=0)
         vals = np.concatenate([_f64(v_ctx[g]), _f64(v_blk[:, g, :])], axis=0)
-        p = softmax_rows(_f64(q[:, j, :]) @ keys.T / np.sqrt(hd))
+        scores = np.where(visible, _f64(q[:, j, :]) @ keys.T / np.sqrt(hd), -np.inf)
+        p = softmax_rows(scores)
         out[:, j, :] = p @ vals
     return out
 
 
-def draft_layer(x, cache_k, cache_v, start_pos: int, lw, cfg, trace: Optional[dict] = None
-                ) -> np.ndarray:
+def layer_window(cfg, l: int) -> Optional[int]:
+    """The attention window of draft layer l: the config's sliding_window for
+    the layers listed in sliding_layers, None (full attention) otherwise."""
+    w = getattr(cfg, "sliding_window", 0) or 0
+    return int(w) if w > 0 and l in tuple(getattr(cfg, "sliding_layers", ())) else None
+
+
+def draft_layer(x, cache_k, cache_v, start_pos: int, lw, cfg, trace: Optional[dict] = None,
+                window: Optional[int] = None) -> np.ndarray:
     """One draft layer over one sequence's block x [B, d] (fp64 residual).
 
     [W draft-layer pseudocode]: queries from the block, keys/values from
@@ -233,7 +255,7 @@ def draft_layer(x, cache_k, cache_v, start_pos: int, lw, cfg, trace: Optional[di
     k = rms_norm(k, lw["k_norm"], eps)
     q = np.stack([rope(q[:, j, :], pos, cfg.rope_theta) for j in range(hq)], axis=1)
     k = np.stack([rope(k[:, g, :], pos, cfg.rope_theta) for g in range(hkv)], axis=1)
-    o = kv_injected_attention(q, k, v, cache_k, cache_v, hq // hkv)
+    o = kv_injected_attention(q, k, v, cache_k, cache_v, hq // hkv, window)
     x = x + o.reshape(B, hq * hd) @ _f64(lw["wo"]).T
     h2 = rms_norm(x, lw["post_norm"], eps)
     act = silu(h2 @ _f64(lw["w_gate"]).T) * (h2 @ _f64(lw["w_up"]).T)
@@ -288,7 +310,7 @@ def draft_forward(cfg, weights: Dict[str, np.ndarray], caches: Sequence[SeqCache
         for s in range(b):
             sp = caches[s].ctx_len if start_pos is None else int(start_pos[s])
             xs[s] = draft_layer(xs[s], caches[s].k[l], caches[s].v[l], sp, lw, cfg,
-                                trace=trace if s == 0 else None)
+                                trace=trace if s == 0 else None, window=layer_window(cfg, l))
             hidden[s, l] = xs[s]
     y = rms_norm(xs[:, 1:, :], weights["final_norm"], cfg.rms_eps)
     logits, drafts, margins = lm_head_argmax(y, weights["lm_head"])

@@ -33,6 +33,8 @@ class DrafterConfig:
     rope_theta: Optional[float]  # None: no rotary embedding (used by invariance checks)
     dtype: str                   # "fp32" or "bf16": storage/compute type of the GPU path
     tied_embeddings: bool        # embedding table and LM head are the same matrix
+    sliding_window: int = 0      # > 0: attention window of the layers in sliding_layers
+    sliding_layers: Tuple[int, ...] = ()
 
     @property
     def mask_token_id(self) -> int:

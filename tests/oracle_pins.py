@@ -158,6 +158,88 @@ def check_attention_brute(O):
             _close(got[i, j], o, what=f"attention brute ({i},{j})")
 
 
+def _window_mask(B, c, window):
+    qpos = np.arange(c, c + B)[:, None]
+    kpos = np.arange(c + B)[None, :]
+    return torch.from_numpy(qpos - kpos < window)
+
+
+def check_window_vs_sdpa_mask(O):
+    # Sliding-window layers against torch SDPA with an explicit boolean mask:
+    # query i (position c + i) sees key position p iff c + i - p < window.
+    rng = np.random.default_rng(14)
+    for (B, hq, hkv, hd, c, win) in [(4, 4, 2, 8, 20, 6), (4, 4, 2, 8, 20, 3), (16, 8, 2, 16, 40, 17),
+                                     (5, 2, 1, 4, 9, 1), (4, 4, 2, 8, 7, 11), (3, 6, 6, 4, 0, 2)]:
+        q = rng.normal(size=(B, hq, hd))
+        kb, vb = rng.normal(size=(B, hkv, hd)), rng.normal(size=(B, hkv, hd))
+        kc, vc = rng.normal(size=(hkv, c, hd)), rng.normal(size=(hkv, c, hd))
+        got = O.kv_injected_attention(q, kb, vb, kc, vc, hq // hkv, win)
+        keys = torch.cat([IT.t(kc), IT.t(kb).transpose(0, 1)], dim=1)[None]
+        vals = torch.cat([IT.t(vc), IT.t(vb).transpose(0, 1)], dim=1)[None]
+        ref = F.scaled_dot_product_attention(IT.t(q).transpose(0, 1)[None], keys, vals,
+                                             attn_mask=_window_mask(B, c, win),
+                                             enable_gqa=True)[0].transpose(0, 1).numpy()
+        _close(got, ref, what=f"window attention vs sdpa {B, hq, hkv, hd, c, win}")
+
+
+def check_window_hides_old_keys(O):
+    # Context keys at positions p <= c - window are invisible to every query;
+    # position c - window + 1 is visible to query 0 only.
+    rng = np.random.default_rng(15)
+    B, hq, hkv, hd, c, win = 4, 4, 2, 8, 12, 5
+    q = rng.normal(size=(B, hq, hd))
+    kb, vb = rng.normal(size=(B, hkv, hd)), rng.normal(size=(B, hkv, hd))
+    kc, vc = rng.normal(size=(hkv, c, hd)), rng.normal(size=(hkv, c, hd))
+    base = O.kv_injected_attention(q, kb, vb, kc, vc, hq // hkv, win)
+    kc2, vc2 = kc.copy(), vc.copy()
+    kc2[:, : c - win + 1] += 3.0
+    vc2[:, : c - win + 1] -= 2.0
+    _close(O.kv_injected_attention(q, kb, vb, kc2, vc2, hq // hkv, win), base,
+           what="keys outside every query's window")
+    kc3, vc3 = kc.copy(), vc.copy()
+    vc3[:, c - win + 1] += 5.0
+    moved = O.kv_injected_attention(q, kb, vb, kc3, vc3, hq // hkv, win)
+    assert np.max(np.abs(moved[0] - base[0])) > 1e-6, "query 0 must see position c - window + 1"
+    _close(moved[1:], base[1:], what="later queries must not see position c - window + 1")
+
+
+def check_window_layers_in_forward(O):
+    # Only the layers listed as sliding take the window: changing layer 1's
+    # oldest context values changes the output when layer 1 is full-attention
+    # and leaves it unchanged when layer 1 slides (window 3).
+    cfg = micro_cfg(sliding_window=3, sliding_layers=(1,))
+    w = micro_weights(cfg, seed=16)
+    cache, _, _ = micro_cache(O, cfg, w, 10, seed=17)
+    v1 = [x.copy() for x in cache.v]
+    v1[1][:, :4] += 2.0
+    moved = O.SeqCache(cache.k, v1)
+    anchor = [3]
+    full = cfg.with_(sliding_window=0, sliding_layers=())
+    a = O.draft_forward(cfg, w, [cache], anchor).hidden
+    b = O.draft_forward(cfg, w, [moved], anchor).hidden
+    _close(b, a, what="sliding layer 1 ignores context outside its window")
+    a = O.draft_forward(full, w, [cache], anchor).hidden
+    b = O.draft_forward(full, w, [moved], anchor).hidden
+    assert np.max(np.abs(a - b)) > 1e-6, "full-attention layer 1 must see every context row"
+    # layer 0 is full attention in the sliding config too
+    k0 = [x.copy() for x in cache.v]
+    k0[0][:, :4] += 2.0
+    a = O.draft_forward(cfg, w, [cache], anchor).hidden
+    b = O.draft_forward(cfg, w, [O.SeqCache(cache.k, k0)], anchor).hidden
+    assert np.max(np.abs(a - b)) > 1e-6, "layer 0 (not listed) must see every context row"
+
+
+def check_wide_window_is_full_attention(O):
+    rng = np.random.default_rng(18)
+    B, hq, hkv, hd, c = 4, 4, 2, 8, 9
+    q = rng.normal(size=(B, hq, hd))
+    kb, vb = rng.normal(size=(B, hkv, hd)), rng.normal(size=(B, hkv, hd))
+    kc, vc = rng.normal(size=(hkv, c, hd)), rng.normal(size=(hkv, c, hd))
+    full = O.kv_injected_attention(q, kb, vb, kc, vc, hq // hkv)
+    _close(O.kv_injected_attention(q, kb, vb, kc, vc, hq // hkv, c + B), full,
+           what="window c + B = full attention")
+
+
 def check_block_of_one_is_decode(O):
     """B = 1 (no mask tokens): the anchor's attention is the last row of a
     causal SDPA over [context ; anchor]; acceptance has nothing to accept."""

@@ -55,52 +55,53 @@ def _silu_sign(x):
     return x / (1.0 + np.exp(x))
 
 
-def _attn_no_scale(q, kb, vb, kc, vc, group):
+def _attn_no_scale(q, kb, vb, kc, vc, group, window=None):
     hd = q.shape[-1]
-    return _orig["kv_injected_attention"](np.asarray(q) * np.sqrt(hd), kb, vb, kc, vc, group)
+    return _orig["kv_injected_attention"](np.asarray(q) * np.sqrt(hd), kb, vb, kc, vc, group,
+                                          window)
 
 
-def _attn_wrong_group(q, kb, vb, kc, vc, group):
+def _attn_wrong_group(q, kb, vb, kc, vc, group, window=None):
     B, hq, hd = q.shape
     hkv = kb.shape[1]
     out = np.empty((B, hq, hd))
     for j in range(hq):
         one = _orig["kv_injected_attention"](q[:, j:j + 1], kb[:, [j % hkv]], vb[:, [j % hkv]],
-                                             kc[[j % hkv]], vc[[j % hkv]], 1)
+                                             kc[[j % hkv]], vc[[j % hkv]], 1, window)
         out[:, j] = one[:, 0]
     return out
 
 
-def _attn_causal_block(q, kb, vb, kc, vc, group):
+def _attn_causal_block(q, kb, vb, kc, vc, group, window=None):
     B = q.shape[0]
     out = np.empty(q.shape)
     for i in range(B):
         out[i] = _orig["kv_injected_attention"](q[i:i + 1], kb[:i + 1], vb[:i + 1], kc, vc,
-                                                group)[0]
+                                                group, window)[0]
     return out
 
 
-def _attn_block_keys_dropped(q, kb, vb, kc, vc, group):
+def _attn_block_keys_dropped(q, kb, vb, kc, vc, group, window=None):
     if kc.shape[1] == 0:
-        return _orig["kv_injected_attention"](q, kb, vb, kc, vc, group)
-    return _orig["kv_injected_attention"](q, kb[:0], vb[:0], kc, vc, group)
+        return _orig["kv_injected_attention"](q, kb, vb, kc, vc, group, window)
+    return _orig["kv_injected_attention"](q, kb[:0], vb[:0], kc, vc, group, window)
 
 
-def _layer_no_attn_residual(x, ck, cv, sp, lw, cfg, trace=None):
+def _layer_no_attn_residual(x, ck, cv, sp, lw, cfg, trace=None, window=None):
     lw2 = dict(lw)
-    return _orig["draft_layer"](x, ck, cv, sp, lw2, cfg, trace) - np.asarray(x) * 0.5
+    return _orig["draft_layer"](x, ck, cv, sp, lw2, cfg, trace, window) - np.asarray(x) * 0.5
 
 
-def _layer_k_from_q_weights(x, ck, cv, sp, lw, cfg, trace=None):
+def _layer_k_from_q_weights(x, ck, cv, sp, lw, cfg, trace=None, window=None):
     lw2 = dict(lw)
     lw2["k_norm"] = lw["q_norm"]
-    return _orig["draft_layer"](x, ck, cv, sp, lw2, cfg, trace)
+    return _orig["draft_layer"](x, ck, cv, sp, lw2, cfg, trace, window)
 
 
-def _layer_mlp_swapped(x, ck, cv, sp, lw, cfg, trace=None):
+def _layer_mlp_swapped(x, ck, cv, sp, lw, cfg, trace=None, window=None):
     lw2 = dict(lw)
     lw2["w_gate"], lw2["w_up"] = lw["w_up"], lw["w_gate"]
-    return _orig["draft_layer"](x, ck, cv, sp, lw2, cfg, trace)
+    return _orig["draft_layer"](x, ck, cv, sp, lw2, cfg, trace, window)
 
 
 def _ctx_concat_reversed(feats, w_fc, g_fc, eps):
@@ -154,7 +155,42 @@ def _tau_missing_one(a, m):
     return _orig["tau_geometric"](a, m) - 1.0
 
 
+def _window_off_by_one(q, kb, vb, kc, vc, group, window=None):
+    return _orig["kv_injected_attention"](q, kb, vb, kc, vc, group,
+                                          None if window is None else window + 1)
+
+
+def _window_reversed(q, kb, vb, kc, vc, group, window=None):
+    # the window measured from the keys' side: hides the block's later keys
+    if window is None:
+        return _orig["kv_injected_attention"](q, kb, vb, kc, vc, group)
+    B, hq, hd = q.shape
+    c = kc.shape[1]
+    out = np.empty((B, hq, hd))
+    for i in range(B):
+        # query i keeps the keys p with p - (c + i) < window
+        lim = c + i + window
+        keys_k = np.concatenate([kc, np.transpose(kb, (1, 0, 2))], axis=1)[:, :lim]
+        keys_v = np.concatenate([vc, np.transpose(vb, (1, 0, 2))], axis=1)[:, :lim]
+        out[i] = _orig["kv_injected_attention"](q[i:i + 1], kb[:0], vb[:0], keys_k, keys_v,
+                                                group)[0]
+    return out
+
+
+def _layer_window_ignored(cfg, l):
+    return None
+
+
+def _layer_window_every_layer(cfg, l):
+    w = getattr(cfg, "sliding_window", 0) or 0
+    return int(w) if w > 0 else None
+
+
 MUTATIONS = {
+    "window_off_by_one": ("kv_injected_attention", _window_off_by_one),
+    "window_reversed": ("kv_injected_attention", _window_reversed),
+    "layer_window_ignored": ("layer_window", _layer_window_ignored),
+    "layer_window_every_layer": ("layer_window", _layer_window_every_layer),
     "rope_sign": ("rope", _rope_sign),
     "rope_interleaved_pairs": ("rope", _rope_interleaved),
     "rope_freq_index": ("rope", _rope_freq_off_by_one),
