@@ -72,6 +72,12 @@ def parse():
     ap.add_argument("--temperature", type=float, default=0.0,
                     help="> 0: draft by sampling softmax(logits / T) and verify by speculative "
                          "rejection sampling against seeded target logits (0: greedy)")
+    ap.add_argument("--block", type=int, default=0,
+                    help="drafter variant: block size B (default: the workload's, 16)")
+    ap.add_argument("--layers", type=int, default=0,
+                    help="drafter variant: number of draft layers (default: the workload's, 5)")
+    ap.add_argument("--window", type=int, default=0,
+                    help="drafter variant: every layer a sliding-window layer of this many keys")
     ap.add_argument("--graph", action="store_true",
                     help="also time the device-resident round (accept, fuse the block, inject "
                          "the accepted rows, draft) eagerly and as one replayed HIP graph")
@@ -100,10 +106,21 @@ def main() -> int:
         print("no GPU visible: bench.py needs an MI355X", file=sys.stderr)
         return 1
     W = WORKLOADS[a.workload]
+    variant = {}
+    if a.block:
+        variant["block_size"] = a.block
+    if a.layers:
+        variant["n_layers"] = a.layers
+    if a.window:
+        variant["sliding_window"] = a.window
+        variant["sliding_layers"] = tuple(range(a.layers or W.model.n_layers))
+    if variant:
+        import dataclasses
+        W = dataclasses.replace(W, model=W.model.with_(**variant))
     cfg = W.model
     b, Bk, d = W.batch, cfg.block_size, cfg.hidden
     ctx_lens = I.ctx_lengths(W)
-    max_new = 16
+    max_new = cfg.block_size  # a round appends a + 1 <= B rows
     n_prof = max(3, min(10, a.steps))
     total_steps = a.warmup + n_prof + a.steps + (2 * (a.warmup + a.steps) if a.graph else 0)
     cap = int(((int(ctx_lens.max()) + max_new * total_steps + Bk + 31) // 32) * 32)
@@ -258,7 +275,9 @@ def main() -> int:
                for k, e in prof_all.items() if e["launches"]}
 
     out = {
-        "metric": METRIC, "value": round(value, 1), "unit": "block-tokens/s",
+        "metric": METRIC if (L, Bk) == (5, 16) else
+        f"drafted block-tokens/sec ({L}-layer, block {Bk}) + % HBM/MFMA roofline",
+        "value": round(value, 1), "unit": "block-tokens/s",
         "n_gpus": 1, "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": cfg.dtype,
@@ -268,6 +287,7 @@ def main() -> int:
                    "new_rows_per_round": int(n_tok), "hidden": d, "heads": [Hq, Hkv],
                    "intermediate": cfg.intermediate, "vocab": cfg.vocab,
                    "decoding": f"sampled, temperature {T}" if T > 0 else "greedy",
+                   "sliding_window": cfg.sliding_window or None,
                    "parallelism": "none (1 GPU)"},
         "roofline": roof,
         "step_roofline": {"t_roof_ms": round(t_roof * 1e3, 5),

@@ -29,7 +29,9 @@ class Config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
                 ("hidden", "n_heads", "n_kv_heads", "head_dim", "n_layers", "intermediate",
                  "n_target_feats", "target_hidden", "vocab", "block_size", "mask_token_id",
-                 "dtype")] + [("rms_eps", ctypes.c_float), ("rope_theta", ctypes.c_float)]
+                 "dtype")] + [("rms_eps", ctypes.c_float), ("rope_theta", ctypes.c_float),
+                              ("sliding_window", ctypes.c_int32),
+                              ("sliding_layer_mask", ctypes.c_uint32)]
 
 
 class LayerWeights(ctypes.Structure):
@@ -156,7 +158,9 @@ def make_config(cfg) -> Config:
                   vocab=cfg.vocab, block_size=cfg.block_size, mask_token_id=cfg.mask_token_id,
                   dtype=DFLASH_BF16 if cfg.dtype == "bf16" else DFLASH_FP32,
                   rms_eps=cfg.rms_eps,
-                  rope_theta=float(cfg.rope_theta) if cfg.rope_theta is not None else 0.0)
+                  rope_theta=float(cfg.rope_theta) if cfg.rope_theta is not None else 0.0,
+                  sliding_window=int(getattr(cfg, "sliding_window", 0) or 0),
+                  sliding_layer_mask=sum(1 << int(l) for l in getattr(cfg, "sliding_layers", ())))
 
 
 class KVCache:

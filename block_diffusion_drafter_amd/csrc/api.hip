@@ -199,6 +199,10 @@ int32_t check_config(const dflash_config& c) {
   if (c.head_dim != 64 && c.head_dim != 128) return DFLASH_ERR_UNSUPPORTED;
   if (c.block_size < 1 || c.block_size > 16) return DFLASH_ERR_UNSUPPORTED;
   if (c.n_layers > kMaxLayers) return DFLASH_ERR_UNSUPPORTED;
+  if (c.sliding_layer_mask != 0u) {
+    if (c.sliding_window < 1) return DFLASH_ERR_SHAPE;
+    if (c.n_layers < 32 && (c.sliding_layer_mask >> c.n_layers) != 0u) return DFLASH_ERR_SHAPE;
+  }
   if (c.n_target_feats > kMaxASeg) return DFLASH_ERR_UNSUPPORTED;
   if (c.hidden % mult || c.intermediate % mult || c.target_hidden % mult) return DFLASH_ERR_SHAPE;
   // Fused features are separate A segments; a 256-byte GEMM chunk must not straddle two.
@@ -623,6 +627,7 @@ int32_t dflash_draft_forward(const dflash_handle* h, const dflash_kv_cache* cach
     at.head_dim = hd;
     at.block = B;
     at.cap = cap;
+    at.window = ((c.sliding_layer_mask >> l) & 1u) ? c.sliding_window : 0;
     at.wg_per_head = P.attn_wg;
     at.min_blocks = kAttnMinBlocks;
     at.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)hd));

@@ -26,6 +26,8 @@
 //     segment's (max, sum, unnormalised O) goes to a partial buffer.
 //   attn_combine: merges the segments of the sequences that span several
 //     workgroups.
+#include <climits>
+
 #include "common.h"
 #include "internal.h"
 
@@ -64,15 +66,33 @@ __device__ __forceinline__ u32x4 keep_first(u32x4 v, int nvalid) {
   return v;
 }
 
+__device__ __forceinline__ int seq_ctx(const AttnArgs& p, int s) {
+  const int cl = p.ctx_len[s];
+  return cl < 0 ? 0 : cl;
+}
+
 __device__ __forceinline__ int seq_keys(const AttnArgs& p, int s) {
-  int cl = p.ctx_len[s];
-  cl = cl < 0 ? 0 : cl;
-  return min(cl + p.block, p.cap);
+  return min(seq_ctx(p, s) + p.block, p.cap);
+}
+
+// First key position a layer reads for sequence s: 0, or in a sliding-window
+// layer the 32-key block holding the oldest position query 0 sees
+// (ctx_len - window + 1); positions below a query's own window edge inside
+// that block are masked per query.
+__device__ __forceinline__ int seq_first(const AttnArgs& p, int s) {
+  if (p.window <= 0) return 0;
+  const int lo = seq_ctx(p, s) - p.window + 1;
+  return lo <= 0 ? 0 : (lo & ~31);
+}
+
+// Lowest key position query row r of sequence s may see (none below it).
+__device__ __forceinline__ int query_first(const AttnArgs& p, int s, int r) {
+  return p.window > 0 ? seq_ctx(p, s) + r - p.window + 1 : INT_MIN;
 }
 
 // First 32-key block of every sequence when one KV head's keys are laid end
-// to end: pre[s] = sum over t < s of ceil(keys(t) / 32), pre[batch] = the
-// total. Built in LDS by wave 0 (one load per lane and sequence, a wave scan
+// to end: pre[s] = sum over t < s of the blocks sequence t reads (from
+// seq_first to its last key), pre[batch] = the total. Built in LDS by wave 0 (one load per lane and sequence, a wave scan
 // per 64 sequences); every thread returns after the barrier that publishes it.
 __device__ __forceinline__ void seq_block_prefix(const AttnArgs& p, int* pre) {
   if (threadIdx.x < 64) {
@@ -80,7 +100,7 @@ __device__ __forceinline__ void seq_block_prefix(const AttnArgs& p, int* pre) {
     int carry = 0;
     for (int base = 0; base < p.batch; base += 64) {
       const int s = base + lane;
-      int v = s < p.batch ? (seq_keys(p, s) + 31) >> 5 : 0;
+      int v = s < p.batch ? (seq_keys(p, s) - seq_first(p, s) + 31) >> 5 : 0;
 #pragma unroll
       for (int o = 1; o < 64; o <<= 1) {
         const int u = __shfl_up(v, o);
@@ -169,8 +189,8 @@ struct AttnState {
 
 template <typename T, int HD>
 __device__ __forceinline__ void attn_update(AttnState<T, HD>& S, const KVBlock<T, HD>& b,
-                                            const u32x4* qf, int kb, int k_hi, float scale_log2,
-                                            int grp) {
+                                            const u32x4* qf, int kb, int k_hi, int k_min,
+                                            float scale_log2, int grp) {
   using KB = KVBlock<T, HD>;
   constexpr int FR = KB::FR, NDT = KB::NDT;
   f32x4 st[2];
@@ -186,22 +206,24 @@ __device__ __forceinline__ void attn_update(AttnState<T, HD>& S, const KVBlock<T
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int key = kb + key_of<T>(t, 4 * grp + i);
-      const float v = key < k_hi ? st[t][i] * scale_log2 : -INFINITY;
+      const float v = (key < k_hi && key >= k_min) ? st[t][i] * scale_log2 : -INFINITY;
       st[t][i] = v;
       mx = fmaxf(mx, v);
     }
   mx = fmaxf(mx, __shfl_xor(mx, 16));
   mx = fmaxf(mx, __shfl_xor(mx, 32));
-  // Every block holds at least one valid key, so m_new is finite.
+  // A block may hold no key this query sees yet (sliding window): m_new stays
+  // -inf, and a finite reference keeps alpha at 1 and every p at 0.
   const float m_new = fmaxf(S.m_run, mx);
-  const float alpha = exp2f(S.m_run - m_new);
+  const float m_ref = m_new == -INFINITY ? 0.f : m_new;
+  const float alpha = exp2f(S.m_run - m_ref);
   S.m_run = m_new;
   float psum = 0.f;
 #pragma unroll
   for (int t = 0; t < 2; ++t)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float pv = exp2f(st[t][i] - m_new);
+      const float pv = exp2f(st[t][i] - m_ref);
       st[t][i] = pv;
       psum += pv;
     }
@@ -291,9 +313,9 @@ __device__ __forceinline__ void for_each_segment(const AttnArgs& p, const int* p
   }
   for (int s = lo; s < p.batch && pre[s] < b1; ++s) {
     const int bs = pre[s], be = pre[s + 1];
-    const int n_keys = seq_keys(p, s);
+    const int n_keys = seq_keys(p, s), k0 = seq_first(p, s);
     const int a = max(b0, bs), b = min(b1, be);
-    if (a < b) seg(s, 32 * (a - bs), min(n_keys, 32 * (b - bs)), a == bs && b == be);
+    if (a < b) seg(s, k0 + 32 * (a - bs), min(n_keys, k0 + 32 * (b - bs)), a == bs && b == be);
   }
 }
 
@@ -316,6 +338,7 @@ __global__ __launch_bounds__(512) void attn_partial_kernel(AttnArgs p) {
   const T* K = reinterpret_cast<const T*>(p.k) + kvoff;
   const T* V = reinterpret_cast<const T*>(p.v) + kvoff;
 
+  const int k_min = query_first(p, s, r);
   u32x4 qf[FR];
   load_q<T, HD>(qf, p, s, h, r, grp);
   AttnState<T, HD> S;
@@ -329,10 +352,10 @@ __global__ __launch_bounds__(512) void attn_partial_kernel(AttnArgs p) {
     for (int kb = k_lo; kb < k_hi; kb += 64) {
       const bool has1 = kb + 32 < k_hi;
       if (has1) load_block<T, HD>(b1, K, V, kb + 32, k_hi, r, grp);
-      attn_update<T, HD>(S, b0, qf, kb, k_hi, p.scale_log2, grp);
+      attn_update<T, HD>(S, b0, qf, kb, k_hi, k_min, p.scale_log2, grp);
       if (has1) {
         if (kb + 64 < k_hi) load_block<T, HD>(b0, K, V, kb + 64, k_hi, r, grp);
-        attn_update<T, HD>(S, b1, qf, kb + 32, k_hi, p.scale_log2, grp);
+        attn_update<T, HD>(S, b1, qf, kb + 32, k_hi, k_min, p.scale_log2, grp);
       }
     }
   } else {
@@ -340,7 +363,7 @@ __global__ __launch_bounds__(512) void attn_partial_kernel(AttnArgs p) {
     for (int kb = k_lo; kb < k_hi; kb += 32) {
       KB b0;
       load_block<T, HD>(b0, K, V, kb, k_hi, r, grp);
-      attn_update<T, HD>(S, b0, qf, kb, k_hi, p.scale_log2, grp);
+      attn_update<T, HD>(S, b0, qf, kb, k_hi, k_min, p.scale_log2, grp);
     }
   }
   attn_finish<T, HD>(S, p, s, g, part_entry(p, g, w, s), j, G, single, r, grp);
@@ -418,6 +441,7 @@ __global__ __launch_bounds__(64 * G) void attn_partial_lds_kernel(AttnArgs p) {
     }
   };
 
+  const int k_min = query_first(p, s, r);
   u32x4 qf[FR];
   load_q<T, HD>(qf, p, s, h, r, grp);
   // Consume Q here, so the compiler's wait for it happens before the ring's
@@ -452,7 +476,7 @@ __global__ __launch_bounds__(64 * G) void attn_partial_lds_kernel(AttnArgs p) {
       if (kb + 32 > k_hi) x = keep_first<T>(x, k_hi - (kb + 8 * grp));
       b.v[dt][0] = x;
     }
-    attn_update<T, HD>(S, b, qf, kb, k_hi, p.scale_log2, grp);
+    attn_update<T, HD>(S, b, qf, kb, k_hi, k_min, p.scale_log2, grp);
     if (n + 1 < nblk) {
       if (n + NSB <= nblk) attn_wait_barrier<IPW * (NSB - 2)>();
       else attn_wait_barrier<0>();

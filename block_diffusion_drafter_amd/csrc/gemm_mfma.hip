@@ -415,7 +415,9 @@ static int mfma_shape(int epi, int M, int N, int K) {
     const int ks = (sh.bm == 128 && sh.bn == 128) ? ksplit_128(epi, M, N, K) : 1;
     const long long wgs =
         (long long)((M + sh.bm - 1) / sh.bm) * mfma_colblocks(epi, N, sh.bn) * ks;
-    const double t = (double)((wgs + 255) / 256) * sh.bm * sh.bn / (ks * sh.eff);
+    // the LM head's 256x256 blocks issue their loads early: 1.25x measured
+    const double eff = sh.eff * (epi == EPI_ARGMAX && sh.bm == 256 ? 1.25 : 1.0);
+    const double t = (double)((wgs + 255) / 256) * sh.bm * sh.bn / (ks * eff);
     if (t < best_t * 0.999) {
       best_t = t;
       best = i;

@@ -113,6 +113,7 @@ struct AttnArgs {
   const void* v;         // this layer's V cache base: [cache_batch][Hkv][cap/32][hd][32]
   const int32_t* ctx_len;
   int batch, n_heads, n_kv_heads, head_dim, block, cap;
+  int window;            // > 0: query i (position ctx_len + i) sees keys p > ctx_len + i - window
   int wg_per_head;       // workgroups per KV head that split its keys (grid x)
   int min_blocks;        // fewest 32-key blocks a workgroup is given
   float scale_log2;      // log2(e) / sqrt(head_dim)

@@ -85,6 +85,14 @@ typedef struct dflash_config {
   int32_t dtype;            /* dflash_dtype */
   float rms_eps;
   float rope_theta;
+  /* Sliding-window layers [W "Paper vs code", attention-pattern bullet: the
+   * reference code supports per-layer sliding-window attention]: layer l
+   * with bit l of sliding_layer_mask set lets block query i (position
+   * ctx_len + i) see key position p only when ctx_len + i - p < sliding_window;
+   * other layers attend to every position. mask 0: no sliding layer (window
+   * ignored); otherwise window >= 1 and no bit at or above n_layers. */
+  int32_t sliding_window;
+  uint32_t sliding_layer_mask;
 } dflash_config;
 
 /* One draft layer. Shapes (d = hidden, hd = head_dim, I = intermediate):

@@ -267,3 +267,21 @@ def test_block_append_and_round_graph_reject_bad_arguments_before_launching():
     assert lib.dflash_round_graph_launch(None, None) == -1
     lib.dflash_round_graph_destroy(None)  # no-op
     lib.dflash_destroy(h)
+
+
+def test_sliding_window_config_is_validated():
+    lib = B.lib()
+    c = B.make_config(TINY_FP32.with_(n_layers=2, sliding_window=8, sliding_layers=(1,)))
+    rc, h = create(c)
+    assert rc == 0
+    lib.dflash_destroy(h)
+    c.sliding_window = 0          # a sliding layer needs a window >= 1
+    assert create(c)[0] == -2
+    c.sliding_window = 8
+    c.sliding_layer_mask = 1 << 2  # no layer 2 in a 2-layer drafter
+    assert create(c)[0] == -2
+    c.sliding_layer_mask = 0       # no sliding layer: the window is ignored
+    c.sliding_window = -5
+    rc, h = create(c)
+    assert rc == 0
+    lib.dflash_destroy(h)

@@ -40,9 +40,12 @@ def test_gpu_accept_matches_oracle():
             assert (anc.cpu().numpy() == b_o).all()
 
 
-def run_flow(cfg, ctx_lens, tag, seed=0, cap_extra=0, split_append=1):
+def run_flow(cfg, ctx_lens, tag, seed=0, cap_extra=0, split_append=1, degenerate=False):
     """Prefill through ctx_project + ctx_kv_append, then one draft forward with
-    fused accept on planted targets; every stage compared with the oracle."""
+    fused accept on planted targets; every stage compared with the oracle.
+    degenerate: the case's drafts are near ties by construction (e.g. every
+    mask slot sees only mask slots), so the draft and accept checks run on the
+    confident slots only, without requiring those to be the majority."""
     ctx_lens = [int(c) for c in ctx_lens]
     b, Bk, d = len(ctx_lens), cfg.block_size, cfg.hidden
     m = Bk - 1
@@ -114,7 +117,8 @@ def run_flow(cfg, ctx_lens, tag, seed=0, cap_extra=0, split_append=1):
     if m:
         assert_close(cfg, to_np(logits_g), res.logits, "logits")
         excl = check_drafts(res, drafts, "drafts")
-        assert excl <= max(2, 0.5 * res.drafts.size), "too many low-margin slots to be a test"
+        if not degenerate:
+            assert excl <= max(2, 0.5 * res.drafts.size), "too many low-margin slots to be a test"
     check_accept(res, targets, acc_g.cpu().numpy(), bon_g.cpu().numpy(), drafts, "accept")
     return M, cache, res
 
