@@ -133,6 +133,13 @@ int64_t splitk_elems(int dtype, int epi, int M, int N, int K) {
   return ks > 1 ? (int64_t)ks * M * N : 0;
 }
 
+// The same for a call of any row count up to Mmax (the plan's split is not
+// monotone in M): the bound every K split of the MFMA path stays within.
+int64_t splitk_elems_upto(int dtype, int M, int N, int K) {
+  if (!gemm_uses_mfma(dtype, M, K, true)) return 0;
+  return kMfmaMaxSplit * std::min<int64_t>((int64_t)M * N, kMfmaSplitMaxElems);
+}
+
 Plan make_plan(const dflash_config& c, int batch, int cap, int max_tokens) {
   Plan p{};
   const size_t es = elem_size(c.dtype);
@@ -174,13 +181,13 @@ Plan make_plan(const dflash_config& c, int batch, int cap, int max_tokens) {
   p.u = take((size_t)max_tokens * d * 4);
   const int fk = c.n_target_feats * c.target_hidden;
   p.ua = gemm_uses_mfma(dt, max_tokens, fk, true) ? take(tiled_bytes(dt, max_tokens, fk)) : 0;
-  p.upart_elems = splitk_elems(dt, EPI_STORE_F32, max_tokens, (int)d, fk);
+  p.upart_elems = splitk_elems_upto(dt, max_tokens, (int)d, fk);
   p.upart = take((size_t)p.upart_elems * 4);
   p.proj_end = off;
   off = 0;
   p.kv = take((size_t)max_tokens * c.n_layers * 2 * Hkv * hd * 4);
   p.ca = gemm_uses_mfma(dt, max_tokens, (int)d, true) ? take(tiled_bytes(dt, max_tokens, (int)d)) : 0;
-  p.kvpart_elems = splitk_elems(dt, EPI_STORE_F32, max_tokens, (int)(c.n_layers * 2 * Hkv * hd), (int)d);
+  p.kvpart_elems = splitk_elems_upto(dt, max_tokens, (int)(c.n_layers * 2 * Hkv * hd), (int)d);
   p.kvpart = take((size_t)p.kvpart_elems * 4);
   p.app_end = off;
   p.total = std::max(p.fwd_end, std::max(p.proj_end, p.app_end));

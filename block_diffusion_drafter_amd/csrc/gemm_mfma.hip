@@ -9,19 +9,22 @@
 //     waves, 128x128 or 128x96 with 4, whichever fills the 256 CUs best for
 //     the least work); each wave a (BM/WGM) x (BN/WGN) sub-block of 16x16
 //     MFMA tiles held in registers;
-//   * K advances in stages of 32 or 64. A stage of A and W is copied from
+//   * K advances in stages of 32 (8 waves) or 64 (4 waves). A stage of A
+//     and W is copied from
 //     the tiled layout into LDS unchanged by direct global->LDS loads
 //     (global_load_lds_dwordx4: one 1 KB fragment per wave instruction, no
 //     registers), and every LDS read of an MFMA operand is 64 lanes x 16
 //     contiguous bytes (no bank conflicts, no shuffles);
-//   * the stages form a ring of NS slots in LDS with NS-1 stages in flight,
-//     so each stage's loads have NS-2 stages of MFMA work to arrive; one
-//     wait + barrier per stage (a register-staged double buffer left the
-//     matrix cores idle on load latency at every stage);
+//   * the stages form a ring of NS slots in LDS with NS-1 stages in flight;
+//     one wait + barrier per stage (a register-staged double buffer left the
+//     matrix cores idle on load latency at every stage); every wave reads
+//     the next stage's operands into a second register set while it
+//     multiplies the current ones;
 //   * workgroups that share a column block but differ in row block are
 //     numbered 8 apart, so they run on the same XCD at about the same time
 //     and the second reads the weight block from that XCD's L2.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 #include "internal.h"
@@ -60,21 +63,44 @@ __device__ __forceinline__ void wait_loads_and_barrier() {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
-// Wait for this wave's LDS reads, then meet the other waves.
-__device__ __forceinline__ void wait_lds_and_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
 }  // namespace
 
-// One workgroup per CU (the LDS ring takes most of it): WGM*WGN/4 waves per
-// SIMD, which lets the compiler spend registers on two stages of operands.
-template <int BM, int BN, int WGM, int WGN, int KF, int NS, int EPI, bool EARLY>
+// resid[m, n] += acc over a wave's TM x TN tiles (lane (r, grp) holds rows
+// 4*grp + e of column col0 + 16 j in tile (i, j)). All loads of a row of
+// tiles go out before its stores: element by element, the compiler waited for
+// every load, since a store might alias the next load.
+template <int TM, int TN>
+__device__ __forceinline__ void resid_add_tiles(const GemmArgs& p, const f32x4 (&acc)[TM][TN],
+                                                int row0, int col0, int grp) {
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    float v[TN][4];
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int m = row0 + 16 * i + 4 * grp + e, n = col0 + 16 * j;
+        v[j][e] = (m < p.M && n < p.N) ? p.resid[(int64_t)m * p.out_stride + n] : 0.f;
+      }
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int m = row0 + 16 * i + 4 * grp + e, n = col0 + 16 * j;
+        if (m < p.M && n < p.N) p.resid[(int64_t)m * p.out_stride + n] = v[j][e] + acc[i][j][e];
+      }
+  }
+}
+
+// Four waves, one per SIMD, for the narrow blocks (128 x 128 / 96): one
+// workgroup per CU (the LDS ring takes most of it), each wave prefetching the
+// next stage's operands into registers while it multiplies the current ones.
+template <int BM, int BN, int WGM, int WGN, int KF, int NS, int EPI>
 __global__ __launch_bounds__(64 * WGM * WGN)
-__attribute__((amdgpu_waves_per_eu(WGM * WGN / 4, WGM * WGN / 4)))
+__attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_mfma_kernel(GemmArgs p, int n_colblk, int n_rowblk) {
   using G = MfmaGeom<BM, BN, WGM, WGN, KF, NS>;
-  constexpr bool PF = WGM * WGN == 4;  // one wave per SIMD: prefetch operands in registers
+  static_assert(WGM * WGN == 4, "one wave per SIMD");
   constexpr int TM = G::TM, TN = G::TN, AT = G::AT, BT = G::BT, SF = G::SF, FPW = G::FPW;
   constexpr int NW = G::NW;
   __shared__ u32x4 lds[NS][SF][64];
@@ -202,72 +228,34 @@ void gemm_mfma_kernel(GemmArgs p, int n_colblk, int n_rowblk) {
   // reads of stage s have returned (its operands are in registers) and every
   // wave passes the barrier, so slot s % NS is free and stage s + NS is issued
   // into it; stage s + 1 has landed (each wave waited for its own loads
-  // before the barrier). With one wave per SIMD (PF) stage s+1's LDS reads go
-  // out between stage s's MFMAs; with two, the other wave on the SIMD covers
-  // them and the operands of one stage at a time fit the registers.
+  // before the barrier). Stage s+1's LDS reads go out between stage s's
+  // MFMAs.
 #pragma unroll
   for (int st = 0; st < NS; ++st)
     if (st < nst) issue(st, st);
   if (nst >= NS) wait_loads_and_barrier<FPW * (NS - 1)>();
   else wait_loads_and_barrier<0>();
-  if constexpr (PF) {
-    Frags f0, f1;
-    lds_read(f0, 0);
-    auto step = [&](int s, Frags& cur, Frags& nxt) {
-      const int slot = s % NS;
-      if (s + 1 < nst) {
-        // Issued so far: stages up to min(nst, s + NS) - 1, so stage s+1 has
-        // landed once at most min(NS - 2, nst - 2 - s) later stages are outstanding.
-        if (s + NS <= nst) wait_loads_and_barrier<FPW * (NS - 2)>();
-        else wait_loads_and_barrier<0>();
-        if (s + NS < nst) issue(s + NS, slot);
-        mma(cur, &nxt, (s + 1) % NS);
-      } else {
-        mma(cur, nullptr, 0);
-      }
-    };
-    int s = 0;
-    for (; s + 1 < nst; s += 2) {
-      step(s, f0, f1);
-      step(s + 1, f1, f0);
+  Frags f0, f1;
+  lds_read(f0, 0);
+  auto step = [&](int s, Frags& cur, Frags& nxt) {
+    const int slot = s % NS;
+    if (s + 1 < nst) {
+      // Issued so far: stages up to min(nst, s + NS) - 1, so stage s+1 has
+      // landed once at most min(NS - 2, nst - 2 - s) later stages are outstanding.
+      if (s + NS <= nst) wait_loads_and_barrier<FPW * (NS - 2)>();
+      else wait_loads_and_barrier<0>();
+      if (s + NS < nst) issue(s + NS, slot);
+      mma(cur, &nxt, (s + 1) % NS);
+    } else {
+      mma(cur, nullptr, 0);
     }
-    if (s < nst) step(s, f0, f1);
-  } else if constexpr (EARLY) {
-    // Early issue: once every wave holds stage s in registers (second
-    // barrier), its slot takes stage s + NS before the MFMAs of stage s, so a
-    // stage's loads have NS stages of matrix work to arrive instead of NS - 1.
-    // Pays where the loads' latency, not the matrix core, sets the pace (the
-    // LM head streams each weight block once); the extra barrier costs
-    // elsewhere.
-    for (int s = 0; s < nst; ++s) {
-      const int slot = s % NS;
-      if (s > 0) {
-        // Issued: stages up to min(s - 1 + NS, nst - 1); stage s must have landed.
-        if (nst - 1 - s >= NS - 1) wait_loads_and_barrier<FPW * (NS - 1)>();
-        else wait_loads_and_barrier<0>();
-      }
-      Frags f;
-      lds_read(f, slot);
-      if (s + NS < nst) {
-        wait_lds_and_barrier();
-        issue(s + NS, slot);
-      }
-      mma(f, nullptr, 0);
-    }
-  } else {
-    for (int s = 0; s < nst; ++s) {
-      const int slot = s % NS;
-      Frags f;
-      lds_read(f, slot);
-      mma(f, nullptr, 0);
-      if (s + 1 < nst) {
-        // The reads of stage s are done (lgkmcnt) before the barrier frees its slot.
-        if (s + NS <= nst) wait_loads_and_barrier<FPW * (NS - 2)>();
-        else wait_loads_and_barrier<0>();
-        if (s + NS < nst) issue(s + NS, slot);
-      }
-    }
+  };
+  int s = 0;
+  for (; s + 1 < nst; s += 2) {
+    step(s, f0, f1);
+    step(s + 1, f1, f0);
   }
+  if (s < nst) step(s, f0, f1);
   __syncthreads();
 
   // Epilogue. Lane (r, grp) of tile (i, j) holds rows 4*grp + e of column r.
@@ -348,7 +336,7 @@ void gemm_mfma_kernel(GemmArgs p, int n_colblk, int n_rowblk) {
           }
         }
       }
-  } else {
+  } else if constexpr (EPI == EPI_STORE_F32) {
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -358,13 +346,276 @@ void gemm_mfma_kernel(GemmArgs p, int n_colblk, int n_rowblk) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int m = row0 + 16 * i + 4 * grp + e;
-          if (m >= p.M) continue;
-          if constexpr (EPI == EPI_STORE_F32)
-            reinterpret_cast<float*>(p.out)[(int64_t)m * p.out_stride + n] = acc[i][j][e];
-          else
-            p.resid[(int64_t)m * p.out_stride + n] += acc[i][j][e];
+          if (m < p.M) reinterpret_cast<float*>(p.out)[(int64_t)m * p.out_stride + n] = acc[i][j][e];
         }
       }
+  } else {
+    resid_add_tiles<TM, TN>(p, acc, row0, (tile_n0 + wn * TN) * 16 + r, grp);
+  }
+}
+
+// Eight waves (two per SIMD) over a 256-row block, k = 32 per stage in an
+// NS-slot LDS ring, and everything a stage needs besides its MFMAs hidden
+// inside them. The block's data for one stage is one 1 KB fragment per
+// 16-row tile of A and of W: (BM + BN) / 16 fragments, split over the waves.
+// Iteration s of the loop:
+//   * wait until stage s+1 has landed and every wave holds stage s in
+//     registers (vmcnt + lgkmcnt, then a barrier), so the slot of stage s is
+//     free;
+//   * run stage s's MFMAs from registers in program order, fenced in groups
+//     of MPR: after each group one LDS read of stage s+1's operands (into the
+//     second register set), and after the first groups this wave's loads of
+//     stage s+NS into the freed slot.
+// The loads go out one at a time between MFMAs instead of all waves queueing
+// theirs at the same moment after the barrier, which stalled the issuing
+// waves (measured: +10-25% at 480-2048 rows); the LDS reads of the next
+// stage overlap the current MFMAs. Every iteration issues a stage (past the
+// end: the slice's last stage again, into a slot nobody reads any more), so
+// the wait count is the same in every iteration and the loop has no branches
+// (branches in the loop made the register allocator spill the accumulators).
+// LDS holds nothing but the ring during the loop: a second LDS array made the
+// compiler wait for every outstanding global->LDS load before each LDS read.
+template <int BM, int BN, int WGM, int WGN, int NS, int EPI>
+__global__ __launch_bounds__(64 * WGM * WGN)
+__attribute__((amdgpu_waves_per_eu(WGM * WGN / 4, WGM * WGN / 4)))
+void gemm_pipe_kernel(GemmArgs p, int n_colblk, int n_rowblk) {
+  constexpr int NW = WGM * WGN;
+  constexpr int WM = BM / WGM, WN = BN / WGN;
+  constexpr int TM = WM / 16, TN = WN / 16;
+  constexpr int AT = BM / 16, BT = BN / 16;
+  constexpr int SF = AT + BT;             // fragments per stage
+  constexpr int FPW = (SF + NW - 1) / NW; // loads per wave per stage (the last may be idle)
+  constexpr bool SW = EPI == EPI_SWIGLU;
+  static_assert(NS >= 3, "a slot being read, one arriving, one being filled");
+  static_assert(!SW || TN % 2 == 0, "SwiGLU pairs gate and up tiles");
+  __shared__ u32x4 lds[NS][SF][64];
+
+  const int per_split = gridDim.x / p_ksplit(p);
+  const int z = blockIdx.x / per_split;
+  const int id = blockIdx.x - z * per_split;
+  const int xcd = id & 7, q = id >> 3;
+  const int rb = q % n_rowblk;
+  const int cb = (q / n_rowblk) * 8 + xcd;
+  if (cb >= n_colblk) return;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave / WGN, wn = wave % WGN;
+  const int r = lane & 15, grp = lane >> 4;
+  const int nck = (p.K + kKC - 1) / kKC;
+  // The host guarantees K % 64 == 0 and an even number of stages per slice.
+  const int nst_all = p.K / 32;
+  const int nst = nst_all / p_ksplit(p);
+  const int s0 = z * nst;
+  const int m_tiles = (p.M + 15) >> 4, n_tiles = (p.N + 15) >> 4;
+  const int tile_m0 = rb * AT;
+  const int tile_n0 = cb * (SW ? BT / 2 : BT);
+
+  const bf16* A = reinterpret_cast<const bf16*>(p.a[0]);
+  const bf16* W = reinterpret_cast<const bf16*>(p.w);
+  const bf16* W2 = reinterpret_cast<const bf16*>(p.w2);
+
+  // Fragment j = wave + NW * i of a stage: j < AT: A row tile j, else W tile
+  // j - AT (SwiGLU: BT/2 gate tiles, then the same BT/2 up tiles). Tiles past
+  // the matrix re-read its last tile (valid memory, never stored).
+  const bf16* src[FPW];
+#pragma unroll
+  for (int i = 0; i < FPW; ++i) {
+    const int j = min(wave + NW * i, SF - 1);
+    const bf16* base;
+    int t;
+    if (j < AT) {
+      base = A;
+      t = min(tile_m0 + j, m_tiles - 1);
+    } else {
+      const int bt = j - AT;
+      base = W;
+      t = tile_n0 + bt;
+      if constexpr (SW) {
+        if (bt >= BT / 2) {
+          base = W2;
+          t = tile_n0 + bt - BT / 2;
+        }
+      }
+      t = min(t, n_tiles - 1);
+    }
+    src[i] = base + ((int64_t)t * nck * 4 + s0) * kFRAG + lane * kEPF;
+  }
+  // When the stage's fragments do not split evenly, waves >= SF % NW have one
+  // load fewer (the last), and wait for correspondingly fewer.
+  constexpr bool EVEN = SF % NW == 0;
+  const bool full = EVEN || wave < SF % NW;  // wave-uniform
+  auto load = [&](int i, int st, int slot) {
+    if (EVEN || i < FPW - 1 || full)
+      __builtin_amdgcn_global_load_lds((gbl_ptr_t)(src[i] + (int64_t)st * kFRAG),
+                                       (lds_ptr_t)&lds[slot][wave + NW * i][0], 16, 0, 0);
+  };
+  // Stage s+1 landed: at most `later` stages of this wave's loads outstanding.
+  auto wait_stage = [&](auto later) {
+    constexpr int L = decltype(later)::value;
+    if (full) wait_loads_and_barrier<FPW * L>();
+    else wait_loads_and_barrier<(FPW - 1) * L>();
+  };
+
+  f32x4 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // LDS index of the wave's B tile j (SwiGLU: first TN/2 gate, then up).
+  auto btile = [&](int j) -> int {
+    if constexpr (SW) return j < TN / 2 ? wn * (TN / 2) + j : BT / 2 + wn * (TN / 2) + j - TN / 2;
+    else return wn * TN + j;
+  };
+  struct Ops {
+    u32x4 a[TM];
+    u32x4 b[TN];
+  };
+  auto read_one = [&](Ops& O, int slot, int k) {
+    if (k < TM) O.a[k] = lds[slot][wm * TM + k][lane];
+    else O.b[k - TM] = lds[slot][AT + btile(k - TM)][lane];
+  };
+  constexpr int NMFMA = TM * TN, NREAD = TM + TN;
+  constexpr int MPR = NMFMA / NREAD > 0 ? NMFMA / NREAD : 1;
+  static_assert(NREAD >= FPW, "one load per read group");
+  auto compute = [&](const Ops& C) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) acc[i][j] = mfma_frag<bf16>(C.a[i], C.b[j], acc[i][j]);
+  };
+  // Groups of MPR MFMAs, each with one LDS read of the next stage (and, in
+  // the first FPW groups, one load), fenced from the next group; the
+  // compiler places each read ahead of its group's MFMAs.
+  auto stage = [&](int s, const Ops& C, Ops& N) {
+    wait_stage(std::integral_constant<int, NS - 2>());
+    const int ist = min(s + NS, nst - 1), islot = s % NS, nslot = (s + 1) % NS;
+    __builtin_amdgcn_sched_barrier(0);
+    int rd = 0;
+#pragma unroll
+    for (int t = 0; t < NMFMA; ++t) {
+      acc[t / TN][t % TN] = mfma_frag<bf16>(C.a[t / TN], C.b[t % TN], acc[t / TN][t % TN]);
+      if ((t + 1) % MPR == 0 && rd < NREAD) {
+        read_one(N, nslot, rd);
+        if (rd < FPW) load(rd, ist, islot);
+        ++rd;
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+
+#pragma unroll
+  for (int st = 0; st < NS; ++st)
+#pragma unroll
+    for (int i = 0; i < FPW; ++i) load(i, min(st, nst - 1), st);
+  wait_stage(std::integral_constant<int, NS - 1>());
+  Ops r0, r1;
+#pragma unroll
+  for (int k = 0; k < NREAD; ++k) read_one(r0, 0, k);
+  for (int s = 0; s < nst - 2; s += 2) {
+    stage(s, r0, r1);
+    stage(s + 1, r1, r0);
+  }
+  stage(nst - 2, r0, r1);
+  compute(r1);
+  __syncthreads();
+
+  // Epilogue. Lane (r, grp) of tile (i, j) holds rows 4*grp + e of column r.
+  const int row0 = tile_m0 * 16 + wm * (TM * 16);
+  if constexpr (EPI == EPI_STORE_F32 || EPI == EPI_RESID) {
+    if (p_ksplit(p) > 1) {
+      // K slice z: fp32 partial tile, summed in slice order by splitk_reduce_kernel.
+      float* part = p.part + (int64_t)z * p.M * p.N;
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const int n = (tile_n0 + wn * TN + j) * 16 + r;
+          if (n >= p.N) continue;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int m = row0 + 16 * i + 4 * grp + e;
+            if (m < p.M) part[(int64_t)m * p.N + n] = acc[i][j][e];
+          }
+        }
+      return;
+    }
+  }
+  if constexpr (EPI == EPI_ARGMAX) {
+    // The ring is free after the loop: it holds the per-wave row keys.
+    static_assert((int64_t)BM * WGN * 8 <= (int64_t)NS * SF * 64 * 16, "key scratch");
+    unsigned long long* kred = reinterpret_cast<unsigned long long*>(&lds[0][0][0]);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int m = row0 + 16 * i + 4 * grp + e;
+        unsigned long long key = 0ull;
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const int n = (tile_n0 + wn * TN + j) * 16 + r;
+          if (n < p.N) {
+            if (p.logits && m < p.M) p.logits[(int64_t)m * p.logits_stride + n] = acc[i][j][e];
+            const unsigned long long k = argmax_key(acc[i][j][e], (unsigned)n);
+            key = k > key ? k : key;
+          }
+        }
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) {
+          const unsigned long long other = __shfl_xor(key, o);
+          key = other > key ? other : key;
+        }
+        if (r == 0) kred[(wm * TM * 16 + 16 * i + 4 * grp + e) * WGN + wn] = key;
+      }
+    }
+    __syncthreads();
+    for (int row = threadIdx.x; row < BM; row += 64 * NW) {
+      const int m = tile_m0 * 16 + row;
+      if (m < p.M) {
+        unsigned long long best = 0ull;
+#pragma unroll
+        for (int w = 0; w < WGN; ++w) {
+          const unsigned long long k = kred[row * WGN + w];
+          best = k > best ? k : best;
+        }
+        p.amax[(int64_t)m * p.amax_stride + cb] = best;
+      }
+    }
+  } else if constexpr (SW) {
+    bf16* out = reinterpret_cast<bf16*>(p.out);
+    const int out_nck = (p.N + kKC - 1) / kKC;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN / 2; ++j) {
+        const int n = (tile_n0 + wn * (TN / 2) + j) * 16 + r;
+        if (n >= p.N) continue;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int m = row0 + 16 * i + 4 * grp + e;
+          if (m < p.M) {
+            const float gt = acc[i][j][e];
+            const float silu = gt / (1.0f + __expf(-gt));
+            out[tiled_index<bf16>(m, n, out_nck)] = (bf16)(silu * acc[i][j + TN / 2][e]);
+          }
+        }
+      }
+  } else if constexpr (EPI == EPI_STORE_F32) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int n = (tile_n0 + wn * TN + j) * 16 + r;
+        if (n >= p.N) continue;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int m = row0 + 16 * i + 4 * grp + e;
+          if (m < p.M) reinterpret_cast<float*>(p.out)[(int64_t)m * p.out_stride + n] = acc[i][j][e];
+        }
+      }
+  } else {
+    resid_add_tiles<TM, TN>(p, acc, row0, (tile_n0 + wn * TN) * 16 + r, grp);
   }
 }
 
@@ -375,65 +626,84 @@ static int mfma_colblocks(int epi, int N, int BN) {
   return (N + cols - 1) / cols;
 }
 
-// Block shapes, largest first: 256x256 (8 waves of 128x64), 256x192 (8 waves
-// of 64x96), 128x128 (4 waves of 64x64), 128x96 (4 waves of 64x48). Bigger
-// blocks read fewer operand bytes per flop; smaller ones fill the 256 CUs at
-// fewer rows or columns. `eff` is each shape's measured throughput per busy CU
-// relative to 256x256 (gate/up and QKV at 512 rows on MI355X).
+// Block shapes, largest first: 256x256 (8 waves of 128x64, pipelined),
+// 256x192 (8 waves of 64x96, pipelined), 128x128 (4 waves of 64x64), 128x96
+// (4 waves of 64x48). Bigger blocks read fewer operand bytes per flop;
+// smaller ones fill the 256 CUs at fewer rows or columns. `tflops` is each
+// shape's measured throughput per CU with every CU busy (MI355X, bf16, 256 -
+// 2048 rows); with fewer CUs busy the chip clocks higher, ~35% more per CU
+// when almost all are idle.
 struct MfmaShape {
   int bm, bn;
-  double eff;
+  bool pipe;
+  double tflops;
 };
-static const MfmaShape kShapes[4] = {{256, 256, 1.0}, {256, 192, 0.92}, {128, 128, 0.75},
-                                     {128, 96, 0.70}};
+static const MfmaShape kShapes[4] = {{256, 256, true, 5.0}, {256, 192, true, 4.75},
+                                     {128, 128, false, 3.15}, {128, 96, false, 2.75}};
 
-// K slices for a 128x128 fp32-store / residual projection that leaves most
-// CUs without a block (<= 128 blocks: O, down and the fusion at a few hundred
-// rows, QKV at 256): as many slices as fit 256 blocks, each keeping >= 8
-// stages of K. The partial tiles cost one extra fp32 pass (M x N x 4 B per
-// slice, written and read once).
-static int ksplit_128(int epi, int M, int N, int K) {
-  if (epi != EPI_STORE_F32 && epi != EPI_RESID) return 1;
-  const long long blocks = (long long)((M + 127) / 128) * ((N + 127) / 128);
-  if (blocks > 128) return 1;
-  int ks = 1;
-  while (ks < 4 && blocks * ks * 2 <= 256 && K / (64 * ks * 2) >= 8) ks *= 2;
-  return ks;
+// Whether a shape can take K slices of ks: fp32-store / residual epilogues
+// only (slices write fp32 partials that splitk_reduce_kernel sums in order);
+// the pipelined kernel needs an even number (>= 8) of k=32 stages per slice,
+// the 4-wave one >= 8 stages of k = 64.
+static bool ksplit_ok(const MfmaShape& sh, int epi, int K, int ks) {
+  if (ks == 1) return true;
+  if (epi != EPI_STORE_F32 && epi != EPI_RESID) return false;
+  if (sh.pipe) return (K / 32) % (2 * ks) == 0 && K / 32 / ks >= 8;
+  return (K / 64) % ks == 0 && K / 64 / ks >= 8;
 }
 
-// The shape with the least estimated time: whole rounds of 256 workgroups
-// times the work of one block (a K slice of it when 128x128 is split) over its
-// efficiency. SwiGLU needs an even number of column tiles per wave (not
-// 128x96); the LM-head argmax keeps square blocks. Ties go to the larger block.
-static int mfma_shape(int epi, int M, int N, int K) {
-  int best = 0;
+// Estimated time (us) of one launch: rounds of up to 256 workgroups, each
+// block of bm x bn x K/ks at the shape's rate per CU (raised when the round
+// leaves CUs idle), plus the fp32 output traffic at ~5 TB/s: the residual's
+// read-modify-write (latency-bound at the end of a block: counted 3x), or
+// with K slices the partials (written, then read by the reduce) and the
+// reduce's output, plus its launch.
+static double mfma_time_us(const MfmaShape& sh, int epi, int M, int N, int K, int ks) {
+  const long long wgs = (long long)((M + sh.bm - 1) / sh.bm) * mfma_colblocks(epi, N, sh.bn) * ks;
+  const double block_mflop = 2.0 * sh.bm * sh.bn * ((double)K / ks) * 1e-6;
+  double t = 0;
+  for (long long left = wgs; left > 0; left -= 256) {
+    const double busy = (double)(left < 256 ? left : 256);
+    t += block_mflop / (sh.tflops * (1.0 + 0.35 * (1.0 - busy / 256.0)));
+  }
+  const double out_mb = (double)M * N * 4 * 1e-6;
+  if (ks > 1) t += (2.0 * ks + (epi == EPI_RESID ? 2.0 : 1.0)) * out_mb / 5.0 + 2.0;
+  else t += (epi == EPI_RESID ? 3.0 : epi == EPI_STORE_F32 ? 1.0 : 0.0) * out_mb / 5.0;
+  return t;
+}
+
+struct MfmaPlan {
+  int shape, ksplit;
+};
+// The shape and K split with the least estimated time. SwiGLU needs an even
+// number of column tiles per wave (not 128x96); the LM-head argmax keeps
+// square blocks. Ties go to the larger block and fewer slices.
+static MfmaPlan mfma_plan(int epi, int M, int N, int K) {
+  MfmaPlan best{0, 1};
   double best_t = 1e300;
   for (int i = 0; i < 4; ++i) {
     const MfmaShape& sh = kShapes[i];
     if (epi == EPI_SWIGLU && sh.bn == 96) continue;
     if (epi == EPI_ARGMAX && sh.bm != sh.bn) continue;
-    const int ks = (sh.bm == 128 && sh.bn == 128) ? ksplit_128(epi, M, N, K) : 1;
-    const long long wgs =
-        (long long)((M + sh.bm - 1) / sh.bm) * mfma_colblocks(epi, N, sh.bn) * ks;
-    // the LM head's 256x256 blocks issue their loads early: 1.25x measured
-    const double eff = sh.eff * (epi == EPI_ARGMAX && sh.bm == 256 ? 1.25 : 1.0);
-    const double t = (double)((wgs + 255) / 256) * sh.bm * sh.bn / (ks * eff);
-    if (t < best_t * 0.999) {
-      best_t = t;
-      best = i;
+    if (sh.pipe && (K / 32) % 2) continue;
+    for (int ks = 1; ks <= kMfmaMaxSplit; ks *= 2) {
+      if (ks > 1 && (int64_t)M * N > kMfmaSplitMaxElems) break;
+      if (!ksplit_ok(sh, epi, K, ks)) continue;
+      const double t = mfma_time_us(sh, epi, M, N, K, ks);
+      if (t < best_t * 0.999) {
+        best_t = t;
+        best = MfmaPlan{i, ks};
+      }
     }
   }
   return best;
 }
 
 int mfma_gemm_colblocks(int epi, int M, int N, int K) {
-  return mfma_colblocks(epi, N, kShapes[mfma_shape(epi, M, N, K)].bn);
+  return mfma_colblocks(epi, N, kShapes[mfma_plan(epi, M, N, K).shape].bn);
 }
 
-int mfma_gemm_ksplit(int epi, int M, int N, int K) {
-  const MfmaShape& sh = kShapes[mfma_shape(epi, M, N, K)];
-  return (sh.bm == 128 && sh.bn == 128) ? ksplit_128(epi, M, N, K) : 1;
-}
+int mfma_gemm_ksplit(int epi, int M, int N, int K) { return mfma_plan(epi, M, N, K).ksplit; }
 
 // Sum of the K-slice partials in slice order, then the projection's epilogue:
 // out = sum (EPI_STORE_F32) or resid += sum (EPI_RESID). Four columns per thread.
@@ -466,43 +736,71 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
   }
 }
 
-template <int BM, int BN, int WGM, int WGN, int KF, int NS, int EPI, bool EARLY = false>
+// Sums the K slices' partials into the projection's output (launched after
+// the GEMM on the same stream).
+static hipError_t launch_splitk_reduce(int epi, const GemmArgs& a, hipStream_t st) {
+  float* dst = epi == EPI_RESID ? a.resid : reinterpret_cast<float*>(a.out);
+  const int64_t n4 = (int64_t)a.M * a.N / 4;
+  const int blocks = (int)std::min<int64_t>((n4 + 255) / 256, 4096);
+  hipLaunchKernelGGL(splitk_reduce_kernel, dim3(blocks), dim3(256), 0, st, a.part, a.ksplit, a.M,
+                     a.N, dst, a.out_stride, epi == EPI_RESID ? 1 : 0);
+  return hipGetLastError();
+}
+
+// The K split the plan asks for, if the caller's partial buffer and the
+// output layout allow it (else 1).
+static int usable_ksplit(int epi, const GemmArgs& a) {
+  if (epi != EPI_STORE_F32 && epi != EPI_RESID) return 1;
+  const int ks = mfma_gemm_ksplit(epi, a.M, a.N, a.K);
+  if (ks > 1 && a.part && a.part_elems >= (int64_t)ks * a.M * a.N && a.N % 4 == 0 &&
+      a.out_stride % 4 == 0)
+    return ks;
+  return 1;
+}
+
+template <int BM, int BN, int WGM, int WGN, int KF, int NS, int EPI>
 static hipError_t launch_mfma_t(const GemmArgs& a0, hipStream_t st) {
   GemmArgs a = a0;
-  a.ksplit = 1;
-  if constexpr (EPI == EPI_STORE_F32 || EPI == EPI_RESID) {
-    const int ks = mfma_gemm_ksplit(EPI, a.M, a.N, a.K);
-    if (ks > 1 && a.part && a.part_elems >= (int64_t)ks * a.M * a.N && a.N % 4 == 0 &&
-        a.out_stride % 4 == 0)
-      a.ksplit = ks;
-  }
+  a.ksplit = usable_ksplit(EPI, a);
   const int n_colblk = mfma_colblocks(EPI, a.N, BN);
   const int n_rowblk = (a.M + BM - 1) / BM;
   const int groups = (n_colblk + 7) / 8;
   const dim3 grid(groups * 8 * n_rowblk * a.ksplit), block(64 * WGM * WGN);
-  hipLaunchKernelGGL((gemm_mfma_kernel<BM, BN, WGM, WGN, KF, NS, EPI, EARLY>), grid, block, 0, st,
+  hipLaunchKernelGGL((gemm_mfma_kernel<BM, BN, WGM, WGN, KF, NS, EPI>), grid, block, 0, st,
                      a, n_colblk, n_rowblk);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.ksplit == 1) return e;
-  float* dst = EPI == EPI_RESID ? a.resid : reinterpret_cast<float*>(a.out);
-  const int64_t n4 = (int64_t)a.M * a.N / 4;
-  const int blocks = (int)std::min<int64_t>((n4 + 255) / 256, 4096);
-  hipLaunchKernelGGL(splitk_reduce_kernel, dim3(blocks), dim3(256), 0, st, a.part, a.ksplit, a.M,
-                     a.N, dst, a.out_stride, EPI == EPI_RESID ? 1 : 0);
-  return hipGetLastError();
+  return launch_splitk_reduce(EPI, a, st);
+}
+
+template <int BM, int BN, int WGM, int WGN, int NS, int EPI>
+static hipError_t launch_pipe_t(const GemmArgs& a0, hipStream_t st) {
+  GemmArgs a = a0;
+  a.ksplit = usable_ksplit(EPI, a);
+  if ((a.K / 32) % (2 * a.ksplit)) return hipErrorInvalidValue;
+  const int n_colblk = mfma_colblocks(EPI, a.N, BN);
+  const int n_rowblk = (a.M + BM - 1) / BM;
+  const int groups = (n_colblk + 7) / 8;
+  const dim3 grid(groups * 8 * n_rowblk * a.ksplit), block(64 * WGM * WGN);
+  hipLaunchKernelGGL((gemm_pipe_kernel<BM, BN, WGM, WGN, NS, EPI>), grid, block, 0, st, a,
+                     n_colblk, n_rowblk);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.ksplit == 1) return e;
+  return launch_splitk_reduce(EPI, a, st);
 }
 
 template <int EPI>
 static hipError_t launch_mfma_epi(const GemmArgs& a, hipStream_t st) {
-  // Stages of k = 64 in 2 slots for the 8-wave shapes (64 / 56 KB each), in
-  // 4 slots for the 4-wave ones (32 / 28 KB): measured best at these shapes.
-  switch (mfma_shape(EPI, a.M, a.N, a.K)) {
+  // Pipelined shapes: 4 ring slots of k = 32 for the LM head (128 KB; its
+  // weights stream from HBM once), 3 for the others (96 / 84 KB); the 4-wave
+  // shapes keep stages of k = 64 in 4 slots (32 / 28 KB each).
+  switch (mfma_plan(EPI, a.M, a.N, a.K).shape) {
     case 0:
-      if constexpr (EPI == EPI_ARGMAX) return launch_mfma_t<256, 256, 2, 4, 2, 2, EPI, true>(a, st);
-      else return launch_mfma_t<256, 256, 2, 4, 2, 2, EPI>(a, st);
+      if constexpr (EPI == EPI_ARGMAX) return launch_pipe_t<256, 256, 2, 4, 4, EPI>(a, st);
+      else return launch_pipe_t<256, 256, 2, 4, 3, EPI>(a, st);
     case 1:
       if constexpr (EPI == EPI_ARGMAX) return hipErrorInvalidValue;
-      else return launch_mfma_t<256, 192, 4, 2, 2, 2, EPI>(a, st);
+      else return launch_pipe_t<256, 192, 4, 2, 3, EPI>(a, st);
     case 2: return launch_mfma_t<128, 128, 2, 2, 2, 4, EPI>(a, st);
     default:
       if constexpr (EPI == EPI_ARGMAX || EPI == EPI_SWIGLU) return hipErrorInvalidValue;

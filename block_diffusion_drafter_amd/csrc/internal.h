@@ -78,6 +78,12 @@ inline bool gemm_uses_mfma(int dtype, int M, int K, bool a_tiled) {
   return dtype == DFLASH_BF16 && a_tiled && M >= kMfmaMinRows && K % 64 == 0;
 }
 hipError_t launch_gemm_mfma(int epi, const GemmArgs& a, hipStream_t st);
+// K splits of the MFMA path: at most kMfmaMaxSplit slices, and only for
+// outputs of at most kMfmaSplitMaxElems elements (larger ones fill the chip
+// without), so the partials of any row count up to M never exceed
+// kMfmaMaxSplit * min(M * N, kMfmaSplitMaxElems) floats.
+constexpr int kMfmaMaxSplit = 4;
+constexpr int64_t kMfmaSplitMaxElems = (int64_t)1 << 22;
 int mfma_gemm_colblocks(int epi, int M, int N, int K);
 // K slices the MFMA kernel splits a projection into (1 = no split); the
 // partial buffer it then needs is ksplit * M * N floats.
