@@ -27,6 +27,7 @@
 //   attn_combine: merges the segments of the sequences that span several
 //     workgroups.
 #include <climits>
+#include <type_traits>
 
 #include "common.h"
 #include "internal.h"
@@ -385,17 +386,24 @@ __device__ __forceinline__ void attn_wait_barrier() {
 // V), copied by direct global->LDS loads split over the waves; each load's
 // lanes gather exactly the 16-byte pieces the MFMA operand layout wants, so a
 // wave reads every fragment back as 64 lanes x 16 contiguous bytes. NSB ring
-// slots keep NSB-1 blocks in flight per group with no staging registers; 3
-// slots (48 KB at head_dim 128) leave room for several groups per CU, which
-// measured better than deeper rings with fewer groups.
-template <int HD, int G, int NSB = 3>
-__global__ __launch_bounds__(64 * G) void attn_partial_lds_kernel(AttnArgs p) {
+// slots keep NSB-1 blocks in flight per group with no staging registers.
+// Every step issues a block (past the end: the last one again, into a slot
+// nobody reads any more), so the wait counts are constants and the loop has
+// no branches; only the sequence's final block (a partial one) and
+// sliding-window layers apply the key masks. The softmax rescale is lazy: the running reference max moves
+// only when a block's max exceeds it by more than 2^8 (probabilities stay
+// <= 256, exact for the final normalisation), so the output accumulators are
+// rarely touched outside the MFMAs.
+template <int HD, int G, int NSB = 4>
+__global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_partial_lds_kernel(AttnArgs p) {
   using T = bf16;
   using KB = KVBlock<T, HD>;
   constexpr int EPF = KB::EPF, FR = KB::FR, NDT = KB::NDT;
   constexpr int NI = 2 * FR + NDT;  // fragments per block
   constexpr int IPW = NI / G;       // fragments each wave copies per block
   static_assert(NI % G == 0, "block fragments must split evenly over the group");
+  static_assert(NSB >= 3, "a slot being read, one arriving, one being filled");
   __shared__ u32x4 ring[NSB][NI][64];
 
   const int lane = threadIdx.x & 63;
@@ -419,26 +427,38 @@ __global__ __launch_bounds__(64 * G) void attn_partial_lds_kernel(AttnArgs p) {
   const T* K = reinterpret_cast<const T*>(p.k) + kvoff;
   const T* V = reinterpret_cast<const T*>(p.v) + kvoff;
 
-  // Fragment i of block n (key base kb, a multiple of 32 below cap, so every
-  // address stays inside the sequence's cache rows): i < 2*FR is K tile i/FR,
-  // fragment i%FR: lane (r, grp) takes key kb + key_of(t, r), channels
-  // [4*EPF*f + EPF*grp, +EPF). Else V channel tile dt = i - 2*FR: lane (r, grp)
-  // takes channel 16 dt + r, keys 8 grp .. 8 grp + 7 of the block.
-  auto issue = [&](int n, int slot) {
-    const int kb = k_lo + 32 * n;
+  // Fragment i of block n (key base kb = k_lo + 32 n, a multiple of 32 below
+  // cap, so every address stays inside the sequence's cache rows): i < 2*FR
+  // is K tile i/FR, fragment i%FR: lane (r, grp) takes key kb + key_of(t, r),
+  // channels [4*EPF*f + EPF*grp, +EPF). Else V channel tile dt = i - 2*FR:
+  // lane (r, grp) takes channel 16 dt + r, keys 8 grp .. 8 grp + 7 of the
+  // block. Either way block n's fragment is block 0's plus n * 32 * HD
+  // elements, so each wave's sources are set up once per segment.
+  const T* src[IPW];
 #pragma unroll
-    for (int u = 0; u < IPW; ++u) {
-      const int i = j + G * u;
-      const T* src;
-      if (i < 2 * FR) {
-        const int t = i / FR, f = i % FR;
-        src = K + (size_t)(kb + key_of<T>(t, r)) * HD + f * 4 * EPF + grp * EPF;
-      } else {
-        const int dt = i - 2 * FR;
-        src = V + (size_t)(kb / kKeyBlock) * HD * kKeyBlock + (16 * dt + r) * kKeyBlock + 8 * grp;
-      }
-      __builtin_amdgcn_global_load_lds((attn_gbl_ptr)src, (attn_lds_ptr)&ring[slot][i][0], 16, 0, 0);
+  for (int u = 0; u < IPW; ++u) {
+    const int i = j + G * u;
+    if (i < 2 * FR) {
+      const int t = i / FR, f = i % FR;
+      src[u] = K + (size_t)(k_lo + key_of<T>(t, r)) * HD + f * 4 * EPF + grp * EPF;
+    } else {
+      const int dt = i - 2 * FR;
+      src[u] = V + (size_t)(k_lo / kKeyBlock) * HD * kKeyBlock + (16 * dt + r) * kKeyBlock + 8 * grp;
     }
+  }
+  auto issue = [&](int n, int slot) {
+#pragma unroll
+    for (int u = 0; u < IPW; ++u)
+      __builtin_amdgcn_global_load_lds((attn_gbl_ptr)(src[u] + (size_t)n * 32 * HD),
+                                       (attn_lds_ptr)&ring[slot][j + G * u][0], 16, 0, 0);
+  };
+  auto read_block = [&](KB& b, int slot) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int f = 0; f < FR; ++f) b.k[t][f] = ring[slot][t * FR + f][lane];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) b.v[dt][0] = ring[slot][2 * FR + dt][lane];
   };
 
   const int k_min = query_first(p, s, r);
@@ -452,103 +472,138 @@ __global__ __launch_bounds__(64 * G) void attn_partial_lds_kernel(AttnArgs p) {
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) S.o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Ring: before block n is read, every wave has waited for its own loads of
-  // it and passed the barrier; the barrier after block n's reads frees its
-  // slot for block n + NSB.
-#pragma unroll
-  for (int n = 0; n < NSB; ++n)
-    if (n < nblk) issue(n, n);
-  if (nblk >= NSB) attn_wait_barrier<IPW * (NSB - 1)>();
-  else attn_wait_barrier<0>();
-  for (int n = 0; n < nblk; ++n) {
-    const int slot = n % NSB;
+  // One block's update. Scores outside [k_min, k_hi) are masked (a handful
+  // of compares; only the final block and sliding-window layers have any).
+  auto update = [&](const KB& b, int n) {
     const int kb = k_lo + 32 * n;
-    KB b;
+    f32x4 st[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      st[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int f = 0; f < FR; ++f) st[t] = mfma_frag<T>(b.k[t][f], qf[f], st[t]);
+    }
+    float mx = -INFINITY;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int f = 0; f < FR; ++f) b.k[t][f] = ring[slot][t * FR + f][lane];
+      for (int i = 0; i < 4; ++i) {
+        const int key = kb + key_of<T>(t, 4 * grp + i);
+        const float v = (key < k_hi && key >= k_min) ? st[t][i] * p.scale_log2 : -INFINITY;
+        st[t][i] = v;
+        mx = fmaxf(mx, v);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    if (__any(mx > S.m_run + 8.0f)) {
+      const float m_new = fmaxf(S.m_run, mx);
+      // m_new stays -inf while a query has seen no key (sliding window)
+      const float alpha = m_new == -INFINITY ? 1.0f : exp2f(S.m_run - m_new);
+      S.m_run = m_new;
+      S.l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) S.o[dt] *= alpha;
+    }
+    const float m_ref = S.m_run == -INFINITY ? 0.f : S.m_run;
+    float psum = 0.f;
+    bf16x8 phi, plo;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        // v_exp_f32: the argument is <= 8; tiny results may flush to 0
+        const float pv = __builtin_amdgcn_exp2f(st[t][i] - m_ref);
+        psum += pv;
+        const bf16 hi = (bf16)pv;
+        phi[4 * t + i] = hi;
+        plo[4 * t + i] = (bf16)(pv - (float)hi);
+      }
+    S.l_run += psum;
+    // P as the sum of two bf16 parts (16 significant bits): the products with
+    // the bf16 values are then as exact as the fp32 sum of probabilities they
+    // are normalised by. Two MFMAs per tile cost nothing here: the kernel
+    // waits on HBM.
+    const u32x4 pf = __builtin_bit_cast(u32x4, phi), pl = __builtin_bit_cast(u32x4, plo);
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
-      u32x4 x = ring[slot][2 * FR + dt][lane];
-      // Positions past the last key may hold anything (even NaN bit patterns);
-      // their probabilities are 0, so their values must be 0 too.
-      if (kb + 32 > k_hi) x = keep_first<T>(x, k_hi - (kb + 8 * grp));
-      b.v[dt][0] = x;
+      S.o[dt] = mfma_frag<T>(b.v[dt][0], pf, S.o[dt]);
+      S.o[dt] = mfma_frag<T>(b.v[dt][0], pl, S.o[dt]);
     }
-    attn_update<T, HD>(S, b, qf, kb, k_hi, k_min, p.scale_log2, grp);
-    if (n + 1 < nblk) {
-      if (n + NSB <= nblk) attn_wait_barrier<IPW * (NSB - 2)>();
-      else attn_wait_barrier<0>();
-      if (n + NSB < nblk) issue(n + NSB, slot);
+  };
+
+  // Block n: wait until it has landed and every wave is done with block n-1,
+  // refill block n-1's slot with block n-1+NSB, read block n from LDS and
+  // multiply it (the other waves on the SIMD cover the LDS latency).
+#pragma unroll
+  for (int n = 0; n < NSB; ++n) issue(min(n, nblk - 1), n);
+  attn_wait_barrier<IPW * (NSB - 1)>();
+  KB b;
+  for (int n = 0; n < nblk; ++n) {
+    if (n > 0) {
+      attn_wait_barrier<IPW * (NSB - 2)>();
+      issue(min(n - 1 + NSB, nblk - 1), (n - 1) % NSB);
     }
+    read_block(b, n % NSB);
+    if (n == nblk - 1 && k_lo + 32 * n + 32 > k_hi) {
+      // Positions past the last key may hold anything (even NaN bit
+      // patterns); their probabilities are 0, so their values must be 0 too.
+      const int kb = k_lo + 32 * n;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) b.v[dt][0] = keep_first<T>(b.v[dt][0], k_hi - (kb + 8 * grp));
+    }
+    update(b, n);
   }
+  // The ring's trailing loads land before its slots are reused (or the
+  // workgroup's LDS is released).
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   attn_finish<T, HD>(S, p, s, g, part_entry(p, g, w, s), j, G, single, r, grp);
   });
 }
 
-// Merge of the segment partials of one (query head, sequence, 16-channel
-// slice). Thread (q, cg) owns query row q and the segments c = cg, cg + 16,
-// ...: it reduces the row's running max and sum over its segments, the 16
-// threads of a row combine them through LDS, then each thread accumulates its
-// segments' weighted partial outputs for the slice's 16 channels and LDS sums
-// the 16 segment groups. Every thread's loads are independent of each other.
-template <typename T, int HD>
-__global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs p) {
-  __shared__ float red_m[16][17], red_l[16][17];
-  __shared__ float red_o[16][16][17];
-  const int h = blockIdx.x, s = blockIdx.y, slice = blockIdx.z;
+// Merge of the segment partials of the sequences that span several
+// workgroups: one workgroup per (KV head, sequence, channel slice), one wave
+// per query head of the group; lane (q, c) owns query q and CPL consecutive
+// channels of the slice (4 * CPL channels). The block prefix is built once
+// per workgroup and a sequence in one piece returns at once. Every lane reads
+// the segments' (max, sum) of its query, then their partial outputs, in
+// segment order (loads independent of each other), and writes its normalised
+// channels. Few (KV head, sequence) pairs with many segments each (batch 1)
+// take narrow slices, so more workgroups share the reads.
+template <typename T, int HD, int CPL>
+__global__ __launch_bounds__(512) void attn_combine_kernel(AttnArgs p) {
+  const int g = blockIdx.x, s = blockIdx.y, slice = blockIdx.z;
   const int G = p.n_heads / p.n_kv_heads;
-  const int g = h / G, j = h % G;
   extern __shared__ int pre[];
   seq_block_prefix(p, pre);
   const KeySplit ks = key_split(p, pre);
   const int w0 = ks.owner(pre[s]), w1 = ks.owner(pre[s + 1] - 1);
   if (w0 == w1) return;  // one segment: written by the partial kernel
-  // Segments c = 0 .. nch-1 come from workgroups w0 + c (every one in between
-  // has a non-empty range since nw <= tb), at entries w0 + c + s.
   const int nch = w1 - w0 + 1;
-  const int t = threadIdx.x, q = t & 15, cg = t >> 4;
-  const size_t item0 = part_entry(p, g, w0, s) * G + j;
-  float m = -INFINITY;
-  for (int c = cg; c < nch; c += 16) m = fmaxf(m, p.part_ml[((item0 + (size_t)c * G) * 16 + q) * 2]);
-  red_m[q][cg] = m;
-  __syncthreads();
+  const int t = threadIdx.x, j = t >> 6, q = t & 15, c = (t >> 4) & 3;
+  if (q >= p.block) return;
+  const size_t e0 = part_entry(p, g, w0, s);  // segment k is entry e0 + k
   float M = -INFINITY;
+#pragma unroll 4
+  for (int k = 0; k < nch; ++k) M = fmaxf(M, p.part_ml[(((e0 + k) * G + j) * 16 + q) * 2]);
+  const int ch0 = 4 * CPL * slice + CPL * c;
+  float L = 0.f, o[CPL];
 #pragma unroll
-  for (int k = 0; k < 16; ++k) M = fmaxf(M, red_m[q][k]);
-  float l = 0.f;
-  for (int c = cg; c < nch; c += 16) {
-    const float* ml = p.part_ml + ((item0 + (size_t)c * G) * 16 + q) * 2;
-    l += ml[1] * exp2f(ml[0] - M);
+  for (int i = 0; i < CPL; ++i) o[i] = 0.f;
+#pragma unroll 2
+  for (int k = 0; k < nch; ++k) {
+    const size_t item = (e0 + k) * G + j;
+    const float wk = exp2f(p.part_ml[(item * 16 + q) * 2] - M);
+    L += p.part_ml[(item * 16 + q) * 2 + 1] * wk;
+    const float* po = p.part_o + (item * HD + ch0) * 16 + q;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) o[i] += po[i * 16] * wk;
   }
-  red_l[q][cg] = l;
-  __syncthreads();
-  float L = 0.f;
-#pragma unroll
-  for (int k = 0; k < 16; ++k) L += red_l[q][k];
   const float inv = 1.0f / L;
-  float acc[16];
+  T* out = reinterpret_cast<T*>(p.out);
+  const int row = s * p.block + q, h = g * G + j;
 #pragma unroll
-  for (int k = 0; k < 16; ++k) acc[k] = 0.f;
-  for (int c = cg; c < nch; c += 16) {
-    const size_t it = item0 + (size_t)c * G;
-    const float w = exp2f(p.part_ml[(it * 16 + q) * 2] - M) * inv;
-    const float* po = p.part_o + (it * HD + 16 * slice) * 16 + q;
-#pragma unroll
-    for (int k = 0; k < 16; ++k) acc[k] += po[k * 16] * w;
-  }
-#pragma unroll
-  for (int k = 0; k < 16; ++k) red_o[k][cg][q] = acc[k];
-  __syncthreads();
-  // thread (q, d = cg) sums the 16 chunk groups of channel 16*slice + d
-  if (q < p.block) {
-    float o = 0.f;
-#pragma unroll
-    for (int k = 0; k < 16; ++k) o += red_o[cg][k][q];
-    T* out = reinterpret_cast<T*>(p.out);
-    out[tiled_index<T>(s * p.block + q, h * HD + 16 * slice + cg, p.out_nck)] = from_f32<T>(o);
-  }
+  for (int i = 0; i < CPL; ++i)
+    out[tiled_index<T>(row, h * HD + ch0 + i, p.out_nck)] = from_f32<T>(o[i] * inv);
 }
 
 template <typename T, int HD>
@@ -571,8 +626,12 @@ static hipError_t launch_hd(const AttnArgs& a, hipStream_t st) {
   if (e != hipSuccess || a.wg_per_head <= 1) return e;
   prof_end(st);
   prof_begin(DFLASH_K_ATTN_COMBINE, 0.0, 0.0, st);
-  hipLaunchKernelGGL((attn_combine_kernel<T, HD>), dim3(a.n_heads, a.batch, HD / 16), dim3(256),
-                     pre_bytes, st, a);
+  if (a.n_kv_heads * a.batch >= 64)
+    hipLaunchKernelGGL((attn_combine_kernel<T, HD, 8>), dim3(a.n_kv_heads, a.batch, HD / 32),
+                       dim3(64 * G), pre_bytes, st, a);
+  else
+    hipLaunchKernelGGL((attn_combine_kernel<T, HD, 2>), dim3(a.n_kv_heads, a.batch, HD / 8),
+                       dim3(64 * G), pre_bytes, st, a);
   return hipGetLastError();
 }
 
