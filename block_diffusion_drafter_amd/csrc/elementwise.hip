@@ -3,6 +3,8 @@
 // the cross-tile argmax reduction, greedy acceptance and the context-length
 // update. All are small next to the weight and cache streams; they are written
 // for coalesced row access and one pass over their data.
+#include <cmath>
+
 #include "common.h"
 #include "internal.h"
 
@@ -159,111 +161,153 @@ hipError_t launch_embed(int dtype, const void* embed, const int32_t* anchor, int
   return hipGetLastError();
 }
 
-// One wave normalises one head vector: lane l owns channels l and l + HD/2,
-// which is exactly one rotary pair.
-template <typename T, int HD>
-__device__ __forceinline__ void norm_rope_head(float x0, float x1, const T* gain, float eps,
-                                               float theta, int pos, int lane, float& o0,
-                                               float& o1) {
-  constexpr int HALF = HD / 2;
-  const float ss = wave_sum(x0 * x0 + x1 * x1);
-  const float inv = rsqrtf(ss / (float)HD + eps);
-  float y0 = 0.f, y1 = 0.f;
-  if (lane < HALF) {
-    y0 = x0 * inv * to_f32(gain[lane]);
-    y1 = x1 * inv * to_f32(gain[lane + HALF]);
-  }
-  if (theta > 0.f && lane < HALF) {
-    // Angle in double: positions reach tens of thousands of radians.
-    const double inv_freq = pow((double)theta, -2.0 * (double)lane / (double)HD);
-    const double ang = (double)pos * inv_freq;
-    double sn, cs;
-    sincos(ang, &sn, &cs);
-    const float c = (float)cs, s = (float)sn;
-    o0 = y0 * c - y1 * s;
-    o1 = y1 * c + y0 * s;
-  } else {
-    o0 = y0;
-    o1 = y1;
-  }
-}
-
-template <typename T, int HD>
-__device__ __forceinline__ void store_v(T* vbase, int pos, int lane, float x0, float x1) {
-  constexpr int HALF = HD / 2;
-  if (lane < HALF) {
-    T* blk = vbase + (size_t)(pos / kKeyBlock) * HD * kKeyBlock + (pos % kKeyBlock);
-    blk[(size_t)lane * kKeyBlock] = from_f32<T>(x0);
-    blk[(size_t)(lane + HALF) * kKeyBlock] = from_f32<T>(x1);
-  }
-}
-
-// Forward mode: grid (Hq + 2*Hkv, batch*16), one wave per (head, block slot).
-template <typename T, int HD>
-__global__ __launch_bounds__(64) void norm_rope_fwd_kernel(NormRopeArgs p) {
-  constexpr int HALF = HD / 2;
-  const int head = blockIdx.x, slot = blockIdx.y, s = slot / 16, i = slot % 16;
-  const int lane = threadIdx.x;
-  const int Hq = p.n_heads, Hkv = p.n_kv_heads;
-  if (head < Hq) {
-    T* qo = reinterpret_cast<T*>(p.q_out) + (((size_t)s * Hq + head) * 16 + i) * HD;
-    if (i >= p.block) {
-      if (lane < HALF) {
-        qo[lane] = from_f32<T>(0.f);
-        qo[lane + HALF] = from_f32<T>(0.f);
-      }
-      return;
+// Rotary pairs of one row: a head vector of HD channels is HD/2 pairs
+// (channel c with c + HD/2). A wave covers 64 / (HD/2) heads at once: lane
+// (sub, c) with c = lane % (HD/2) owns pair c of the iteration's head sub.
+// The rotation angle depends only on the position and the pair index, so
+// each lane computes its (cos, sin) once per row for all the heads it takes.
+// The angle pos * inv_freq is formed in double (positions reach tens of
+// thousands of radians), reduced by 2 pi in double (Cody-Waite: 2 pi as the
+// nearest double plus its remainder), and the reduced angle in [-pi, pi]
+// goes to the fp32 sincos.
+template <int HD>
+struct RopeLane {
+  static constexpr int PAIRS = HD / 2;
+  static constexpr int HPW = 64 / PAIRS;  // heads per wave iteration
+  float c = 1.f, s = 0.f;
+  __device__ RopeLane(const NormRopeArgs& p, int pos, int pair) {
+    if (p.rope_theta > 0.f) {
+      constexpr double kTwoPiHi = 6.283185307179586;         // nearest double to 2 pi
+      constexpr double kTwoPiLo = 2.4492935982947064e-16;    // 2 pi - kTwoPiHi
+      const double ang = (double)pos * p.inv_freq[pair];
+      const double k = rint(ang * (1.0 / kTwoPiHi));
+      const double r = fma(-k, kTwoPiLo, fma(-k, kTwoPiHi, ang));
+      sincosf((float)r, &s, &c);
     }
-  } else if (i >= p.block) {
+  }
+};
+
+// Sum over the PAIRS lanes of one head (lanes with the same `sub`).
+template <int PAIRS>
+__device__ __forceinline__ float head_sum(float v) {
+#pragma unroll
+  for (int o = PAIRS / 2; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// Per-head RMSNorm (gain g0, g1 of the lane's pair) and rotation of one pair.
+template <int HD>
+__device__ __forceinline__ void norm_rope_pair(float x0, float x1, float g0, float g1, float eps,
+                                               const RopeLane<HD>& r, float& o0, float& o1) {
+  const float ss = head_sum<HD / 2>(x0 * x0 + x1 * x1);
+  const float inv = rsqrtf(ss / (float)HD + eps);
+  const float y0 = x0 * inv * g0, y1 = x1 * inv * g1;
+  o0 = y0 * r.c - y1 * r.s;
+  o1 = y1 * r.c + y0 * r.s;
+}
+
+// Pair c of a V head row at position pos (V is stored in 32-position blocks,
+// channel-major inside a block).
+template <typename T, int HD>
+__device__ __forceinline__ void store_v(T* vbase, int pos, int c, float x0, float x1) {
+  T* blk = vbase + (size_t)(pos / kKeyBlock) * HD * kKeyBlock + (pos % kKeyBlock);
+  blk[(size_t)c * kKeyBlock] = from_f32<T>(x0);
+  blk[(size_t)(c + HD / 2) * kKeyBlock] = from_f32<T>(x1);
+}
+
+// Heads (or append columns) per workgroup: 4 waves x kNrIters iterations x
+// RopeLane::HPW heads per iteration. A wave loads all its heads' pairs
+// first, then normalises and stores them: one memory latency per wave.
+constexpr int kNrIters = 4;
+template <int HD>
+__host__ __device__ constexpr int nr_heads_per_wg() { return 4 * kNrIters * (64 / (HD / 2)); }
+
+// Forward mode: grid (batch * 16 block slots, head groups); workgroup
+// (slot, y) takes heads y * nr_heads_per_wg + (it * 4 + wave) * HPW + sub of
+// the row's Hq + 2*Hkv. Slots i >= block only zero-fill the padded Q rows.
+template <typename T, int HD>
+__global__ __launch_bounds__(256) void norm_rope_fwd_kernel(NormRopeArgs p) {
+  using RL = RopeLane<HD>;
+  const int slot = blockIdx.x, s = slot / 16, i = slot % 16;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int sub = lane / RL::PAIRS, c = lane % RL::PAIRS;
+  const int Hq = p.n_heads, Hkv = p.n_kv_heads, NH = Hq + 2 * Hkv;
+  const int hbase = blockIdx.y * nr_heads_per_wg<HD>() + wave * RL::HPW + sub;
+  if (i >= p.block) {
+#pragma unroll
+    for (int it = 0; it < kNrIters; ++it) {
+      const int h = hbase + it * 4 * RL::HPW;
+      if (h < Hq) {
+        T* qo = reinterpret_cast<T*>(p.q_out) + (((size_t)s * Hq + h) * 16 + i) * HD;
+        qo[c] = from_f32<T>(0.f);
+        qo[c + RL::PAIRS] = from_f32<T>(0.f);
+      }
+    }
     return;
   }
   const int m = s * p.block + i;
-  const float* src = p.src + (int64_t)m * p.src_stride + (int64_t)head * HD;
-  const float x0 = lane < HALF ? src[lane] : 0.f;
-  const float x1 = lane < HALF ? src[lane + HALF] : 0.f;
+  const float* src = p.src + (int64_t)m * p.src_stride;
+  float x0[kNrIters], x1[kNrIters];
+#pragma unroll
+  for (int it = 0; it < kNrIters; ++it) {
+    const int hc = min(hbase + it * 4 * RL::HPW, NH - 1);
+    x0[it] = src[hc * HD + c];
+    x1[it] = src[hc * HD + c + RL::PAIRS];
+  }
   int cl = p.ctx_len[s];
   cl = cl < 0 ? 0 : cl;
   const int pos = cl + i;
   const bool in_cap = pos < p.cap;
-  if (head >= Hq + Hkv) {
-    if (!in_cap) {
-      if (lane == 0 && p.dev_status) atomicOr(p.dev_status, DFLASH_DEV_CAPACITY);
-      return;
+  if (!in_cap && threadIdx.x == 0 && blockIdx.y == 0 && p.dev_status)
+    atomicOr(p.dev_status, DFLASH_DEV_CAPACITY);
+  const RL rope(p, pos, c);
+  const T* qg = reinterpret_cast<const T*>(p.q_norm[0]);
+  const T* kg = reinterpret_cast<const T*>(p.k_norm[0]);
+  const float qg0 = to_f32(qg[c]), qg1 = to_f32(qg[c + RL::PAIRS]);
+  const float kg0 = to_f32(kg[c]), kg1 = to_f32(kg[c + RL::PAIRS]);
+  // Every lane of an iteration takes part (the head sums shuffle across it);
+  // heads past the last were clamped and are not stored.
+#pragma unroll
+  for (int it = 0; it < kNrIters; ++it) {
+    const int h = hbase + it * 4 * RL::HPW;
+    const int hc = min(h, NH - 1);
+    const bool is_q = hc < Hq, is_v = hc >= Hq + Hkv;
+    float o0 = x0[it], o1 = x1[it];
+    if (!is_v)
+      norm_rope_pair<HD>(x0[it], x1[it], is_q ? qg0 : kg0, is_q ? qg1 : kg1, p.eps, rope, o0, o1);
+    if (h >= NH) continue;
+    if (is_q) {
+      T* qo = reinterpret_cast<T*>(p.q_out) + (((size_t)s * Hq + h) * 16 + i) * HD;
+      qo[c] = from_f32<T>(o0);
+      qo[c + RL::PAIRS] = from_f32<T>(o1);
+    } else if (in_cap) {
+      if (is_v) {
+        const int g = h - Hq - Hkv;
+        store_v<T, HD>(reinterpret_cast<T*>(p.v_cache) + (size_t)(s * Hkv + g) * p.cap * HD, pos,
+                       c, o0, o1);
+      } else {
+        const int g = h - Hq;
+        T* kr = reinterpret_cast<T*>(p.k_cache) + ((size_t)(s * Hkv + g) * p.cap + pos) * HD;
+        kr[c] = from_f32<T>(o0);
+        kr[c + RL::PAIRS] = from_f32<T>(o1);
+      }
     }
-    const int g = head - Hq - Hkv;
-    T* vbase = reinterpret_cast<T*>(p.v_cache) + (size_t)(s * Hkv + g) * p.cap * HD;
-    store_v<T, HD>(vbase, pos, lane, x0, x1);
-    return;
-  }
-  const bool is_q = head < Hq;
-  const T* gain = reinterpret_cast<const T*>(is_q ? p.q_norm[0] : p.k_norm[0]);
-  float o0, o1;
-  norm_rope_head<T, HD>(x0, x1, gain, p.eps, p.rope_theta, pos, lane, o0, o1);
-  if (lane >= HALF) return;
-  if (is_q) {
-    T* qo = reinterpret_cast<T*>(p.q_out) + (((size_t)s * Hq + head) * 16 + i) * HD;
-    qo[lane] = from_f32<T>(o0);
-    qo[lane + HALF] = from_f32<T>(o1);
-  } else {
-    if (!in_cap) {
-      if (lane == 0 && p.dev_status) atomicOr(p.dev_status, DFLASH_DEV_CAPACITY);
-      return;
-    }
-    const int g = head - Hq;
-    T* kr = reinterpret_cast<T*>(p.k_cache) + ((size_t)(s * Hkv + g) * p.cap + pos) * HD;
-    kr[lane] = from_f32<T>(o0);
-    kr[lane + HALF] = from_f32<T>(o1);
   }
 }
 
-// Append mode: grid (n_layers * 2 * Hkv, n_tok); column c = layer * 2*Hkv + h,
-// h < Hkv a key head, h >= Hkv a value head.
+// Append mode: grid (appended rows, column groups); column
+// col = layer * 2*Hkv + hh of the row (hh < Hkv a key head, else a value
+// head) is written to position ctx_len[s] + (row's index in its sequence) of
+// that layer's cache.
 template <typename T, int HD>
-__global__ __launch_bounds__(64) void norm_rope_append_kernel(NormRopeArgs p) {
-  constexpr int HALF = HD / 2;
-  const int col = blockIdx.x, row = blockIdx.y, lane = threadIdx.x;
-  const int Hkv = p.n_kv_heads;
-  const int l = col / (2 * Hkv), hh = col % (2 * Hkv);
+__global__ __launch_bounds__(256) void norm_rope_append_kernel(NormRopeArgs p) {
+  using RL = RopeLane<HD>;
+  const int row = blockIdx.x;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int sub = lane / RL::PAIRS, c = lane % RL::PAIRS;
+  const int Hkv = p.n_kv_heads, NC = p.n_layers * 2 * Hkv;
+  const int cbase = blockIdx.y * nr_heads_per_wg<HD>() + wave * RL::HPW + sub;
+  const bool flagger = threadIdx.x == 0 && blockIdx.y == 0;
   int s = -1, i = 0;
   if (p.accept_len) {
     // block rows: position i of sequence s, kept for i <= accept length
@@ -278,7 +322,7 @@ __global__ __launch_bounds__(64) void norm_rope_append_kernel(NormRopeArgs p) {
       }
     }
     if (s < 0) {
-      if (lane == 0 && p.dev_status) atomicOr(p.dev_status, DFLASH_DEV_OFFSETS);
+      if (flagger && p.dev_status) atomicOr(p.dev_status, DFLASH_DEV_OFFSETS);
       return;
     }
     i = row - p.cu_new[s];
@@ -287,47 +331,64 @@ __global__ __launch_bounds__(64) void norm_rope_append_kernel(NormRopeArgs p) {
   cl = cl < 0 ? 0 : cl;
   const int pos = cl + i;
   if (pos >= p.cap) {
-    if (lane == 0 && p.dev_status) atomicOr(p.dev_status, DFLASH_DEV_CAPACITY);
+    if (flagger && p.dev_status) atomicOr(p.dev_status, DFLASH_DEV_CAPACITY);
     return;
   }
-  const float* src = p.src + (int64_t)row * p.src_stride + (int64_t)col * HD;
-  const float x0 = lane < HALF ? src[lane] : 0.f;
-  const float x1 = lane < HALF ? src[lane + HALF] : 0.f;
+  const float* src = p.src + (int64_t)row * p.src_stride;
+  float x0[kNrIters], x1[kNrIters];
+#pragma unroll
+  for (int it = 0; it < kNrIters; ++it) {
+    const int cc = min(cbase + it * 4 * RL::HPW, NC - 1);
+    x0[it] = src[cc * HD + c];
+    x1[it] = src[cc * HD + c + RL::PAIRS];
+  }
+  const RL rope(p, pos, c);
   const size_t layer_stride = (size_t)p.cache_batch * Hkv * p.cap * HD;
-  if (hh >= Hkv) {
-    const int g = hh - Hkv;
-    T* vbase = reinterpret_cast<T*>(p.v_cache) + l * layer_stride + (size_t)(s * Hkv + g) * p.cap * HD;
-    store_v<T, HD>(vbase, pos, lane, x0, x1);
-    return;
+#pragma unroll
+  for (int it = 0; it < kNrIters; ++it) {
+    const int col = cbase + it * 4 * RL::HPW;
+    const int cc = min(col, NC - 1);
+    const int l = cc / (2 * Hkv), hh = cc % (2 * Hkv);
+    float o0 = x0[it], o1 = x1[it];
+    if (hh < Hkv) {
+      const T* kg = reinterpret_cast<const T*>(p.k_norm[l]);
+      norm_rope_pair<HD>(x0[it], x1[it], to_f32(kg[c]), to_f32(kg[c + RL::PAIRS]), p.eps, rope,
+                         o0, o1);
+    }
+    if (col >= NC) continue;
+    if (hh >= Hkv) {
+      const int g = hh - Hkv;
+      store_v<T, HD>(reinterpret_cast<T*>(p.v_cache) + l * layer_stride +
+                         (size_t)(s * Hkv + g) * p.cap * HD,
+                     pos, c, o0, o1);
+    } else {
+      T* kr = reinterpret_cast<T*>(p.k_cache) + l * layer_stride +
+              ((size_t)(s * Hkv + hh) * p.cap + pos) * HD;
+      kr[c] = from_f32<T>(o0);
+      kr[c + RL::PAIRS] = from_f32<T>(o1);
+    }
   }
-  const int g = hh;
-  float o0, o1;
-  norm_rope_head<T, HD>(x0, x1, reinterpret_cast<const T*>(p.k_norm[l]), p.eps, p.rope_theta, pos,
-                        lane, o0, o1);
-  if (lane >= HALF) return;
-  T* kr = reinterpret_cast<T*>(p.k_cache) + l * layer_stride + ((size_t)(s * Hkv + g) * p.cap + pos) * HD;
-  kr[lane] = from_f32<T>(o0);
-  kr[lane + HALF] = from_f32<T>(o1);
 }
 
 template <int MODE>
 static hipError_t launch_nr(int dtype, const NormRopeArgs& a, dim3 grid, hipStream_t st) {
   const bool bf = dtype == DFLASH_BF16;
+  const dim3 blk(256);
   if (a.head_dim == 128) {
     if (MODE == 0) {
-      if (bf) hipLaunchKernelGGL((norm_rope_fwd_kernel<bf16, 128>), grid, dim3(64), 0, st, a);
-      else hipLaunchKernelGGL((norm_rope_fwd_kernel<float, 128>), grid, dim3(64), 0, st, a);
+      if (bf) hipLaunchKernelGGL((norm_rope_fwd_kernel<bf16, 128>), grid, blk, 0, st, a);
+      else hipLaunchKernelGGL((norm_rope_fwd_kernel<float, 128>), grid, blk, 0, st, a);
     } else {
-      if (bf) hipLaunchKernelGGL((norm_rope_append_kernel<bf16, 128>), grid, dim3(64), 0, st, a);
-      else hipLaunchKernelGGL((norm_rope_append_kernel<float, 128>), grid, dim3(64), 0, st, a);
+      if (bf) hipLaunchKernelGGL((norm_rope_append_kernel<bf16, 128>), grid, blk, 0, st, a);
+      else hipLaunchKernelGGL((norm_rope_append_kernel<float, 128>), grid, blk, 0, st, a);
     }
   } else if (a.head_dim == 64) {
     if (MODE == 0) {
-      if (bf) hipLaunchKernelGGL((norm_rope_fwd_kernel<bf16, 64>), grid, dim3(64), 0, st, a);
-      else hipLaunchKernelGGL((norm_rope_fwd_kernel<float, 64>), grid, dim3(64), 0, st, a);
+      if (bf) hipLaunchKernelGGL((norm_rope_fwd_kernel<bf16, 64>), grid, blk, 0, st, a);
+      else hipLaunchKernelGGL((norm_rope_fwd_kernel<float, 64>), grid, blk, 0, st, a);
     } else {
-      if (bf) hipLaunchKernelGGL((norm_rope_append_kernel<bf16, 64>), grid, dim3(64), 0, st, a);
-      else hipLaunchKernelGGL((norm_rope_append_kernel<float, 64>), grid, dim3(64), 0, st, a);
+      if (bf) hipLaunchKernelGGL((norm_rope_append_kernel<bf16, 64>), grid, blk, 0, st, a);
+      else hipLaunchKernelGGL((norm_rope_append_kernel<float, 64>), grid, blk, 0, st, a);
     }
   } else {
     return hipErrorInvalidValue;
@@ -335,13 +396,30 @@ static hipError_t launch_nr(int dtype, const NormRopeArgs& a, dim3 grid, hipStre
   return hipGetLastError();
 }
 
+// The rotary inverse frequencies of the config, in double.
+static NormRopeArgs with_inv_freq(const NormRopeArgs& a0) {
+  NormRopeArgs a = a0;
+  for (int i = 0; i < 64; ++i)
+    a.inv_freq[i] = (a.rope_theta > 0.f && 2 * i < a.head_dim)
+                        ? std::pow((double)a.rope_theta, -2.0 * i / (double)a.head_dim)
+                        : 0.0;
+  return a;
+}
+
+static int nr_groups(int n, int head_dim) {
+  const int per = head_dim == 64 ? nr_heads_per_wg<64>() : nr_heads_per_wg<128>();
+  return (n + per - 1) / per;
+}
+
 hipError_t launch_norm_rope_forward(int dtype, const NormRopeArgs& a, hipStream_t st) {
-  return launch_nr<0>(dtype, a, dim3(a.n_heads + 2 * a.n_kv_heads, a.batch * 16), st);
+  return launch_nr<0>(dtype, with_inv_freq(a),
+                      dim3(a.batch * 16, nr_groups(a.n_heads + 2 * a.n_kv_heads, a.head_dim)), st);
 }
 
 hipError_t launch_norm_rope_append(int dtype, const NormRopeArgs& a, hipStream_t st) {
   if (a.n_tok <= 0) return hipSuccess;
-  return launch_nr<1>(dtype, a, dim3(a.n_layers * 2 * a.n_kv_heads, a.n_tok), st);
+  return launch_nr<1>(dtype, with_inv_freq(a),
+                      dim3(a.n_tok, nr_groups(a.n_layers * 2 * a.n_kv_heads, a.head_dim)), st);
 }
 
 // One workgroup per draft row: its 1024 threads reduce the row's per-column

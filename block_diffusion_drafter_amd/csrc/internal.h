@@ -156,6 +156,7 @@ struct NormRopeArgs {
   int n_tok;              // append mode
   float eps;
   float rope_theta;       // <= 0: no rotation
+  double inv_freq[64];    // rope_theta^(-2i / head_dim), i < head_dim / 2 (set by the launchers)
 };
 
 hipError_t launch_norm_rope_forward(int dtype, const NormRopeArgs& a, hipStream_t st);
