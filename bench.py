@@ -68,7 +68,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="q1", choices=["q1", "q32", "q4l", "l16"])
+    ap.add_argument("--workload", default="q1", choices=["q1", "q32", "q4l", "l16", "train"],
+                    help="train: the training-pattern attention of packed blocks alone "
+                         "(its own metric; the drafting workloads time whole rounds)")
     ap.add_argument("--temperature", type=float, default=0.0,
                     help="> 0: draft by sampling softmax(logits / T) and verify by speculative "
                          "rejection sampling against seeded target logits (0: greedy)")
@@ -105,6 +107,8 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("no GPU visible: bench.py needs an MI355X", file=sys.stderr)
         return 1
+    if a.workload == "train":
+        return bench_packed(a)
     W = WORKLOADS[a.workload]
     variant = {}
     if a.block:
@@ -385,6 +389,126 @@ def cpu_baseline(W, host, ctx_lens, n_new, feats, budget_s):
             "cores": cores, "kind": "oracle",
             "sample": f"{rounds} round(s) of 1 sequence of {W.name} (ctx {c0}, {n0} new rows), "
                       f"fp64 NumPy, {t_used:.1f} s"}
+
+
+def bench_packed(a) -> int:
+    """Training-pattern attention of packed blocks, every draft layer once per
+    step: 4 sequences of 4096 positions of Qwen3-8B-shaped context (fused +
+    injected by the library from seeded features), 512 anchors per sequence
+    drawn over the response (positions 512..4096), block 16. The kernel reads
+    each block's context prefix (mostly from L2: the blocks of a sequence share
+    it) and its own 16 keys."""
+    import torch
+    from block_diffusion_drafter_amd import binding as B
+    from synth import QWEN3_8B_SHAPED
+    from synth import inputs as I
+    from synth import torch_io
+
+    cfg = QWEN3_8B_SHAPED
+    n_seq, ctx_len, nb, prompt = 4, 4096, 512, 512
+    Bk, L, Hq, Hkv, hd = cfg.block_size, cfg.n_layers, cfg.n_heads, cfg.n_kv_heads, cfg.head_dim
+    name = f"packed-blocks-qwen3-8b-shaped-{n_seq}x{ctx_len}-{nb}anchors"
+    print(f"[bench] workload {name}", file=sys.stderr, flush=True)
+    host = I.Weights(cfg, 0)
+    model = B.DraftModel(cfg, torch_io.weights_to_device(host))
+    cap = ((ctx_len + Bk + 31) // 32) * 32
+    ws = model.new_workspace(n_seq, cap, 8192)
+    cache = model.new_cache(n_seq, cap)
+    for s in range(n_seq):
+        for lo in range(0, ctx_len, 4096):
+            n = min(4096, ctx_len - lo)
+            fd = [torch_io.to_device(f) for f in I.target_hiddens(cfg, n, seed=1, tag=f"train.{s}.{lo}")]
+            ctx = torch.empty((n, cfg.hidden), dtype=model.dtype, device="cuda")
+            model.ctx_project(fd, ctx, ws)
+            counts = np.zeros(n_seq, np.int32)
+            counts[s] = n
+            cu = torch.from_numpy(np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)).cuda()
+            model.ctx_kv_append(cache, ctx, cu, ws)
+    anchors = np.stack([I.training_anchors(ctx_len, nb, prompt, seed=6, tag=f"bench{s}")
+                        for s in range(n_seq)])
+    qh, kh, vh = I.packed_block_qkv(cfg, n_seq * nb, seed=5, tag="bench")
+    q = torch_io.to_device(qh).view(n_seq, nb, Bk, Hq, hd)
+    kb = torch_io.to_device(kh).view(n_seq, nb, Bk, Hkv, hd)
+    vb = torch_io.to_device(vh).view(n_seq, nb, Bk, Hkv, hd)
+    out = torch.empty_like(q)
+    anc = torch.from_numpy(anchors).cuda()
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+
+    def step():
+        for l in range(L):
+            model.packed_block_attention(cache, l, anc, q, kb, vb, out, status)
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(a.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    assert status.item() == 0, f"device status {status.item()}"
+    ms = e0.elapsed_time(e1) / a.steps
+    keys = anchors.astype(np.int64) + Bk                          # keys per block
+    flops = float(4 * hd * Hq * Bk * keys.sum()) * L              # QK^T and PV per step
+    ctx_bytes = float(keys.sum()) * 2 * Hkv * hd * 2 * L           # K/V rows each block reads
+    uniq = (n_seq * ctx_len * 2 * Hkv * hd * 2 + q.numel() * 2 * 2 + 2 * kb.numel() * 2) * L
+    t = ms / 1e3
+    res = {
+        "metric": "packed-block attention block-tokens/sec (training pattern, 5 layers, block 16)",
+        "value": round(n_seq * nb * Bk / t, 1), "unit": "block-tokens/s", "n_gpus": 1,
+        "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype,
+        "data": "synthetic: seeded drafter, N(0,1) target features, N(0,1) block q/k/v",
+        "config": {"workload": name, "sequences": n_seq, "ctx_len": ctx_len,
+                   "anchors_per_seq": nb, "block": Bk, "layers": L, "heads": [Hq, Hkv],
+                   "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "mfma", "achieved": round(flops / t / 1e12, 1),
+                     "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(flops / t / 1e12 / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel_class": "attention_packed",
+                     "context_rows_streamed_TBps": round(ctx_bytes / t / 1e12, 2),
+                     "unique_hbm_bytes_per_step": int(uniq),
+                     "hbm_frac_of_unique_bytes": round(uniq / t / 1e12 / (HBM_PEAK_GBS / 1e3), 4)},
+    }
+    if not a.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_packed(cfg, host, anchors, qh, kh, vh, ctx_len, a.cpu_seconds)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+def cpu_baseline_packed(cfg, host, anchors, qh, kh, vh, ctx_len, budget_s):
+    """The training-pattern oracle (fp64 NumPy) on blocks of sequence 0, layer
+    0, one block at a time until the budget is spent; the context K/V of that
+    sequence through the oracle's own fusion and projection (setup, untimed)."""
+    from oracle import dflash_oracle as O
+    from oracle import training as TR
+    from synth import inputs as I
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    ow = {n: host.get(n).f32() for n in ("fc", "fc_norm", "layers.0.wk", "layers.0.wv",
+                                         "layers.0.k_norm")}
+    feats = [f.f32() for f in I.target_hiddens(cfg, ctx_len, seed=1, tag="train.0.0")]
+    ctx = O.ctx_project(feats, ow["fc"], ow["fc_norm"], cfg.rms_eps)
+    k, v = O.context_kv(ctx, np.arange(ctx_len), O.layer_weights(ow, 0), cfg)
+    Bk, nb = cfg.block_size, anchors.shape[1]
+    q = qh.f32().reshape(-1, Bk, cfg.n_heads, cfg.head_dim)
+    kb = kh.f32().reshape(-1, Bk, cfg.n_kv_heads, cfg.head_dim)
+    vb = vh.f32().reshape(-1, Bk, cfg.n_kv_heads, cfg.head_dim)
+    done, t_used = 0, 0.0
+    while done < nb and (done < 1 or t_used < budget_s):
+        t0 = time.perf_counter()
+        TR.packed_block_attention(q[done:done + 1], kb[done:done + 1], vb[done:done + 1], k, v,
+                                  anchors[0, done:done + 1], cfg.n_heads // cfg.n_kv_heads)
+        t_used += time.perf_counter() - t0
+        done += 1
+    return {"value": round(Bk * done / t_used / cfg.n_layers, 3), "unit": "block-tokens/s",
+            "cores": cores, "kind": "oracle",
+            "sample": f"{done} block(s) of sequence 0 at layer 0 (anchors {int(anchors[0, 0])}.."
+                      f"{int(anchors[0, done - 1])}), fp64 NumPy, {t_used:.1f} s; scaled to "
+                      f"{cfg.n_layers} layers per step"}
 
 
 if __name__ == "__main__":

@@ -19,7 +19,8 @@ _lib = None
 DFLASH_FP32, DFLASH_BF16 = 0, 1
 DEV_CAPACITY, DEV_TOKEN, DEV_OFFSETS = 1, 2, 4
 KERNEL_CLASSES = ["gemm_f32out", "gemm_resid", "gemm_swiglu", "lm_head", "attention",
-                  "attention_combine", "norm_rope", "rmsnorm", "small", "sampling"]
+                  "attention_combine", "norm_rope", "rmsnorm", "small", "sampling",
+                  "attention_packed"]
 
 LAYER_FIELDS = ["in_norm", "wq", "wk", "wv", "q_norm", "k_norm", "wo", "post_norm",
                 "w_gate", "w_up", "w_down"]
@@ -106,6 +107,9 @@ def lib() -> ctypes.CDLL:
                                            vp, vp, vp, vp, vp, vp, i64, vp]
         L.dflash_accept.restype = i32
         L.dflash_accept.argtypes = [vp, vp, i32, i32, vp, vp, vp, vp]
+        L.dflash_packed_block_attention.restype = i32
+        L.dflash_packed_block_attention.argtypes = [vp, ctypes.POINTER(KVCacheStruct), i32, i32,
+                                                    i32, vp, vp, vp, vp, vp, vp, vp]
         L.dflash_sampling_workspace_bytes.restype = i64
         L.dflash_sampling_workspace_bytes.argtypes = [i32, i32, i32]
         L.dflash_sample_drafts.restype = i32
@@ -305,6 +309,20 @@ class DraftModel:
             self.handle, ctypes.byref(st), _ptr(anchor), anchor.shape[0], _ptr(draft_tokens),
             _ptr(logits), _ptr(hidden_out), _ptr(target_tokens), _ptr(accept_len), _ptr(bonus),
             _ptr(dev_status), _ptr(ws), ws.numel(), _stream()), "dflash_draft_forward")
+
+
+    def packed_block_attention(self, cache: KVCache, layer: int, anchors: torch.Tensor,
+                               q: torch.Tensor, k_blk: torch.Tensor, v_blk: torch.Tensor,
+                               out: torch.Tensor,
+                               dev_status: Optional[torch.Tensor] = None) -> None:
+        """Training-pattern attention of packed blocks (one layer): anchors
+        [n_seq, nb] int32; q, out [n_seq, nb, B, Hq, hd]; k_blk, v_blk
+        [n_seq, nb, B, Hkv, hd]; the context K/V come from `cache`."""
+        st = cache.struct()
+        n_seq, nb = anchors.shape
+        _check(lib().dflash_packed_block_attention(
+            self.handle, ctypes.byref(st), layer, n_seq, nb, _ptr(anchors), _ptr(q), _ptr(k_blk),
+            _ptr(v_blk), _ptr(out), _ptr(dev_status), _stream()), "dflash_packed_block_attention")
 
 
 class RoundGraph:

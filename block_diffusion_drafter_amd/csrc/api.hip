@@ -771,6 +771,51 @@ int32_t dflash_accept(const int32_t* draft_tokens, const int32_t* target_tokens,
   return e == hipSuccess ? DFLASH_OK : DFLASH_ERR_HIP;
 }
 
+int32_t dflash_packed_block_attention(const dflash_handle* h, const dflash_kv_cache* cache,
+                                      int32_t layer, int32_t n_seq, int32_t blocks_per_seq,
+                                      const int32_t* anchors, const void* q, const void* k_blk,
+                                      const void* v_blk, void* out, int32_t* dev_status,
+                                      void* stream) {
+  if (!h) return DFLASH_ERR_NULL;
+  int32_t rc = check_cache(h, cache);
+  if (rc != DFLASH_OK) return rc;
+  const dflash_config& c = h->cfg;
+  if (layer < 0 || layer >= c.n_layers || n_seq < 0 || blocks_per_seq < 0 || n_seq > cache->batch)
+    return DFLASH_ERR_SHAPE;
+  const int64_t n_blk = (int64_t)n_seq * blocks_per_seq;
+  if (n_blk * c.block_size > INT32_MAX) return DFLASH_ERR_SHAPE;
+  if (n_blk == 0) return DFLASH_OK;
+  if (!anchors || !q || !k_blk || !v_blk || !out) return DFLASH_ERR_NULL;
+  if (!al16(q) || !al16(k_blk) || !al16(v_blk) || !al16(out)) return DFLASH_ERR_ALIGN;
+  const int hd = c.head_dim, Hkv = c.n_kv_heads;
+  const size_t es = elem_size(c.dtype);
+  const size_t layer_elems = (size_t)cache->batch * Hkv * cache->capacity * hd;
+  PackedAttnArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.q = q;
+  a.k_blk = k_blk;
+  a.v_blk = v_blk;
+  a.k = (const char*)cache->k + layer_elems * es * layer;
+  a.v = (const char*)cache->v + layer_elems * es * layer;
+  a.ctx_len = cache->ctx_len;
+  a.anchors = anchors;
+  a.out = out;
+  a.dev_status = dev_status;
+  a.n_blk = (int)n_blk;
+  a.blocks_per_seq = blocks_per_seq;
+  a.n_heads = c.n_heads;
+  a.n_kv_heads = Hkv;
+  a.head_dim = hd;
+  a.block = c.block_size;
+  a.cap = cache->capacity;
+  a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)hd));
+  hipStream_t st = (hipStream_t)stream;
+  prof_begin(DFLASH_K_ATTN_PACKED, 0.0, 0.0, st);
+  const hipError_t e = launch_packed_attention(c.dtype, a, st);
+  prof_end(st);
+  return e == hipSuccess ? DFLASH_OK : DFLASH_ERR_HIP;
+}
+
 int32_t dflash_round_graph_create(const dflash_handle* h, const dflash_kv_cache* cache,
                                   const dflash_round_io* io, void* stream,
                                   dflash_round_graph** out) {

@@ -635,6 +635,129 @@ static hipError_t launch_hd(const AttnArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+// Training-pattern attention of packed blocks: one workgroup per (block,
+// KV head), one wave per query head of the group. The block's context is the
+// prefix 0 .. anchor-1 of its sequence's cache, streamed as in the decoding
+// kernel's register path with two 32-key blocks in flight (many blocks of a
+// sequence read the same prefix, which stays in L2); then the block's own B
+// keys, gathered from the packed K/V into one masked 32-key block. Anchors
+// outside [0, min(ctx_len, cap)] are clamped and flag DFLASH_DEV_CAPACITY.
+template <typename T, int HD>
+__global__ __launch_bounds__(512) void packed_attn_kernel(PackedAttnArgs p) {
+  using KB = KVBlock<T, HD>;
+  constexpr int EPF = KB::EPF, FR = KB::FR, NDT = KB::NDT;
+  const int lane = threadIdx.x & 63, j = threadIdx.x >> 6;
+  const int r = lane & 15, grp = lane >> 4;
+  const int blk = blockIdx.x, g = blockIdx.y;
+  const int G = p.n_heads / p.n_kv_heads, Hq = p.n_heads, Hkv = p.n_kv_heads;
+  const int h = g * G + j, B = p.block;
+  const int s = blk / p.blocks_per_seq;
+  int a = p.anchors[blk];
+  const int lim = min(max(p.ctx_len[s], 0), p.cap);
+  if (a < 0 || a > lim) {
+    if (threadIdx.x == 0 && g == 0 && p.dev_status) atomicOr(p.dev_status, DFLASH_DEV_CAPACITY);
+    a = a < 0 ? 0 : lim;
+  }
+
+  // Q fragments of query row r (zero past the block), channel order as K.
+  u32x4 qf[FR];
+  {
+    const T* qp = reinterpret_cast<const T*>(p.q) + (((size_t)blk * B + r) * Hq + h) * HD + grp * EPF;
+#pragma unroll
+    for (int f = 0; f < FR; ++f) qf[f] = r < B ? ld16(qp + f * 4 * EPF) : zero16();
+  }
+  AttnState<T, HD> S;
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) S.o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const size_t kvoff = (size_t)(s * Hkv + g) * p.cap * HD;
+  const T* K = reinterpret_cast<const T*>(p.k) + kvoff;
+  const T* V = reinterpret_cast<const T*>(p.v) + kvoff;
+  if (a > 0 && sizeof(T) == 4 && HD == 128) {
+    // fp32 at head_dim 128: one block of fragments already fills the registers
+    for (int kb = 0; kb < a; kb += 32) {
+      KB b0;
+      load_block<T, HD>(b0, K, V, kb, a, r, grp);
+      attn_update<T, HD>(S, b0, qf, kb, a, INT_MIN, p.scale_log2, grp);
+    }
+  } else if (a > 0) {
+    KB b0, b1;
+    load_block<T, HD>(b0, K, V, 0, a, r, grp);
+    for (int kb = 0; kb < a; kb += 64) {
+      const bool has1 = kb + 32 < a;
+      if (has1) load_block<T, HD>(b1, K, V, kb + 32, a, r, grp);
+      attn_update<T, HD>(S, b0, qf, kb, a, INT_MIN, p.scale_log2, grp);
+      if (has1) {
+        if (kb + 64 < a) load_block<T, HD>(b0, K, V, kb + 64, a, r, grp);
+        attn_update<T, HD>(S, b1, qf, kb + 32, a, INT_MIN, p.scale_log2, grp);
+      }
+    }
+  }
+
+  // The block's own keys as one 32-key block: key k < B of the block at the
+  // fragment positions the decoding layout gives key k; the rest zero (their
+  // scores are masked, their values must be 0).
+  {
+    KB b;
+    const T* kp = reinterpret_cast<const T*>(p.k_blk);
+    const T* vp = reinterpret_cast<const T*>(p.v_blk);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int key = key_of<T>(t, r);
+      const T* src = kp + (((size_t)blk * B + key) * Hkv + g) * HD + grp * EPF;
+#pragma unroll
+      for (int f = 0; f < FR; ++f) b.k[t][f] = key < B ? ld16(src + f * 4 * EPF) : zero16();
+    }
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      const int ch = 16 * dt + r;
+#pragma unroll
+      for (int u = 0; u < KB::VF; ++u) {
+        // the decoding layout's V fragment: keys koff .. koff + EPF - 1 of channel ch
+        const int koff = (sizeof(T) == 2) ? 8 * grp : 16 * u + 4 * grp;
+        T vals[EPF];
+#pragma unroll
+        for (int e = 0; e < EPF; ++e) {
+          const int key = koff + e;
+          vals[e] = key < B ? vp[(((size_t)blk * B + key) * Hkv + g) * HD + ch] : from_f32<T>(0.f);
+        }
+        b.v[dt][u] = *reinterpret_cast<const u32x4*>(vals);
+      }
+    }
+    attn_update<T, HD>(S, b, qf, 0, B, INT_MIN, p.scale_log2, grp);
+  }
+
+  // Normalise and write query rows r < B: lane (r, grp) holds channels
+  // 16 dt + 4 grp + i.
+  S.l_run += __shfl_xor(S.l_run, 16);
+  S.l_run += __shfl_xor(S.l_run, 32);
+  if (r < B) {
+    const float inv = 1.0f / S.l_run;
+    T* out = reinterpret_cast<T*>(p.out) + (((size_t)blk * B + r) * Hq + h) * HD;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) out[16 * dt + 4 * grp + i] = from_f32<T>(S.o[dt][i] * inv);
+  }
+}
+
+hipError_t launch_packed_attention(int dtype, const PackedAttnArgs& a, hipStream_t st) {
+  if (a.n_blk <= 0) return hipSuccess;
+  const int G = a.n_heads / a.n_kv_heads;
+  if (G > 8 || a.block < 1 || a.block > 16) return hipErrorInvalidValue;
+  const dim3 grid(a.n_blk, a.n_kv_heads), block(64 * G);
+  if (dtype == DFLASH_BF16) {
+    if (a.head_dim == 128) hipLaunchKernelGGL((packed_attn_kernel<bf16, 128>), grid, block, 0, st, a);
+    else if (a.head_dim == 64) hipLaunchKernelGGL((packed_attn_kernel<bf16, 64>), grid, block, 0, st, a);
+    else return hipErrorInvalidValue;
+  } else {
+    if (a.head_dim == 128) hipLaunchKernelGGL((packed_attn_kernel<float, 128>), grid, block, 0, st, a);
+    else if (a.head_dim == 64) hipLaunchKernelGGL((packed_attn_kernel<float, 64>), grid, block, 0, st, a);
+    else return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_attention(int dtype, const AttnArgs& a, hipStream_t st) {
   if (a.n_heads / a.n_kv_heads > 8) return hipErrorInvalidValue;
   if (dtype == DFLASH_BF16) {

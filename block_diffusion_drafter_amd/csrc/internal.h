@@ -132,6 +132,24 @@ struct AttnArgs {
 
 hipError_t launch_attention(int dtype, const AttnArgs& a, hipStream_t st);
 
+// Training-pattern attention of packed blocks: block b (sequence b / nb,
+// anchor position anchors[b]) attends to its sequence's context rows
+// 0 .. anchor-1 in the decoding cache and to its own B keys.
+struct PackedAttnArgs {
+  const void* q;          // [n_blk][B][Hq][hd] model dtype
+  const void* k_blk;      // [n_blk][B][Hkv][hd]
+  const void* v_blk;
+  const void* k;          // one layer's K cache: [cache_batch][Hkv][cap][hd]
+  const void* v;          // one layer's V cache: [cache_batch][Hkv][cap/32][hd][32]
+  const int32_t* ctx_len; // [cache_batch]
+  const int32_t* anchors; // [n_blk]
+  void* out;              // [n_blk][B][Hq][hd]
+  int32_t* dev_status;
+  int n_blk, blocks_per_seq, n_heads, n_kv_heads, head_dim, block, cap;
+  float scale_log2;
+};
+hipError_t launch_packed_attention(int dtype, const PackedAttnArgs& a, hipStream_t st);
+
 // Per-head RMSNorm + RoPE of q/k and the K/V cache scatter.
 //  Forward mode (kv_rows == nullptr): src is the fused QKV output
 //   [batch*B][(Hq + 2*Hkv)*hd] fp32; q heads go to q_out ([batch][Hq][16][hd],

@@ -238,6 +238,35 @@ int32_t dflash_draft_forward(const dflash_handle *h, const dflash_kv_cache *cach
                              int32_t *accept_len, int32_t *bonus, int32_t *dev_status,
                              void *ws, int64_t ws_bytes, void *stream);
 
+/* Training-pattern attention of packed blocks [W "Training" step 4 and the
+ * training-loss pseudocode; R sec. 6.1]: the blocks drawn from one sequence
+ * are trained together; a block anchored at position a (its B positions at
+ * a .. a+B-1) attends, in both directions, to its own B keys and to the
+ * target's context features at positions 0 .. a-1 (the anchor's own feature
+ * is not used, as when drafting, where the context ends right before the
+ * anchor), never to another block. One call covers one layer.
+ *   cache, layer: the context K/V of every sequence in the drafting cache
+ *        layout (dflash_kv_cache), e.g. written by dflash_ctx_kv_append over
+ *        the sequence's fused features; sequence s reads cache row s, whose
+ *        ctx_len[s] must cover its anchors.
+ *   n_seq <= cache->batch sequences of blocks_per_seq blocks each; block
+ *        b = s * blocks_per_seq + j.
+ *   anchors: device int32 [n_seq * blocks_per_seq]; an anchor outside
+ *        [0, min(ctx_len[s], capacity)] is clamped and flags DFLASH_DEV_CAPACITY.
+ *   q: [n_blk][B][n_heads][head_dim], the blocks' queries after q-norm and
+ *        rotation at their positions; k_blk, v_blk: [n_blk][B][n_kv_heads]
+ *        [head_dim] likewise (keys rotated); out: [n_blk][B][n_heads][head_dim].
+ *        All in the config's dtype, 16-byte aligned, caller-owned device memory.
+ * Scale 1/sqrt(head_dim); query head j reads KV head j / (n_heads / n_kv_heads).
+ * Errors (nothing enqueued): DFLASH_ERR_NULL, _ALIGN, _SHAPE (layer or counts
+ * out of range, n_seq > cache->batch), as for the cache in
+ * dflash_draft_forward; DFLASH_ERR_HIP on a launch failure. */
+int32_t dflash_packed_block_attention(const dflash_handle *h, const dflash_kv_cache *cache,
+                                      int32_t layer, int32_t n_seq, int32_t blocks_per_seq,
+                                      const int32_t *anchors, const void *q, const void *k_blk,
+                                      const void *v_blk, void *out, int32_t *dev_status,
+                                      void *stream);
+
 /* Greedy accept-prefix [W decoding-loop pseudocode; R sec. 4.1]:
  *   accept_len[s] = number of leading i < B-1 with draft[s][i] == target[s][i],
  *   bonus[s] = target[s][accept_len[s]]; anchor_out (optional) = bonus.
@@ -369,7 +398,8 @@ typedef enum dflash_kernel_class {
   DFLASH_K_RMSNORM = 7,
   DFLASH_K_SMALL = 8,        /* embedding, argmax reduce, accept, ctx_len update */
   DFLASH_K_SAMPLING = 9,     /* temperature > 0 drafting and verification */
-  DFLASH_K_NCLASSES = 10
+  DFLASH_K_ATTN_PACKED = 10, /* training-pattern attention of packed blocks */
+  DFLASH_K_NCLASSES = 11
 } dflash_kernel_class;
 
 int32_t dflash_profiler_start(int32_t max_launches, uint32_t class_mask);

@@ -257,3 +257,23 @@ def cache_state(cfg: DrafterConfig, ctx_lens: Sequence[int], seed: int
             row.append((k, v))
         out.append(row)
     return out
+
+
+def training_anchors(ctx_len: int, n_blocks: int, prompt_len: int, seed: int, tag: str
+                     ) -> np.ndarray:
+    """Sorted anchor positions of one training sequence, uniform over its
+    response part [prompt_len, ctx_len] (drawn with replacement, so blocks may
+    start closer than B apart, as independent draws do)."""
+    g = np.random.Generator(np.random.PCG64(_seed_seq(seed, "train.anchors." + tag)))
+    return np.sort(g.integers(prompt_len, ctx_len + 1, size=n_blocks)).astype(np.int32)
+
+
+def packed_block_qkv(cfg: DrafterConfig, n_blk: int, seed: int, tag: str) -> List[HostTensor]:
+    """Synthetic packed-block queries [n_blk, B, Hq, hd] and keys / values
+    [n_blk, B, Hkv, hd], N(0,1) (the scale of RMS-normed heads)."""
+    bf16 = cfg.dtype == "bf16"
+    B, hd = cfg.block_size, cfg.head_dim
+    shp = {"q": (n_blk, B, cfg.n_heads, hd), "k": (n_blk, B, cfg.n_kv_heads, hd),
+           "v": (n_blk, B, cfg.n_kv_heads, hd)}
+    return [HostTensor(normal(seed, f"train.{n}.{tag}", shp[n], 1.0, bf16), bf16)
+            for n in ("q", "k", "v")]

@@ -285,3 +285,25 @@ def test_sliding_window_config_is_validated():
     rc, h = create(c)
     assert rc == 0
     lib.dflash_destroy(h)
+
+
+def test_packed_block_attention_rejects_bad_arguments_before_launching():
+    lib = B.lib()
+    rc, h = create(B.make_config(TINY_FP32))
+    assert rc == 0
+    cache = B.KVCacheStruct(FAKE, FAKE, FAKE, 2, 64)
+    call = lib.dflash_packed_block_attention
+    # no handle, no cache
+    assert call(None, ctypes.byref(cache), 0, 1, 2, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == -1
+    assert call(h, None, 0, 1, 2, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == -1
+    # layer outside the drafter, negative counts, more sequences than the cache holds
+    assert call(h, ctypes.byref(cache), 1, 1, 2, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == -2
+    assert call(h, ctypes.byref(cache), 0, -1, 2, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == -2
+    assert call(h, ctypes.byref(cache), 0, 3, 2, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == -2
+    # missing or misaligned buffers
+    assert call(h, ctypes.byref(cache), 0, 1, 2, None, FAKE, FAKE, FAKE, FAKE, None, None) == -1
+    assert call(h, ctypes.byref(cache), 0, 1, 2, FAKE, FAKE + 8, FAKE, FAKE, FAKE, None,
+                None) == -4
+    # nothing to do: no launch, no pointer needed
+    assert call(h, ctypes.byref(cache), 0, 1, 0, None, None, None, None, None, None, None) == 0
+    lib.dflash_destroy(h)
