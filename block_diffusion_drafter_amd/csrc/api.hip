@@ -118,12 +118,12 @@ struct Plan {
 
 // Attention split: each KV head's keys (all sequences, end to end) are cut
 // into equal ranges over up to 512 / Hkv workgroups, one round over the chip
-// at 2 workgroups of a KV group per CU, each range at least 4 blocks of 32
+// at 2 workgroups of a KV group per CU, each range at least 2 blocks of 32
 // keys; the device sizes the split from ctx_len, the host only bounds it.
 // (Per-sequence chunks left a ragged batch with a part-filled last round:
 // batch 32 at 512-8192 keys ran 1.6 rounds of 1024-key chunks.)
 constexpr int kAttnSlots = 512;
-constexpr int kAttnMinBlocks = 4;
+constexpr int kAttnMinBlocks = 2;
 int attn_wg_per_head(int hkv) { return std::max(1, kAttnSlots / std::max(1, hkv)); }
 
 // Floats of split-K partials a tiled-A projection needs on the MFMA path (0 if none).

@@ -534,12 +534,17 @@ void attn_partial_lds_kernel(AttnArgs p) {
   // Block n: wait until it has landed and every wave is done with block n-1,
   // refill block n-1's slot with block n-1+NSB, read block n from LDS and
   // multiply it (the other waves on the SIMD cover the LDS latency).
+  // A segment of at most NSB blocks is loaded whole and waited for once;
+  // longer ones run the ring.
+  const bool whole = nblk <= NSB;
 #pragma unroll
-  for (int n = 0; n < NSB; ++n) issue(min(n, nblk - 1), n);
-  attn_wait_barrier<IPW * (NSB - 1)>();
+  for (int n = 0; n < NSB; ++n)
+    if (!whole || n < nblk) issue(min(n, nblk - 1), n);
+  if (whole) attn_wait_barrier<0>();
+  else attn_wait_barrier<IPW * (NSB - 1)>();
   KB b;
   for (int n = 0; n < nblk; ++n) {
-    if (n > 0) {
+    if (n > 0 && !whole) {
       attn_wait_barrier<IPW * (NSB - 2)>();
       issue(min(n - 1 + NSB, nblk - 1), (n - 1) % NSB);
     }
@@ -583,13 +588,13 @@ __global__ __launch_bounds__(512) void attn_combine_kernel(AttnArgs p) {
   if (q >= p.block) return;
   const size_t e0 = part_entry(p, g, w0, s);  // segment k is entry e0 + k
   float M = -INFINITY;
-#pragma unroll 4
+#pragma unroll 8
   for (int k = 0; k < nch; ++k) M = fmaxf(M, p.part_ml[(((e0 + k) * G + j) * 16 + q) * 2]);
   const int ch0 = 4 * CPL * slice + CPL * c;
   float L = 0.f, o[CPL];
 #pragma unroll
   for (int i = 0; i < CPL; ++i) o[i] = 0.f;
-#pragma unroll 2
+#pragma unroll 4
   for (int k = 0; k < nch; ++k) {
     const size_t item = (e0 + k) * G + j;
     const float wk = exp2f(p.part_ml[(item * 16 + q) * 2] - M);
@@ -604,6 +609,71 @@ __global__ __launch_bounds__(512) void attn_combine_kernel(AttnArgs p) {
 #pragma unroll
   for (int i = 0; i < CPL; ++i)
     out[tiled_index<T>(row, h * HD + ch0 + i, p.out_nck)] = from_f32<T>(o[i] * inv);
+}
+
+// Many segments per sequence (batch 1-4): merge of the segment partials of
+// one (query head, sequence, 16-channel
+// slice). Thread (q, cg) owns query row q and the segments c = cg, cg + 16,
+// ...: it reduces the row's running max and sum over its segments, the 16
+// threads of a row combine them through LDS, then each thread accumulates its
+// segments' weighted partial outputs for the slice's 16 channels and LDS sums
+// the 16 segment groups. Every thread's loads are independent of each other.
+template <typename T, int HD>
+__global__ __launch_bounds__(256) void attn_combine_chunks_kernel(AttnArgs p) {
+  __shared__ float red_m[16][17], red_l[16][17];
+  __shared__ float red_o[16][16][17];
+  const int h = blockIdx.x, s = blockIdx.y, slice = blockIdx.z;
+  const int G = p.n_heads / p.n_kv_heads;
+  const int g = h / G, j = h % G;
+  extern __shared__ int pre[];
+  seq_block_prefix(p, pre);
+  const KeySplit ks = key_split(p, pre);
+  const int w0 = ks.owner(pre[s]), w1 = ks.owner(pre[s + 1] - 1);
+  if (w0 == w1) return;  // one segment: written by the partial kernel
+  // Segments c = 0 .. nch-1 come from workgroups w0 + c (every one in between
+  // has a non-empty range since nw <= tb), at entries w0 + c + s.
+  const int nch = w1 - w0 + 1;
+  const int t = threadIdx.x, q = t & 15, cg = t >> 4;
+  const size_t item0 = part_entry(p, g, w0, s) * G + j;
+  float m = -INFINITY;
+  for (int c = cg; c < nch; c += 16) m = fmaxf(m, p.part_ml[((item0 + (size_t)c * G) * 16 + q) * 2]);
+  red_m[q][cg] = m;
+  __syncthreads();
+  float M = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) M = fmaxf(M, red_m[q][k]);
+  float l = 0.f;
+  for (int c = cg; c < nch; c += 16) {
+    const float* ml = p.part_ml + ((item0 + (size_t)c * G) * 16 + q) * 2;
+    l += ml[1] * exp2f(ml[0] - M);
+  }
+  red_l[q][cg] = l;
+  __syncthreads();
+  float L = 0.f;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) L += red_l[q][k];
+  const float inv = 1.0f / L;
+  float acc[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) acc[k] = 0.f;
+  for (int c = cg; c < nch; c += 16) {
+    const size_t it = item0 + (size_t)c * G;
+    const float w = exp2f(p.part_ml[(it * 16 + q) * 2] - M) * inv;
+    const float* po = p.part_o + (it * HD + 16 * slice) * 16 + q;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) acc[k] += po[k * 16] * w;
+  }
+#pragma unroll
+  for (int k = 0; k < 16; ++k) red_o[k][cg][q] = acc[k];
+  __syncthreads();
+  // thread (q, d = cg) sums the 16 chunk groups of channel 16*slice + d
+  if (q < p.block) {
+    float o = 0.f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) o += red_o[cg][k][q];
+    T* out = reinterpret_cast<T*>(p.out);
+    out[tiled_index<T>(s * p.block + q, h * HD + 16 * slice + cg, p.out_nck)] = from_f32<T>(o);
+  }
 }
 
 template <typename T, int HD>
@@ -630,8 +700,8 @@ static hipError_t launch_hd(const AttnArgs& a, hipStream_t st) {
     hipLaunchKernelGGL((attn_combine_kernel<T, HD, 8>), dim3(a.n_kv_heads, a.batch, HD / 32),
                        dim3(64 * G), pre_bytes, st, a);
   else
-    hipLaunchKernelGGL((attn_combine_kernel<T, HD, 2>), dim3(a.n_kv_heads, a.batch, HD / 8),
-                       dim3(64 * G), pre_bytes, st, a);
+    hipLaunchKernelGGL((attn_combine_chunks_kernel<T, HD>), dim3(a.n_heads, a.batch, HD / 16),
+                       dim3(256), pre_bytes, st, a);
   return hipGetLastError();
 }
 

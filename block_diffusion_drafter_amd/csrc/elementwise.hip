@@ -215,27 +215,28 @@ __device__ __forceinline__ void store_v(T* vbase, int pos, int c, float x0, floa
   blk[(size_t)(c + HD / 2) * kKeyBlock] = from_f32<T>(x1);
 }
 
-// Heads (or append columns) per workgroup: 4 waves x kNrIters iterations x
+// Heads (or append columns) per workgroup: 4 waves x IT iterations x
 // RopeLane::HPW heads per iteration. A wave loads all its heads' pairs
-// first, then normalises and stores them: one memory latency per wave.
-constexpr int kNrIters = 4;
-template <int HD>
-__host__ __device__ constexpr int nr_heads_per_wg() { return 4 * kNrIters * (64 / (HD / 2)); }
+// first, then normalises and stores them: one memory latency per wave. Few
+// rows (batch 1) take IT = 1 for more waves in flight; many take IT = 4,
+// which shares each row's rotary angles over more heads.
+template <int HD, int IT>
+__host__ __device__ constexpr int nr_heads_per_wg() { return 4 * IT * (64 / (HD / 2)); }
 
 // Forward mode: grid (batch * 16 block slots, head groups); workgroup
 // (slot, y) takes heads y * nr_heads_per_wg + (it * 4 + wave) * HPW + sub of
 // the row's Hq + 2*Hkv. Slots i >= block only zero-fill the padded Q rows.
-template <typename T, int HD>
+template <typename T, int HD, int IT>
 __global__ __launch_bounds__(256) void norm_rope_fwd_kernel(NormRopeArgs p) {
   using RL = RopeLane<HD>;
   const int slot = blockIdx.x, s = slot / 16, i = slot % 16;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int sub = lane / RL::PAIRS, c = lane % RL::PAIRS;
   const int Hq = p.n_heads, Hkv = p.n_kv_heads, NH = Hq + 2 * Hkv;
-  const int hbase = blockIdx.y * nr_heads_per_wg<HD>() + wave * RL::HPW + sub;
+  const int hbase = blockIdx.y * nr_heads_per_wg<HD, IT>() + wave * RL::HPW + sub;
   if (i >= p.block) {
 #pragma unroll
-    for (int it = 0; it < kNrIters; ++it) {
+    for (int it = 0; it < IT; ++it) {
       const int h = hbase + it * 4 * RL::HPW;
       if (h < Hq) {
         T* qo = reinterpret_cast<T*>(p.q_out) + (((size_t)s * Hq + h) * 16 + i) * HD;
@@ -247,9 +248,9 @@ __global__ __launch_bounds__(256) void norm_rope_fwd_kernel(NormRopeArgs p) {
   }
   const int m = s * p.block + i;
   const float* src = p.src + (int64_t)m * p.src_stride;
-  float x0[kNrIters], x1[kNrIters];
+  float x0[IT], x1[IT];
 #pragma unroll
-  for (int it = 0; it < kNrIters; ++it) {
+  for (int it = 0; it < IT; ++it) {
     const int hc = min(hbase + it * 4 * RL::HPW, NH - 1);
     x0[it] = src[hc * HD + c];
     x1[it] = src[hc * HD + c + RL::PAIRS];
@@ -268,7 +269,7 @@ __global__ __launch_bounds__(256) void norm_rope_fwd_kernel(NormRopeArgs p) {
   // Every lane of an iteration takes part (the head sums shuffle across it);
   // heads past the last were clamped and are not stored.
 #pragma unroll
-  for (int it = 0; it < kNrIters; ++it) {
+  for (int it = 0; it < IT; ++it) {
     const int h = hbase + it * 4 * RL::HPW;
     const int hc = min(h, NH - 1);
     const bool is_q = hc < Hq, is_v = hc >= Hq + Hkv;
@@ -299,14 +300,14 @@ __global__ __launch_bounds__(256) void norm_rope_fwd_kernel(NormRopeArgs p) {
 // col = layer * 2*Hkv + hh of the row (hh < Hkv a key head, else a value
 // head) is written to position ctx_len[s] + (row's index in its sequence) of
 // that layer's cache.
-template <typename T, int HD>
+template <typename T, int HD, int IT>
 __global__ __launch_bounds__(256) void norm_rope_append_kernel(NormRopeArgs p) {
   using RL = RopeLane<HD>;
   const int row = blockIdx.x;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int sub = lane / RL::PAIRS, c = lane % RL::PAIRS;
   const int Hkv = p.n_kv_heads, NC = p.n_layers * 2 * Hkv;
-  const int cbase = blockIdx.y * nr_heads_per_wg<HD>() + wave * RL::HPW + sub;
+  const int cbase = blockIdx.y * nr_heads_per_wg<HD, IT>() + wave * RL::HPW + sub;
   const bool flagger = threadIdx.x == 0 && blockIdx.y == 0;
   int s = -1, i = 0;
   if (p.accept_len) {
@@ -335,9 +336,9 @@ __global__ __launch_bounds__(256) void norm_rope_append_kernel(NormRopeArgs p) {
     return;
   }
   const float* src = p.src + (int64_t)row * p.src_stride;
-  float x0[kNrIters], x1[kNrIters];
+  float x0[IT], x1[IT];
 #pragma unroll
-  for (int it = 0; it < kNrIters; ++it) {
+  for (int it = 0; it < IT; ++it) {
     const int cc = min(cbase + it * 4 * RL::HPW, NC - 1);
     x0[it] = src[cc * HD + c];
     x1[it] = src[cc * HD + c + RL::PAIRS];
@@ -345,7 +346,7 @@ __global__ __launch_bounds__(256) void norm_rope_append_kernel(NormRopeArgs p) {
   const RL rope(p, pos, c);
   const size_t layer_stride = (size_t)p.cache_batch * Hkv * p.cap * HD;
 #pragma unroll
-  for (int it = 0; it < kNrIters; ++it) {
+  for (int it = 0; it < IT; ++it) {
     const int col = cbase + it * 4 * RL::HPW;
     const int cc = min(col, NC - 1);
     const int l = cc / (2 * Hkv), hh = cc % (2 * Hkv);
@@ -370,30 +371,44 @@ __global__ __launch_bounds__(256) void norm_rope_append_kernel(NormRopeArgs p) {
   }
 }
 
-template <int MODE>
-static hipError_t launch_nr(int dtype, const NormRopeArgs& a, dim3 grid, hipStream_t st) {
+template <int MODE, int IT>
+static hipError_t launch_nr_it(int dtype, const NormRopeArgs& a, int rows, int n_cols,
+                               hipStream_t st) {
   const bool bf = dtype == DFLASH_BF16;
   const dim3 blk(256);
+#define DF_NR(K, T, HD)                                                                     \
+  hipLaunchKernelGGL((K<T, HD, IT>), dim3(rows, (n_cols + nr_heads_per_wg<HD, IT>() - 1) / \
+                                                   nr_heads_per_wg<HD, IT>()),              \
+                     blk, 0, st, a)
   if (a.head_dim == 128) {
     if (MODE == 0) {
-      if (bf) hipLaunchKernelGGL((norm_rope_fwd_kernel<bf16, 128>), grid, blk, 0, st, a);
-      else hipLaunchKernelGGL((norm_rope_fwd_kernel<float, 128>), grid, blk, 0, st, a);
+      if (bf) DF_NR(norm_rope_fwd_kernel, bf16, 128);
+      else DF_NR(norm_rope_fwd_kernel, float, 128);
     } else {
-      if (bf) hipLaunchKernelGGL((norm_rope_append_kernel<bf16, 128>), grid, blk, 0, st, a);
-      else hipLaunchKernelGGL((norm_rope_append_kernel<float, 128>), grid, blk, 0, st, a);
+      if (bf) DF_NR(norm_rope_append_kernel, bf16, 128);
+      else DF_NR(norm_rope_append_kernel, float, 128);
     }
   } else if (a.head_dim == 64) {
     if (MODE == 0) {
-      if (bf) hipLaunchKernelGGL((norm_rope_fwd_kernel<bf16, 64>), grid, blk, 0, st, a);
-      else hipLaunchKernelGGL((norm_rope_fwd_kernel<float, 64>), grid, blk, 0, st, a);
+      if (bf) DF_NR(norm_rope_fwd_kernel, bf16, 64);
+      else DF_NR(norm_rope_fwd_kernel, float, 64);
     } else {
-      if (bf) hipLaunchKernelGGL((norm_rope_append_kernel<bf16, 64>), grid, blk, 0, st, a);
-      else hipLaunchKernelGGL((norm_rope_append_kernel<float, 64>), grid, blk, 0, st, a);
+      if (bf) DF_NR(norm_rope_append_kernel, bf16, 64);
+      else DF_NR(norm_rope_append_kernel, float, 64);
     }
   } else {
     return hipErrorInvalidValue;
   }
+#undef DF_NR
   return hipGetLastError();
+}
+
+// rows x n_cols head vectors; IT = 1 below 128 rows.
+template <int MODE>
+static hipError_t launch_nr(int dtype, const NormRopeArgs& a, int rows, int n_cols,
+                            hipStream_t st) {
+  if (rows < 128) return launch_nr_it<MODE, 1>(dtype, a, rows, n_cols, st);
+  return launch_nr_it<MODE, 4>(dtype, a, rows, n_cols, st);
 }
 
 // The rotary inverse frequencies of the config, in double.
@@ -406,20 +421,13 @@ static NormRopeArgs with_inv_freq(const NormRopeArgs& a0) {
   return a;
 }
 
-static int nr_groups(int n, int head_dim) {
-  const int per = head_dim == 64 ? nr_heads_per_wg<64>() : nr_heads_per_wg<128>();
-  return (n + per - 1) / per;
-}
-
 hipError_t launch_norm_rope_forward(int dtype, const NormRopeArgs& a, hipStream_t st) {
-  return launch_nr<0>(dtype, with_inv_freq(a),
-                      dim3(a.batch * 16, nr_groups(a.n_heads + 2 * a.n_kv_heads, a.head_dim)), st);
+  return launch_nr<0>(dtype, with_inv_freq(a), a.batch * 16, a.n_heads + 2 * a.n_kv_heads, st);
 }
 
 hipError_t launch_norm_rope_append(int dtype, const NormRopeArgs& a, hipStream_t st) {
   if (a.n_tok <= 0) return hipSuccess;
-  return launch_nr<1>(dtype, with_inv_freq(a),
-                      dim3(a.n_tok, nr_groups(a.n_layers * 2 * a.n_kv_heads, a.head_dim)), st);
+  return launch_nr<1>(dtype, with_inv_freq(a), a.n_tok, a.n_layers * 2 * a.n_kv_heads, st);
 }
 
 // One workgroup per draft row: its 1024 threads reduce the row's per-column
