@@ -250,6 +250,73 @@ __device__ __forceinline__ void attn_update(AttnState<T, HD>& S, const KVBlock<T
   }
 }
 
+// One 32-key block's online-softmax update of a wave's state, bf16 (the
+// decoding kernel's and the packed-block kernel's). Scores outside
+// [k_min, k_hi) are masked (a handful of compares). The softmax reference max
+// moves only when a block exceeds it by more than 2^8 (lazy rescale: the
+// probabilities stay <= 256, exact for the final normalisation, and the output
+// accumulators are rarely touched outside the MFMAs). P enters the PV product
+// as the sum of two bf16 parts (16 significant bits), so the products are as
+// exact as the fp32 sum of probabilities they are normalised by; the second
+// MFMA per tile is free where the kernel waits on memory.
+template <int HD>
+__device__ __forceinline__ void attn_update_lazy(AttnState<bf16, HD>& S,
+                                                 const KVBlock<bf16, HD>& b, const u32x4* qf,
+                                                 int kb, int k_hi, int k_min, float scale_log2,
+                                                 int grp) {
+  using T = bf16;
+  constexpr int FR = KVBlock<T, HD>::FR, NDT = KVBlock<T, HD>::NDT;
+  f32x4 st[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    st[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int f = 0; f < FR; ++f) st[t] = mfma_frag<T>(b.k[t][f], qf[f], st[t]);
+  }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int key = kb + key_of<T>(t, 4 * grp + i);
+      const float v = (key < k_hi && key >= k_min) ? st[t][i] * scale_log2 : -INFINITY;
+      st[t][i] = v;
+      mx = fmaxf(mx, v);
+    }
+  mx = fmaxf(mx, __shfl_xor(mx, 16));
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  if (__any(mx > S.m_run + 8.0f)) {
+    const float m_new = fmaxf(S.m_run, mx);
+    // m_new stays -inf while a query has seen no key (sliding window)
+    const float alpha = m_new == -INFINITY ? 1.0f : exp2f(S.m_run - m_new);
+    S.m_run = m_new;
+    S.l_run *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) S.o[dt] *= alpha;
+  }
+  const float m_ref = S.m_run == -INFINITY ? 0.f : S.m_run;
+  float psum = 0.f;
+  bf16x8 phi, plo;
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      // v_exp_f32: the argument is <= 8; tiny results may flush to 0
+      const float pv = __builtin_amdgcn_exp2f(st[t][i] - m_ref);
+      psum += pv;
+      const bf16 hi = (bf16)pv;
+      phi[4 * t + i] = hi;
+      plo[4 * t + i] = (bf16)(pv - (float)hi);
+    }
+  S.l_run += psum;
+  const u32x4 pf = __builtin_bit_cast(u32x4, phi), pl = __builtin_bit_cast(u32x4, plo);
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) {
+    S.o[dt] = mfma_frag<T>(b.v[dt][0], pf, S.o[dt]);
+    S.o[dt] = mfma_frag<T>(b.v[dt][0], pl, S.o[dt]);
+  }
+}
+
 // The wave's Q fragments (same channel order as the K fragments).
 template <typename T, int HD>
 __device__ __forceinline__ void load_q(u32x4* qf, const AttnArgs& p, int s, int h, int r, int grp) {
@@ -472,63 +539,8 @@ void attn_partial_lds_kernel(AttnArgs p) {
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) S.o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // One block's update. Scores outside [k_min, k_hi) are masked (a handful
-  // of compares; only the final block and sliding-window layers have any).
   auto update = [&](const KB& b, int n) {
-    const int kb = k_lo + 32 * n;
-    f32x4 st[2];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      st[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int f = 0; f < FR; ++f) st[t] = mfma_frag<T>(b.k[t][f], qf[f], st[t]);
-    }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = kb + key_of<T>(t, 4 * grp + i);
-        const float v = (key < k_hi && key >= k_min) ? st[t][i] * p.scale_log2 : -INFINITY;
-        st[t][i] = v;
-        mx = fmaxf(mx, v);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    if (__any(mx > S.m_run + 8.0f)) {
-      const float m_new = fmaxf(S.m_run, mx);
-      // m_new stays -inf while a query has seen no key (sliding window)
-      const float alpha = m_new == -INFINITY ? 1.0f : exp2f(S.m_run - m_new);
-      S.m_run = m_new;
-      S.l_run *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) S.o[dt] *= alpha;
-    }
-    const float m_ref = S.m_run == -INFINITY ? 0.f : S.m_run;
-    float psum = 0.f;
-    bf16x8 phi, plo;
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        // v_exp_f32: the argument is <= 8; tiny results may flush to 0
-        const float pv = __builtin_amdgcn_exp2f(st[t][i] - m_ref);
-        psum += pv;
-        const bf16 hi = (bf16)pv;
-        phi[4 * t + i] = hi;
-        plo[4 * t + i] = (bf16)(pv - (float)hi);
-      }
-    S.l_run += psum;
-    // P as the sum of two bf16 parts (16 significant bits): the products with
-    // the bf16 values are then as exact as the fp32 sum of probabilities they
-    // are normalised by. Two MFMAs per tile cost nothing here: the kernel
-    // waits on HBM.
-    const u32x4 pf = __builtin_bit_cast(u32x4, phi), pl = __builtin_bit_cast(u32x4, plo);
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
-      S.o[dt] = mfma_frag<T>(b.v[dt][0], pf, S.o[dt]);
-      S.o[dt] = mfma_frag<T>(b.v[dt][0], pl, S.o[dt]);
-    }
+    attn_update_lazy<HD>(S, b, qf, k_lo + 32 * n, k_hi, k_min, p.scale_log2, grp);
   };
 
   // Block n: wait until it has landed and every wave is done with block n-1,
@@ -811,15 +823,194 @@ __global__ __launch_bounds__(512) void packed_attn_kernel(PackedAttnArgs p) {
   }
 }
 
+// bf16 training-pattern attention, query tiles over several blocks: one
+// workgroup per (TB consecutive blocks of a sequence, KV head), one wave per
+// query head of the group holding the TB blocks' queries (TB states). The
+// context prefix up to the tile's largest anchor streams once through an
+// LDS ring (direct global->LDS loads, as in the decoding kernel) and every
+// 32-key block updates each of the tile's blocks whose anchor lies past its
+// start (keys at or after a block's anchor masked). Blocks drawn in anchor
+// order share most of their prefix, so one stream serves TB blocks: TB times
+// fewer K/V reads and TB times the matrix work per LDS read. Then each block
+// attends to its own B keys, gathered from the packed K/V.
+template <int HD, int G, int TB, int NSB = 4>
+__global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(TB <= 2 ? 2 : 1, TB <= 2 ? 2 : 1)))
+void packed_attn_tile_kernel(PackedAttnArgs p, int tiles_per_seq) {
+  using T = bf16;
+  using KB = KVBlock<T, HD>;
+  constexpr int EPF = KB::EPF, FR = KB::FR, NDT = KB::NDT;
+  constexpr int NI = 2 * FR + NDT;
+  constexpr int IPW = NI / G;
+  static_assert(NI % G == 0, "block fragments must split evenly over the group");
+  __shared__ u32x4 ring[NSB][NI][64];
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = lane & 15, grp = lane >> 4;
+  const int g = blockIdx.y, Hq = p.n_heads, Hkv = p.n_kv_heads, B = p.block;
+  const int h = g * G + w;
+  const int s = blockIdx.x / tiles_per_seq, j0 = (blockIdx.x % tiles_per_seq) * TB;
+  const int nt = min(TB, p.blocks_per_seq - j0);
+  const int blk0 = s * p.blocks_per_seq + j0;
+  const int lim = min(max(p.ctx_len[s], 0), p.cap);
+  int a[TB];
+  int kmax = 0;
+#pragma unroll
+  for (int t = 0; t < TB; ++t) {
+    a[t] = 0;
+    if (t < nt) {
+      int v = p.anchors[blk0 + t];
+      if (v < 0 || v > lim) {
+        if (threadIdx.x == 0 && g == 0 && p.dev_status) atomicOr(p.dev_status, DFLASH_DEV_CAPACITY);
+        v = v < 0 ? 0 : lim;
+      }
+      a[t] = v;
+      kmax = max(kmax, v);
+    }
+  }
+
+  u32x4 qf[TB][FR];
+  AttnState<T, HD> S[TB];
+#pragma unroll
+  for (int t = 0; t < TB; ++t) {
+    const T* qp = reinterpret_cast<const T*>(p.q) + (((size_t)(blk0 + t) * B + r) * Hq + h) * HD + grp * EPF;
+#pragma unroll
+    for (int f = 0; f < FR; ++f) qf[t][f] = (t < nt && r < B) ? ld16(qp + f * 4 * EPF) : zero16();
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) S[t].o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+#pragma unroll
+  for (int t = 0; t < TB; ++t)
+#pragma unroll
+    for (int f = 0; f < FR; ++f) asm volatile("" ::"v"(qf[t][f]));
+
+  // Context blocks 0 .. nblk-1 through the ring; fragment sources as in the
+  // decoding kernel (block n = block 0 + n * 32 * HD elements).
+  const int nblk = (kmax + 31) / 32;
+  const size_t kvoff = (size_t)(s * Hkv + g) * p.cap * HD;
+  const T* K = reinterpret_cast<const T*>(p.k) + kvoff;
+  const T* V = reinterpret_cast<const T*>(p.v) + kvoff;
+  if (nblk > 0) {
+    const T* src[IPW];
+#pragma unroll
+    for (int u = 0; u < IPW; ++u) {
+      const int i = w + G * u;
+      if (i < 2 * FR) {
+        const int t = i / FR, f = i % FR;
+        src[u] = K + (size_t)key_of<T>(t, r) * HD + f * 4 * EPF + grp * EPF;
+      } else {
+        const int dt = i - 2 * FR;
+        src[u] = V + (size_t)(16 * dt + r) * kKeyBlock + 8 * grp;
+      }
+    }
+    auto issue = [&](int n, int slot) {
+#pragma unroll
+      for (int u = 0; u < IPW; ++u)
+        __builtin_amdgcn_global_load_lds((attn_gbl_ptr)(src[u] + (size_t)n * 32 * HD),
+                                         (attn_lds_ptr)&ring[slot][w + G * u][0], 16, 0, 0);
+    };
+    const bool whole = nblk <= NSB;
+#pragma unroll
+    for (int n = 0; n < NSB; ++n)
+      if (!whole || n < nblk) issue(min(n, nblk - 1), n);
+    if (whole) attn_wait_barrier<0>();
+    else attn_wait_barrier<IPW * (NSB - 1)>();
+    KB b;
+    for (int n = 0; n < nblk; ++n) {
+      if (n > 0 && !whole) {
+        attn_wait_barrier<IPW * (NSB - 2)>();
+        issue(min(n - 1 + NSB, nblk - 1), (n - 1) % NSB);
+      }
+      const int slot = n % NSB;
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int f = 0; f < FR; ++f) b.k[t][f] = ring[slot][t * FR + f][lane];
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) b.v[dt][0] = ring[slot][2 * FR + dt][lane];
+      const int kb = 32 * n;
+      if (kb + 32 > kmax) {
+        // positions past the largest anchor may lie past the context (cache
+        // slack: anything, even NaN bit patterns); every block masks them
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) b.v[dt][0] = keep_first<T>(b.v[dt][0], kmax - (kb + 8 * grp));
+      }
+#pragma unroll
+      for (int t = 0; t < TB; ++t)
+        if (kb < a[t]) attn_update_lazy<HD>(S[t], b, qf[t], kb, a[t], INT_MIN, p.scale_log2, grp);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+
+  // Each block's own keys as one masked 32-key block.
+  const T* kp = reinterpret_cast<const T*>(p.k_blk);
+  const T* vp = reinterpret_cast<const T*>(p.v_blk);
+#pragma unroll
+  for (int t = 0; t < TB; ++t) {
+    if (t >= nt) break;
+    const size_t bb = (size_t)(blk0 + t) * B;
+    KB b;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int key = key_of<T>(u, r);
+      const T* src = kp + ((bb + key) * Hkv + g) * HD + grp * EPF;
+#pragma unroll
+      for (int f = 0; f < FR; ++f) b.k[u][f] = key < B ? ld16(src + f * 4 * EPF) : zero16();
+    }
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      T vals[EPF];
+#pragma unroll
+      for (int e = 0; e < EPF; ++e) {
+        const int key = 8 * grp + e;
+        vals[e] = key < B ? vp[((bb + key) * Hkv + g) * HD + 16 * dt + r] : from_f32<T>(0.f);
+      }
+      b.v[dt][0] = *reinterpret_cast<const u32x4*>(vals);
+    }
+    attn_update_lazy<HD>(S[t], b, qf[t], 0, B, INT_MIN, p.scale_log2, grp);
+  }
+
+#pragma unroll
+  for (int t = 0; t < TB; ++t) {
+    if (t >= nt) break;
+    float l = S[t].l_run;
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    if (r < B) {
+      const float inv = 1.0f / l;
+      T* out = reinterpret_cast<T*>(p.out) + (((size_t)(blk0 + t) * B + r) * Hq + h) * HD;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) out[16 * dt + 4 * grp + i] = from_f32<T>(S[t].o[dt][i] * inv);
+    }
+  }
+}
+
+template <int HD, int TB>
+static hipError_t launch_packed_tile(const PackedAttnArgs& a, hipStream_t st) {
+  const int G = a.n_heads / a.n_kv_heads;
+  const int tiles = (a.blocks_per_seq + TB - 1) / TB;
+  const dim3 grid((a.n_blk / a.blocks_per_seq) * tiles, a.n_kv_heads);
+  switch (G) {
+    case 1: hipLaunchKernelGGL((packed_attn_tile_kernel<HD, 1, TB>), grid, dim3(64), 0, st, a, tiles); break;
+    case 2: hipLaunchKernelGGL((packed_attn_tile_kernel<HD, 2, TB>), grid, dim3(128), 0, st, a, tiles); break;
+    case 4: hipLaunchKernelGGL((packed_attn_tile_kernel<HD, 4, TB>), grid, dim3(256), 0, st, a, tiles); break;
+    case 8: hipLaunchKernelGGL((packed_attn_tile_kernel<HD, 8, TB>), grid, dim3(512), 0, st, a, tiles); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_packed_attention(int dtype, const PackedAttnArgs& a, hipStream_t st) {
   if (a.n_blk <= 0) return hipSuccess;
   const int G = a.n_heads / a.n_kv_heads;
   if (G > 8 || a.block < 1 || a.block > 16) return hipErrorInvalidValue;
   const dim3 grid(a.n_blk, a.n_kv_heads), block(64 * G);
   if (dtype == DFLASH_BF16) {
-    if (a.head_dim == 128) hipLaunchKernelGGL((packed_attn_kernel<bf16, 128>), grid, block, 0, st, a);
-    else if (a.head_dim == 64) hipLaunchKernelGGL((packed_attn_kernel<bf16, 64>), grid, block, 0, st, a);
-    else return hipErrorInvalidValue;
+    // query tiles of 2 blocks: TB = 4 (one wave per SIMD) ran 1.8x slower, TB = 3 spills
+    if (a.head_dim == 128) return launch_packed_tile<128, 2>(a, st);
+    if (a.head_dim == 64) return launch_packed_tile<64, 2>(a, st);
+    return hipErrorInvalidValue;
   } else {
     if (a.head_dim == 128) hipLaunchKernelGGL((packed_attn_kernel<float, 128>), grid, block, 0, st, a);
     else if (a.head_dim == 64) hipLaunchKernelGGL((packed_attn_kernel<float, 64>), grid, block, 0, st, a);
