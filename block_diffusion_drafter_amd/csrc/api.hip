@@ -238,6 +238,14 @@ GemmArgs gemm_tiled(const void* a, const void* w, int M, int N, int K, const voi
   return g;
 }
 
+// Asks a residual projection's K-slice reduce for the RMSNorm of its rows too.
+void set_norm(GemmArgs& g, const void* gain, void* out, int nck, float eps) {
+  g.norm_w = gain;
+  g.norm_out = out;
+  g.norm_nck = nck;
+  g.norm_eps = eps;
+}
+
 // A projection of caller-provided row-major rows (stride a_stride elements).
 GemmArgs gemm_rows(const void* a, int64_t a_stride, const void* w, int M, int N, int K) {
   GemmArgs g = gemm_tiled(a, w, M, N, K);
@@ -578,9 +586,12 @@ int32_t dflash_draft_forward(const dflash_handle* h, const dflash_kv_cache* cach
   prof_end(st);
   if (e != hipSuccess) return DFLASH_ERR_HIP;
 
+  // Layer 0's pre-norm came with the embedding; a later layer's comes with
+  // the previous down projection when that one reduces K slices.
+  bool pre_normed = true;
   for (int l = 0; l < L; ++l) {
     const dflash_layer_weights& lw = h->layers[l];
-    if (l > 0) {  // layer 0's pre-norm came with the embedding
+    if (!pre_normed) {
       prof_begin(DFLASH_K_RMSNORM, 0, 0, st);
       e = launch_rmsnorm(c.dtype, x, d, lw.in_norm, hbuf, 0, nck_d, M, d, c.rms_eps, M, 0, 0, st);
       prof_end(st);
@@ -652,12 +663,16 @@ int32_t dflash_draft_forward(const dflash_handle* h, const dflash_kv_cache* cach
     g.part_elems = P.part_elems;
     g.resid = x;
     g.out_stride = d;
+    const bool post_fused = gemm_fuses_norm(c.dtype, g);
+    if (post_fused) set_norm(g, lw.post_norm, hbuf, nck_d, c.rms_eps);
     if ((rc = run_gemm(c.dtype, EPI_RESID, g, st))) return rc;
 
-    prof_begin(DFLASH_K_RMSNORM, 0, 0, st);
-    e = launch_rmsnorm(c.dtype, x, d, lw.post_norm, hbuf, 0, nck_d, M, d, c.rms_eps, M, 0, 0, st);
-    prof_end(st);
-    if (e != hipSuccess) return DFLASH_ERR_HIP;
+    if (!post_fused) {
+      prof_begin(DFLASH_K_RMSNORM, 0, 0, st);
+      e = launch_rmsnorm(c.dtype, x, d, lw.post_norm, hbuf, 0, nck_d, M, d, c.rms_eps, M, 0, 0, st);
+      prof_end(st);
+      if (e != hipSuccess) return DFLASH_ERR_HIP;
+    }
 
     g = gemm_tiled(hbuf, pk + pl.gate[l], M, I, d, pk + pl.up[l]);
     g.out = act;
@@ -668,6 +683,8 @@ int32_t dflash_draft_forward(const dflash_handle* h, const dflash_kv_cache* cach
     g.part_elems = P.part_elems;
     g.resid = x;
     g.out_stride = d;
+    pre_normed = l + 1 < L && gemm_fuses_norm(c.dtype, g);
+    if (pre_normed) set_norm(g, h->layers[l + 1].in_norm, hbuf, nck_d, c.rms_eps);
     if ((rc = run_gemm(c.dtype, EPI_RESID, g, st))) return rc;
 
     if (hidden_out) {

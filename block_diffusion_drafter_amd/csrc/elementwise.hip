@@ -46,21 +46,16 @@ template <> __device__ __forceinline__ void store4<bf16>(bf16* y, float4 v) {
   *reinterpret_cast<uint2*>(y) = __builtin_bit_cast(uint2, b);
 }
 
-// One row per workgroup, VPT float4 per thread held in registers: one load
-// pass, one block reduction, one store pass (d <= 4 * 256 * VPT). Output row
-// yrow of y: row-major with stride ys when nck == 0, else tiled with nck
-// chunks per row (four consecutive elements stay contiguous in both).
+// RMSNorm of one row whose values thread t holds in v[u] (elements
+// 4 (t + 256 u) .. +3, zero past d): one block reduction, one store pass.
+// Output row yrow of y: row-major with stride ys when nck == 0, else tiled
+// with nck chunks per row (four consecutive elements stay contiguous in both).
 template <typename T, int VPT>
-__device__ __forceinline__ void rmsnorm_row(const float* xr, const T* gain, T* y, int yrow,
-                                            int64_t ys, int nck, int d, float eps, float* sh) {
-  float4 v[VPT];
+__device__ __forceinline__ void rmsnorm_regs(const float4 (&v)[VPT], const T* gain, T* y, int yrow,
+                                             int64_t ys, int nck, int d, float eps, float* sh) {
   float ss = 0.f;
 #pragma unroll
-  for (int u = 0; u < VPT; ++u) {
-    const int k = 4 * (threadIdx.x + u * blockDim.x);
-    v[u] = k < d ? *reinterpret_cast<const float4*>(xr + k) : make_float4(0.f, 0.f, 0.f, 0.f);
-    ss += v[u].x * v[u].x + v[u].y * v[u].y + v[u].z * v[u].z + v[u].w * v[u].w;
-  }
+  for (int u = 0; u < VPT; ++u) ss += v[u].x * v[u].x + v[u].y * v[u].y + v[u].z * v[u].z + v[u].w * v[u].w;
   ss = block_sum(ss, sh);
   const float inv = rsqrtf(ss / (float)d + eps);
 #pragma unroll
@@ -73,6 +68,20 @@ __device__ __forceinline__ void rmsnorm_row(const float* xr, const T* gain, T* y
                                  v[u].w * inv * g.w));
     }
   }
+}
+
+// One row per workgroup, VPT float4 per thread held in registers: one load
+// pass, then rmsnorm_regs (d <= 4 * 256 * VPT).
+template <typename T, int VPT>
+__device__ __forceinline__ void rmsnorm_row(const float* xr, const T* gain, T* y, int yrow,
+                                            int64_t ys, int nck, int d, float eps, float* sh) {
+  float4 v[VPT];
+#pragma unroll
+  for (int u = 0; u < VPT; ++u) {
+    const int k = 4 * (threadIdx.x + u * blockDim.x);
+    v[u] = k < d ? *reinterpret_cast<const float4*>(xr + k) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  rmsnorm_regs<T, VPT>(v, gain, y, yrow, ys, nck, d, eps, sh);
 }
 
 // y[r] = x[src(r)] / sqrt(mean(x^2) + eps) * gain, statistics in fp32.
@@ -111,6 +120,74 @@ hipError_t launch_rmsnorm(int dtype, const float* x, int64_t x_stride, const voi
   else
     launch_rmsnorm_t<float>(x, x_stride, (const float*)gain, (float*)y, y_stride, y_nck, rows, d,
                             eps, rpg, grp_stride, grp_off, st);
+  return hipGetLastError();
+}
+
+// End of a residual projection split over K: x[m] += sum of the ks fp32
+// partials of row m (slice order, then the residual, as splitk_reduce_kernel
+// sums), and the RMSNorm of the updated row into y (tiled, nck chunks per
+// row): the next projection's normalised input, without a second pass over x.
+template <int VPT>
+__global__ __launch_bounds__(256) void splitk_reduce_norm_kernel(const float* __restrict__ part,
+                                                                 int ks, int M, int N,
+                                                                 float* __restrict__ x, int64_t xs,
+                                                                 const bf16* gain, bf16* y, int nck,
+                                                                 float eps) {
+  __shared__ float sh[4];
+  const int m = blockIdx.x;
+  const int64_t MN = (int64_t)M * N;
+  // Every load of the row goes out before the first store (ks <= kMfmaMaxSplit).
+  float4 v[VPT], r[VPT];
+  float4 q[VPT][kMfmaMaxSplit];
+#pragma unroll
+  for (int u = 0; u < VPT; ++u) {
+    const int k = 4 * (threadIdx.x + u * blockDim.x);
+    const float* pp = part + (int64_t)m * N + k;
+#pragma unroll
+    for (int z = 0; z < kMfmaMaxSplit; ++z)
+      q[u][z] = k < N && z < ks ? *reinterpret_cast<const float4*>(pp + z * MN)
+                                : make_float4(0.f, 0.f, 0.f, 0.f);
+    r[u] = k < N ? *reinterpret_cast<const float4*>(x + (int64_t)m * xs + k)
+                 : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+#pragma unroll
+  for (int u = 0; u < VPT; ++u) {
+    float4 acc = q[u][0];
+#pragma unroll
+    for (int z = 1; z < kMfmaMaxSplit; ++z) {
+      if (z < ks) {
+        acc.x += q[u][z].x;
+        acc.y += q[u][z].y;
+        acc.z += q[u][z].z;
+        acc.w += q[u][z].w;
+      }
+    }
+    acc.x += r[u].x;
+    acc.y += r[u].y;
+    acc.z += r[u].z;
+    acc.w += r[u].w;
+    v[u] = acc;
+    const int k = 4 * (threadIdx.x + u * blockDim.x);
+    if (k < N) *reinterpret_cast<float4*>(x + (int64_t)m * xs + k) = acc;
+  }
+  rmsnorm_regs<bf16, VPT>(v, gain, y, m, 0, nck, N, eps, sh);
+}
+
+hipError_t launch_splitk_reduce_norm(const float* part, int ks, int M, int N, float* x,
+                                     int64_t x_stride, const void* gain, void* y, int y_nck,
+                                     float eps, hipStream_t st) {
+  if (M <= 0) return hipSuccess;
+  if (N > 8192 || N % 4 || x_stride % 4 || ks < 1 || ks > kMfmaMaxSplit) return hipErrorInvalidValue;
+  const int vpt = (N + 1023) / 1024;
+  dim3 grid(M), block(256);
+#define DF_RN(V)                                                                               \
+  hipLaunchKernelGGL((splitk_reduce_norm_kernel<V>), grid, block, 0, st, part, ks, M, N, x,   \
+                     x_stride, (const bf16*)gain, (bf16*)y, y_nck, eps)
+  if (vpt <= 1) DF_RN(1);
+  else if (vpt <= 2) DF_RN(2);
+  else if (vpt <= 4) DF_RN(4);
+  else DF_RN(8);
+#undef DF_RN
   return hipGetLastError();
 }
 

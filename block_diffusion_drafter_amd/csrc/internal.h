@@ -56,6 +56,13 @@ struct GemmArgs {
   float* part;
   int64_t part_elems;
   int ksplit;                     // K slices of an MFMA launch (set by its launcher)
+  // EPI_RESID on the MFMA path with K slices (gemm_fuses_norm): the reduce of
+  // the slices also writes RMSNorm(resid row; norm_w) to norm_out, tiled bf16
+  // with norm_nck chunks per row. Ignored (nullptr) otherwise.
+  const void* norm_w;
+  void* norm_out;
+  int norm_nck;
+  float norm_eps;
 };
 
 // Launch geometry of one weight-streaming GEMM (also used to size LM-head partials).
@@ -88,6 +95,12 @@ int mfma_gemm_colblocks(int epi, int M, int N, int K);
 // K slices the MFMA kernel splits a projection into (1 = no split); the
 // partial buffer it then needs is ksplit * M * N floats.
 int mfma_gemm_ksplit(int epi, int M, int N, int K);
+// Whether a residual projection with these arguments ends in a K-slice
+// reduce that can also write the RMSNorm of the updated rows (norm_w).
+bool gemm_fuses_norm(int dtype, const GemmArgs& a);
+hipError_t launch_splitk_reduce_norm(const float* part, int ks, int M, int N, float* x,
+                                     int64_t x_stride, const void* gain, void* y, int y_nck,
+                                     float eps, hipStream_t st);
 // Keys per row that the LM-head projection writes (its column blocks).
 int gemm_amax_cols(int dtype, int M, int N, int K);
 
