@@ -438,6 +438,13 @@ def bench_packed(a) -> int:
         for l in range(L):
             model.packed_block_attention(cache, l, anc, q, kb, vb, out, status)
 
+    if a.copy_probe:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     for _ in range(a.warmup):
         step()
     torch.cuda.synchronize()
@@ -465,7 +472,8 @@ def bench_packed(a) -> int:
                    "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "mfma", "achieved": round(flops / t / 1e12, 1),
                      "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(flops / t / 1e12 / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "frac": round(flops / t / 1e12 / BF16_PEAK_TFLOPS, 4),
+                     "traffic": measured_traffic(name, "attention_packed"),
                      "kernel_class": "attention_packed",
                      "context_rows_streamed_TBps": round(ctx_bytes / t / 1e12, 2),
                      "unique_hbm_bytes_per_step": int(uniq),
