@@ -258,8 +258,10 @@ __device__ __forceinline__ void attn_update(AttnState<T, HD>& S, const KVBlock<T
 // accumulators are rarely touched outside the MFMAs). P enters the PV product
 // as the sum of two bf16 parts (16 significant bits), so the products are as
 // exact as the fp32 sum of probabilities they are normalised by; the second
-// MFMA per tile is free where the kernel waits on memory.
-template <int HD>
+// MFMA per tile is free where the kernel waits on memory. SPLIT = false keeps
+// P's high part only (8 significant bits, as training attention kernels do),
+// a third fewer MFMAs where the kernel waits on them instead.
+template <int HD, bool SPLIT = true>
 __device__ __forceinline__ void attn_update_lazy(AttnState<bf16, HD>& S,
                                                  const KVBlock<bf16, HD>& b, const u32x4* qf,
                                                  int kb, int k_hi, int k_min, float scale_log2,
@@ -306,14 +308,16 @@ __device__ __forceinline__ void attn_update_lazy(AttnState<bf16, HD>& S,
       psum += pv;
       const bf16 hi = (bf16)pv;
       phi[4 * t + i] = hi;
-      plo[4 * t + i] = (bf16)(pv - (float)hi);
+      if constexpr (SPLIT) plo[4 * t + i] = (bf16)(pv - (float)hi);
     }
   S.l_run += psum;
-  const u32x4 pf = __builtin_bit_cast(u32x4, phi), pl = __builtin_bit_cast(u32x4, plo);
+  const u32x4 pf = __builtin_bit_cast(u32x4, phi);
 #pragma unroll
-  for (int dt = 0; dt < NDT; ++dt) {
-    S.o[dt] = mfma_frag<T>(b.v[dt][0], pf, S.o[dt]);
-    S.o[dt] = mfma_frag<T>(b.v[dt][0], pl, S.o[dt]);
+  for (int dt = 0; dt < NDT; ++dt) S.o[dt] = mfma_frag<T>(b.v[dt][0], pf, S.o[dt]);
+  if constexpr (SPLIT) {
+    const u32x4 pl = __builtin_bit_cast(u32x4, plo);
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) S.o[dt] = mfma_frag<T>(b.v[dt][0], pl, S.o[dt]);
   }
 }
 
@@ -936,7 +940,7 @@ void packed_attn_tile_kernel(PackedAttnArgs p, int tiles_per_seq) {
       }
 #pragma unroll
       for (int t = 0; t < TB; ++t)
-        if (kb < a[t]) attn_update_lazy<HD>(S[t], b, qf[t], kb, a[t], INT_MIN, p.scale_log2, grp);
+        if (kb < a[t]) attn_update_lazy<HD, false>(S[t], b, qf[t], kb, a[t], INT_MIN, p.scale_log2, grp);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
@@ -966,7 +970,7 @@ void packed_attn_tile_kernel(PackedAttnArgs p, int tiles_per_seq) {
       }
       b.v[dt][0] = *reinterpret_cast<const u32x4*>(vals);
     }
-    attn_update_lazy<HD>(S[t], b, qf[t], 0, B, INT_MIN, p.scale_log2, grp);
+    attn_update_lazy<HD, false>(S[t], b, qf[t], 0, B, INT_MIN, p.scale_log2, grp);
   }
 
 #pragma unroll
