@@ -108,7 +108,7 @@ PackedLayout packed_layout(const dflash_config& c) {
 }
 
 struct Plan {
-  size_t x, h, qkv, q, po, pml, attn, act, y, amax, arr, part, fwd_end;
+  size_t x, h, qkv, q, po, pml, attn, act, y, amax, arr, part, sq, fwd_end;
   size_t u, ua, upart, proj_end;  // ua: tiled copy of the fused features (MFMA path)
   size_t kv, ca, kvpart, app_end;  // ca: tiled copy of the context rows (MFMA path)
   int64_t part_elems, upart_elems, kvpart_elems;  // split-K partials (floats)
@@ -176,6 +176,8 @@ Plan make_plan(const dflash_config& c, int batch, int cap, int max_tokens) {
                              splitk_elems(dt, EPI_RESID, Mi, (int)d, (int)I)});
     p.part = take((size_t)p.part_elems * 4);
   }
+  // Per-tile row sums of squares of a deferred norm (weight-streaming path).
+  p.sq = take((((d + 15) / 16 + 3) & ~(size_t)3) * M * 4);
   p.fwd_end = off;
   off = 0;
   p.u = take((size_t)max_tokens * d * 4);
@@ -244,6 +246,25 @@ void set_norm(GemmArgs& g, const void* gain, void* out, int nck, float eps) {
   g.norm_out = out;
   g.norm_nck = nck;
   g.norm_eps = eps;
+}
+
+// A projection whose tiled A rows hold x * gain of a deferred RMSNorm: it
+// scales each output row by the norm's 1/rms (from the producer's per-tile
+// sums of squares of the d-wide rows).
+void take_norm(GemmArgs& g, const float* sq, int d, float eps) {
+  g.sq_in = sq;
+  g.sq_d = d;
+  g.norm_eps = eps;
+}
+
+// Whether the norm between a residual projection of M rows (inner size K)
+// and the next projection (inner size d) is deferred: both on the
+// weight-streaming kernel with one 16-row tile (each consumer workgroup then
+// reads only its 16 rows' d/16 partial sums, issued ahead of its weight
+// stream); at more rows those reads cost more than the norm's own pass.
+bool streams_both(int M, int K, int d) {
+  return M <= 16 && !gemm_uses_mfma(DFLASH_BF16, M, K, true) &&
+         !gemm_uses_mfma(DFLASH_BF16, M, d, true);
 }
 
 // A projection of caller-provided row-major rows (stride a_stride elements).
@@ -586,12 +607,18 @@ int32_t dflash_draft_forward(const dflash_handle* h, const dflash_kv_cache* cach
   prof_end(st);
   if (e != hipSuccess) return DFLASH_ERR_HIP;
 
-  // Layer 0's pre-norm came with the embedding; a later layer's comes with
-  // the previous down projection when that one reduces K slices.
-  bool pre_normed = true;
+  // The pre-norm of layer 0 came with the embedding; a later layer's comes
+  // with the previous down projection: written normalised when that one
+  // reduces K slices (MFMA path), or deferred on the weight-streaming path
+  // (the down projection writes x * gain and the rows' sums of squares, the
+  // QKV projection scales its rows).
+  float* sq = reinterpret_cast<float*>(w + P.sq);
+  const bool bf = c.dtype == DFLASH_BF16;
+  enum { kNormNone, kNormDone, kNormDeferred };
+  int pre_norm = kNormDone;
   for (int l = 0; l < L; ++l) {
     const dflash_layer_weights& lw = h->layers[l];
-    if (!pre_normed) {
+    if (pre_norm == kNormNone) {
       prof_begin(DFLASH_K_RMSNORM, 0, 0, st);
       e = launch_rmsnorm(c.dtype, x, d, lw.in_norm, hbuf, 0, nck_d, M, d, c.rms_eps, M, 0, 0, st);
       prof_end(st);
@@ -605,6 +632,7 @@ int32_t dflash_draft_forward(const dflash_handle* h, const dflash_kv_cache* cach
     g.part_elems = P.part_elems;
     g.out = qkv;
     g.out_stride = Nqkv;
+    if (pre_norm == kNormDeferred) take_norm(g, sq, d, c.rms_eps);
     if ((rc = run_gemm(c.dtype, EPI_STORE_F32, g, st))) return rc;
 
     NormRopeArgs nr;
@@ -664,10 +692,12 @@ int32_t dflash_draft_forward(const dflash_handle* h, const dflash_kv_cache* cach
     g.resid = x;
     g.out_stride = d;
     const bool post_fused = gemm_fuses_norm(c.dtype, g);
-    if (post_fused) set_norm(g, lw.post_norm, hbuf, nck_d, c.rms_eps);
+    const bool post_deferred = !post_fused && bf && streams_both(M, Hq * hd, d);
+    if (post_fused || post_deferred) set_norm(g, lw.post_norm, hbuf, nck_d, c.rms_eps);
+    if (post_deferred) g.sq_out = sq;
     if ((rc = run_gemm(c.dtype, EPI_RESID, g, st))) return rc;
 
-    if (!post_fused) {
+    if (!post_fused && !post_deferred) {
       prof_begin(DFLASH_K_RMSNORM, 0, 0, st);
       e = launch_rmsnorm(c.dtype, x, d, lw.post_norm, hbuf, 0, nck_d, M, d, c.rms_eps, M, 0, 0, st);
       prof_end(st);
@@ -676,6 +706,7 @@ int32_t dflash_draft_forward(const dflash_handle* h, const dflash_kv_cache* cach
 
     g = gemm_tiled(hbuf, pk + pl.gate[l], M, I, d, pk + pl.up[l]);
     g.out = act;
+    if (post_deferred) take_norm(g, sq, d, c.rms_eps);
     if ((rc = run_gemm(c.dtype, EPI_SWIGLU, g, st))) return rc;
 
     g = gemm_tiled(act, pk + pl.down[l], M, d, I);
@@ -683,8 +714,13 @@ int32_t dflash_draft_forward(const dflash_handle* h, const dflash_kv_cache* cach
     g.part_elems = P.part_elems;
     g.resid = x;
     g.out_stride = d;
-    pre_normed = l + 1 < L && gemm_fuses_norm(c.dtype, g);
-    if (pre_normed) set_norm(g, h->layers[l + 1].in_norm, hbuf, nck_d, c.rms_eps);
+    pre_norm = kNormNone;
+    if (l + 1 < L) {
+      if (gemm_fuses_norm(c.dtype, g)) pre_norm = kNormDone;
+      else if (bf && streams_both(M, I, d)) pre_norm = kNormDeferred;
+    }
+    if (pre_norm != kNormNone) set_norm(g, h->layers[l + 1].in_norm, hbuf, nck_d, c.rms_eps);
+    if (pre_norm == kNormDeferred) g.sq_out = sq;
     if ((rc = run_gemm(c.dtype, EPI_RESID, g, st))) return rc;
 
     if (hidden_out) {

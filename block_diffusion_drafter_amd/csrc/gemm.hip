@@ -61,6 +61,12 @@ void gemm_stream_kernel(GemmArgs p) {
   constexpr int P = gemm_stages(MT, NB * NT);
   extern __shared__ f32x4 red[];  // [ksplit][NB][MT*NT][64]
   __shared__ unsigned long long kred[EPI == EPI_ARGMAX ? MT * 16 * NT : 1];
+  // Deferred RMSNorm of the A rows (sq_in): per-thread partial sums, then the
+  // rows' scales.
+  constexpr bool SQ = (EPI == EPI_STORE_F32 || EPI == EPI_SWIGLU) && MT == 1;
+  constexpr int SQV = 2;  // float4 partials a thread holds: tiles <= 4 * SQV * threads / 16
+  __shared__ float sq_part[SQ ? 1024 : 1];
+  __shared__ float row_inv[SQ ? 16 * MT : 1];
 
   const int lane = threadIdx.x & 63;
   // Wave-uniform values live in scalar registers: chunk indices derived from
@@ -72,6 +78,22 @@ void gemm_stream_kernel(GemmArgs p) {
   const int n_tiles = (p.N + 15) >> 4;
   const int tile0 = blockIdx.x * NT;
   const int m_base = blockIdx.y * (16 * MT);
+
+  // Deferred norm (one m-tile): thread t loads the tile partials 4 j .. 4 j + 3,
+  // j = t / 16 + u * nparts (u < SQV), of row t % 16 now, ahead of the weight
+  // stream, and adds them after the main loop (so no wait on them before it).
+  float4 sqv[SQ ? SQV : 1];
+  if constexpr (SQ) {
+    const int nparts = (int)blockDim.x / 16, part = threadIdx.x / 16;
+    const int m = m_base + (int)(threadIdx.x % 16), tiles4 = (((p.sq_d + 15) >> 4) + 3) >> 2;
+#pragma unroll
+    for (int u = 0; u < SQV; ++u) {
+      const int j = part + u * nparts;
+      sqv[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (p.sq_in && m < p.M && j < tiles4)
+        sqv[u] = *reinterpret_cast<const float4*>(p.sq_in + ((int64_t)m * tiles4 + j) * 4);
+    }
+  }
 
   // Weight fragments of the lane in each n-tile. Tiles past the last one
   // re-read the last tile (valid memory); their columns are never stored.
@@ -207,7 +229,40 @@ void gemm_stream_kernel(GemmArgs p) {
 #pragma unroll
       for (int t = 0; t < NT; ++t)
         red[((wave * NB + b) * PAIRS + mt * NT + t) * 64 + lane] = acc[b][mt][t];
+  if constexpr (SQ) {
+    if (p.sq_in) {
+      const int nparts = (int)blockDim.x / 16, part = threadIdx.x / 16;
+      const int tiles = (p.sq_d + 15) >> 4;
+      float sq_acc = 0.f;
+#pragma unroll
+      for (int u = 0; u < SQV; ++u) {
+        const int j = 4 * (part + u * nparts);
+        sq_acc += (j < tiles ? sqv[u].x : 0.f) + (j + 1 < tiles ? sqv[u].y : 0.f) +
+                  (j + 2 < tiles ? sqv[u].z : 0.f) + (j + 3 < tiles ? sqv[u].w : 0.f);
+      }
+      // Partials beyond what the registers held (few threads, wide rows).
+      const int m = m_base + (int)(threadIdx.x % 16), tiles4 = (tiles + 3) >> 2;
+      for (int j4 = part + SQV * nparts; m < p.M && j4 < tiles4; j4 += nparts) {
+        const float4 q = *reinterpret_cast<const float4*>(p.sq_in + ((int64_t)m * tiles4 + j4) * 4);
+        const int j = 4 * j4;
+        sq_acc += q.x + (j + 1 < tiles ? q.y : 0.f) + (j + 2 < tiles ? q.z : 0.f) +
+                  (j + 3 < tiles ? q.w : 0.f);
+      }
+      sq_part[threadIdx.x] = sq_acc;
+    }
+  }
   __syncthreads();
+  if constexpr (SQ) {
+    if (p.sq_in) {
+      const int rows_wg = 16 * MT, nparts = (int)blockDim.x / rows_wg;
+      if ((int)threadIdx.x < rows_wg) {
+        float ss = 0.f;
+        for (int k = 0; k < nparts; ++k) ss += sq_part[k * rows_wg + threadIdx.x];
+        row_inv[threadIdx.x] = rsqrtf(ss / (float)p.sq_d + p.norm_eps);
+      }
+      __syncthreads();
+    }
+  }
 
   // Wave w finishes output tiles w, w + ksplit, ... of the MT x NT grid.
   for (int pi = wave; pi < PAIRS; pi += ksplit) {
@@ -221,15 +276,47 @@ void gemm_stream_kernel(GemmArgs p) {
     const int m0 = m_base + 16 * mt + 4 * grp;
     const int n = 16 * (tile0 + t) + r;
     const bool nok = n < p.N;
+    if constexpr (SQ) {
+      if (p.sq_in) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float s = row_inv[16 * mt + 4 * grp + i];
+#pragma unroll
+          for (int b = 0; b < NB; ++b) v[b][i] *= s;
+        }
+      }
+    }
     if constexpr (EPI == EPI_STORE_F32) {
       float* out = reinterpret_cast<float*>(p.out);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         if (m0 + i < p.M && nok) out[(int64_t)(m0 + i) * p.out_stride + n] = v[0][i];
     } else if constexpr (EPI == EPI_RESID) {
+      float xn[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (m0 + i < p.M && nok) p.resid[(int64_t)(m0 + i) * p.out_stride + n] += v[0][i];
+      for (int i = 0; i < 4; ++i) {
+        xn[i] = 0.f;
+        if (m0 + i < p.M && nok) {
+          float* px = p.resid + (int64_t)(m0 + i) * p.out_stride + n;
+          xn[i] = *px + v[0][i];
+          *px = xn[i];
+        }
+      }
+      if (p.sq_out) {
+        // The next norm's input, bf16(x * gain) tiled, and each row's sum of
+        // squares over this tile's 16 columns (lanes r = 0..15 of a group).
+        const float gain = nok ? to_f32(reinterpret_cast<const T*>(p.norm_w)[n]) : 0.f;
+        T* hn = reinterpret_cast<T*>(p.norm_out);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (m0 + i < p.M && nok) hn[tiled_index<T>(m0 + i, n, p.norm_nck)] = from_f32<T>(xn[i] * gain);
+          float sq = xn[i] * xn[i];
+#pragma unroll
+          for (int o = 1; o < 16; o <<= 1) sq += __shfl_xor(sq, o);
+          if (r == 0 && m0 + i < p.M && tile0 + t < n_tiles)
+            p.sq_out[(int64_t)(m0 + i) * ((n_tiles + 3) & ~3) + tile0 + t] = sq;
+        }
+      }
     } else if constexpr (EPI == EPI_SWIGLU) {
       // Tiled output [M, N]: the A operand of the down projection.
       T* out = reinterpret_cast<T*>(p.out);

@@ -63,6 +63,17 @@ struct GemmArgs {
   void* norm_out;
   int norm_nck;
   float norm_eps;
+  // Weight-streaming path (bf16), the next RMSNorm deferred to its consumer:
+  // an EPI_RESID projection with sq_out also writes bf16(x_new * norm_w)
+  // tiled to norm_out and, for every 16-column tile j < T = ceil(N / 16) of
+  // its output and row m, the sum of x_new^2 over the tile to
+  // sq_out[m * T4 + j] (T4 = T rounded up to a multiple of 4; entries T..T4-1
+  // unused); a projection with sq_in (its A operand such a norm_out) scales
+  // output row m by 1 / sqrt(sum over j < T of sq_in[m * T4 + j] / sq_d +
+  // norm_eps), T from sq_d. Unused: nullptr.
+  float* sq_out;
+  const float* sq_in;
+  int sq_d;
 };
 
 // Launch geometry of one weight-streaming GEMM (also used to size LM-head partials).
