@@ -126,7 +126,9 @@ def main() -> int:
     ctx_lens = I.ctx_lengths(W)
     max_new = cfg.block_size  # a round appends a + 1 <= B rows
     n_prof = max(3, min(10, a.steps))
-    total_steps = a.warmup + n_prof + a.steps + (2 * (a.warmup + a.steps) if a.graph else 0)
+    n_dist, n_cold = min(a.steps, 20), min(a.steps, 10)  # per-step spread; cold-MALL steps
+    total_steps = (a.warmup + n_prof + a.steps + n_dist + n_cold +
+                   (2 * (a.warmup + a.steps) if a.graph else 0))
     cap = int(((int(ctx_lens.max()) + max_new * total_steps + Bk + 31) // 32) * 32)
     print(f"[bench] workload {W.name}: batch {b}, ctx {int(ctx_lens.min())}-{int(ctx_lens.max())}, "
           f"capacity {cap}", file=sys.stderr, flush=True)
@@ -250,9 +252,42 @@ def main() -> int:
     B.profiler_stop()
     ms_step = e0.elapsed_time(e1) / a.steps
     dom = read_profile(a.steps, ctx1)[dom_name]
-    ctx_end = cache.ctx_len.cpu().numpy().astype(np.int64)
     assert status.item() == 0, f"device status {status.item()}"
     value = b * Bk / (ms_step / 1e3)
+
+    # ---- after the headline: per-step spread, then steps with the 256 MB MALL
+    # flushed by a 1 GiB read-modify-write before each; and a 1 GiB device copy
+    # as a measured HBM reference ---------------------------------------------
+    def timed_steps(n, before=None):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(n)]
+        for s0, s1 in ev:
+            if before is not None:
+                before()
+            s0.record()
+            step()
+            s1.record()
+        torch.cuda.synchronize()
+        return sorted(s0.elapsed_time(s1) for s0, s1 in ev)
+
+    spread = timed_steps(n_dist)
+    scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    cold = timed_steps(n_cold, before=lambda: scratch.add_(1))
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    dst = torch.empty_like(scratch)
+    dst.copy_(scratch)
+    c0.record()
+    for _ in range(3):
+        dst.copy_(scratch)
+    c1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 3 * 2 * (1 << 30) / (c0.elapsed_time(c1) / 1e3) / 1e9
+    del scratch, dst
+    ctx_end = cache.ctx_len.cpu().numpy().astype(np.int64)
+    assert status.item() == 0, f"device status {status.item()}"
+
+    def pct(v, q):
+        return round(float(np.percentile(np.asarray(v), q)), 5)
 
     ridge = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
     t_dom = dom["ms"] / 1e3
@@ -260,7 +295,8 @@ def main() -> int:
     tfl = dom["flops"] / t_dom / 1e12
     if dom["flops"] / max(dom["bytes"], 1.0) <= ridge:
         roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(gbs / HBM_PEAK_GBS, 4)}
+                "frac": round(gbs / HBM_PEAK_GBS, 4),
+                "frac_of_measured_copy": round(gbs / copy_gbs, 4)}
     else:
         roof = {"bound": "mfma", "achieved": round(tfl, 1), "peak": BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(tfl / BF16_PEAK_TFLOPS, 4)}
@@ -299,6 +335,13 @@ def main() -> int:
                           "peaks": {"hbm_GBps": HBM_PEAK_GBS, "bf16_TFLOPs": BF16_PEAK_TFLOPS}},
         "kernels_event_bracketed": kernels,
         "wall_s_timed": round(wall, 4),
+        "drafted_tokens_per_s": round(b * (Bk - 1) / (ms_step / 1e3), 1),
+        "ms_per_step_spread": {"steps": n_dist, "p10": pct(spread, 10), "p50": pct(spread, 50),
+                               "p90": pct(spread, 90)},
+        "ms_per_step_cold_mall": {"steps": n_cold, "p50": pct(cold, 50),
+                                  "note": "1 GiB read-modify-write before each step, outside "
+                                          "its events"},
+        "measured_hbm_copy_GBps": round(copy_gbs, 1),
     }
 
     if a.graph:
