@@ -147,6 +147,13 @@ def test_gpu_small_bf16_block8_two_layers():
     run_flow(SMALL_BF16.with_(block_size=8), [77, 200], "small-b8")
 
 
+def test_gpu_small_bf16_batch1_hidden480():
+    # One 16-row tile: the norms between projections are deferred to the
+    # consumer; hidden 480 leaves 30 column tiles, so the consumer's float4
+    # reads of the per-tile sums end in a partly used group.
+    run_flow(SMALL_BF16.with_(hidden=480), [150], "small-h480")
+
+
 def test_gpu_qwen3_8b_shaped_batch1_ctx2048():
     run_flow(QWEN3_8B_SHAPED, [2048], "q1")
 
