@@ -90,6 +90,19 @@ def test_gpu_packed_small_bf16_ragged():
     run_packed(cfg, ctx, anc, "small")
 
 
+def test_gpu_packed_bf16_head_dim64_odd_blocks():
+    # head_dim 64, two query heads per KV head, block 10 and an odd number of
+    # blocks per sequence (the last query tile holds one block); anchors at 0
+    # and at the full context
+    cfg = SMALL_BF16.with_(head_dim=64, n_kv_heads=4, block_size=10)
+    ctx = [200, 333]
+    anc = np.stack([I.training_anchors(c, 23, c // 4, seed=7, tag=f"hd64-{s}")
+                    for s, c in enumerate(ctx)])
+    anc[0, 0] = 0
+    anc[1, -1] = ctx[1]
+    run_packed(cfg, ctx, np.sort(anc, axis=1), "small-hd64")
+
+
 def test_gpu_packed_anchor_past_context_is_clamped_and_flagged():
     run_packed(TINY_FP32, [32], [[5, 33]], "tiny-clamp", expect_flag=True)
 
