@@ -147,6 +147,14 @@ def test_gpu_small_bf16_block8_two_layers():
     run_flow(SMALL_BF16.with_(block_size=8), [77, 200], "small-b8")
 
 
+def test_gpu_small_bf16_gqa_groups_1_and_8():
+    # bf16 attention with one query head per KV head (MHA) and with eight
+    # (a KV group of 8 waves sharing each LDS block), contexts spanning one
+    # and several workgroup ranges
+    run_flow(SMALL_BF16.with_(n_kv_heads=8), [40, 900], "small-mha")
+    run_flow(SMALL_BF16.with_(n_heads=16, n_kv_heads=2), [700, 33], "small-g8")
+
+
 def test_gpu_small_bf16_batch1_hidden480():
     # One 16-row tile: the norms between projections are deferred to the
     # consumer; hidden 480 leaves 30 column tiles, so the consumer's float4
