@@ -107,6 +107,15 @@ PackedLayout packed_layout(const dflash_config& c) {
   return p;
 }
 
+// Whether caller rows (features, context rows) are first copied into the
+// tiled layout: always for the MFMA kernel; on the weight-streaming kernel
+// from two 16-row tiles up (bf16), where reading several row-major rows per
+// wave costs as much as the weight stream itself (37 rows: 2.0 TB/s for the
+// context K/V projection against 3.4 at 4 rows).
+bool packs_rows(int dtype, int M, int K) {
+  return gemm_uses_mfma(dtype, M, K, true) || (dtype == DFLASH_BF16 && M > 16);
+}
+
 struct Plan {
   size_t x, h, qkv, q, po, pml, attn, act, y, amax, arr, part, sq, fwd_end;
   size_t u, ua, upart, proj_end;  // ua: tiled copy of the fused features (MFMA path)
@@ -182,13 +191,13 @@ Plan make_plan(const dflash_config& c, int batch, int cap, int max_tokens) {
   off = 0;
   p.u = take((size_t)max_tokens * d * 4);
   const int fk = c.n_target_feats * c.target_hidden;
-  p.ua = gemm_uses_mfma(dt, max_tokens, fk, true) ? take(tiled_bytes(dt, max_tokens, fk)) : 0;
+  p.ua = packs_rows(dt, max_tokens, fk) ? take(tiled_bytes(dt, max_tokens, fk)) : 0;
   p.upart_elems = splitk_elems_upto(dt, max_tokens, (int)d, fk);
   p.upart = take((size_t)p.upart_elems * 4);
   p.proj_end = off;
   off = 0;
   p.kv = take((size_t)max_tokens * c.n_layers * 2 * Hkv * hd * 4);
-  p.ca = gemm_uses_mfma(dt, max_tokens, (int)d, true) ? take(tiled_bytes(dt, max_tokens, (int)d)) : 0;
+  p.ca = packs_rows(dt, max_tokens, (int)d) ? take(tiled_bytes(dt, max_tokens, (int)d)) : 0;
   p.kvpart_elems = splitk_elems_upto(dt, max_tokens, (int)(c.n_layers * 2 * Hkv * hd), (int)d);
   p.kvpart = take((size_t)p.kvpart_elems * 4);
   p.app_end = off;
@@ -436,8 +445,8 @@ int32_t dflash_ctx_project(const dflash_handle* h, const void* const* feats,
   const char* pk = (const char*)h->w.packed;
   const int K = c.n_target_feats * c.target_hidden;
   GemmArgs g;
-  if (gemm_uses_mfma(c.dtype, n_tok, K, true)) {
-    // Enough rows for the MFMA-bound kernel: tile the features first.
+  if (packs_rows(c.dtype, n_tok, K)) {
+    // Tile the features first (MFMA kernel, or several row tiles).
     PackSrc src{};
     for (int f = 0; f < c.n_target_feats; ++f) src.seg[f] = feats[f];
     src.nseg = c.n_target_feats;
@@ -490,7 +499,7 @@ static int32_t append_rows(const dflash_handle* h, const dflash_kv_cache* cache,
     const int N = L * 2 * Hkv * hd;
     const char* wkv = (const char*)h->w.packed + h->pl.kv;
     GemmArgs g;
-    if (gemm_uses_mfma(c.dtype, n_tok, c.hidden, true)) {
+    if (packs_rows(c.dtype, n_tok, c.hidden)) {
       void* at = (char*)ws + P.ca;
       prof_begin(DFLASH_K_SMALL, 0, 0, st);
       const hipError_t pe = launch_pack_tiled(c.dtype, pack_src(ctx, c.hidden), n_tok, c.hidden, at, st);
