@@ -137,7 +137,7 @@ int attn_wg_per_head(int hkv) { return std::max(1, kAttnSlots / std::max(1, hkv)
 
 // Floats of split-K partials a tiled-A projection needs on the MFMA path (0 if none).
 int64_t splitk_elems(int dtype, int epi, int M, int N, int K) {
-  if (!gemm_uses_mfma(dtype, M, K, true)) return 0;
+  if (!gemm_uses_mfma(dtype, M, K, true, epi)) return 0;
   const int ks = mfma_gemm_ksplit(epi, M, N, K);
   return ks > 1 ? (int64_t)ks * M * N : 0;
 }

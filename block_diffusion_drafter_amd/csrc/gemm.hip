@@ -439,13 +439,13 @@ GemmPlan plan_gemm(int dtype, int epi, int M, int N, int K, int a_seg_k) {
 }
 
 int gemm_amax_cols(int dtype, int M, int N, int K) {
-  if (gemm_uses_mfma(dtype, M, K, true)) return mfma_gemm_colblocks(EPI_ARGMAX, M, N, K);
+  if (gemm_uses_mfma(dtype, M, K, true, EPI_ARGMAX)) return mfma_gemm_colblocks(EPI_ARGMAX, M, N, K);
   return plan_gemm(dtype, EPI_ARGMAX, M, N, K, 0).grid_x;
 }
 
 hipError_t launch_gemm(int dtype, int epi, const GemmArgs& a0, hipStream_t st) {
   if (a0.M <= 0 || a0.N <= 0 || a0.K <= 0) return hipSuccess;
-  if (gemm_uses_mfma(dtype, a0.M, a0.K, a0.a_tiled != 0)) return launch_gemm_mfma(epi, a0, st);
+  if (gemm_uses_mfma(dtype, a0.M, a0.K, a0.a_tiled != 0, epi)) return launch_gemm_mfma(epi, a0, st);
   // Row-major activations only come from callers, as inputs of fp32-output projections.
   if (!a0.a_tiled && epi != EPI_STORE_F32) return hipErrorInvalidValue;
   const bool multi = !a0.a_tiled && a0.a_nseg > 1;

@@ -763,7 +763,7 @@ static int usable_ksplit(int epi, const GemmArgs& a) {
 }
 
 bool gemm_fuses_norm(int dtype, const GemmArgs& a) {
-  return gemm_uses_mfma(dtype, a.M, a.K, a.a_tiled != 0) && usable_ksplit(EPI_RESID, a) > 1 &&
+  return gemm_uses_mfma(dtype, a.M, a.K, a.a_tiled != 0, EPI_RESID) && usable_ksplit(EPI_RESID, a) > 1 &&
          a.N <= 8192;
 }
 
