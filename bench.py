@@ -283,6 +283,29 @@ def main() -> int:
     torch.cuda.synchronize()
     copy_gbs = 3 * 2 * (1 << 30) / (c0.elapsed_time(c1) / 1e3) / 1e9
     del scratch, dst
+
+    # KV append alone (the round's new rows: the stacked context K/V projection
+    # of every layer, then norm/RoPE and the scatter into the cache); ctx_len
+    # is put back after each call, so the same positions are rewritten.
+    saved_len = cache.ctx_len.clone()
+    n_app = 10
+    app_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(n_app)]
+    for s0, s1 in app_ev:
+        s0.record()
+        model.ctx_kv_append(cache, ctx_new, cu_new, ws, status)
+        s1.record()
+        cache.ctx_len.copy_(saved_len)
+    torch.cuda.synchronize()
+    app_ms = float(np.median([s0.elapsed_time(s1) for s0, s1 in app_ev]))
+    kvw = L * 2 * Hkv * hd
+    app_bytes = (kvw * d * es              # K/V projection weights of every layer
+                 + n_tok * d * es           # the new context rows
+                 + 2 * n_tok * kvw * 4      # fp32 projections written, then read
+                 + n_tok * kvw * es)        # K/V rows scattered into the cache
+    kv_append = {"ms": round(app_ms, 5), "rows": n_tok, "algorithmic_bytes": int(app_bytes),
+                 "GBps": round(app_bytes / (app_ms / 1e3) / 1e9, 1),
+                 "frac_of_hbm_peak": round(app_bytes / (app_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}
     ctx_end = cache.ctx_len.cpu().numpy().astype(np.int64)
     assert status.item() == 0, f"device status {status.item()}"
 
@@ -342,6 +365,7 @@ def main() -> int:
                                   "note": "1 GiB read-modify-write before each step, outside "
                                           "its events"},
         "measured_hbm_copy_GBps": round(copy_gbs, 1),
+        "kv_append": kv_append,
     }
 
     if a.graph:
