@@ -7,7 +7,8 @@ only module both consume is ``synth`` (seeded random draws, no arithmetic of
 the method).
 
 Plain NumPy in float64: every input (fp32 values, or bf16 bit patterns widened
-exactly) is upcast to fp64 and no intermediate is rounded. Each function states
+exactly) is upcast to fp64 and no intermediate is rounded (compute_dtype() can
+switch the same steps to float32 for the CPU throughput baseline only). Each function states
 the passage it follows. Pages cited, by title:
 
   [W] "DFlash: Block Diffusion for Flash Speculative Decoding" -- wikillm.com
@@ -45,16 +46,33 @@ example on the pages, so beyond those pins the whole pass is "parity unpinned".
 """
 from __future__ import annotations
 
+import contextlib
 from dataclasses import dataclass
 from typing import Dict, List, Optional, Sequence
 
 import numpy as np
 
 F64 = np.float64
+# The type every step computes in: float64 for parity. compute_dtype() lets
+# the CPU throughput baseline time the same steps in float32; no parity
+# result is ever taken in that mode.
+_COMPUTE = [F64]
+
+
+@contextlib.contextmanager
+def compute_dtype(dtype):
+    """Run the oracle's arithmetic in dtype inside the block (timing only)."""
+    prev = _COMPUTE[0]
+    _COMPUTE[0] = np.dtype(dtype).type
+    try:
+        yield
+    finally:
+        _COMPUTE[0] = prev
 
 
 def _f64(a) -> np.ndarray:
-    return np.asarray(a, dtype=F64)
+    """a in the compute type (float64 unless compute_dtype says otherwise)."""
+    return np.asarray(a, dtype=_COMPUTE[0])
 
 
 # ---------------------------------------------------------------------------
@@ -66,7 +84,8 @@ def select_target_layers(n_target_layers: int, n_feats: int = 5) -> List[int]:
     [W "Paper vs code"]: layers spaced evenly from index 1 to index L-3; the
     code adds one when indexing a hidden-state list whose entry 0 is the
     embedding output. Reading: the evenly spaced points are rounded to the
-    nearest integer. Returned values are hidden-state-list indices (+1 offset).
+    nearest integer, halves up (7.5 -> 8; the pages do not say). Returned
+    values are hidden-state-list indices (+1 offset).
     """
     lo, hi = 1, n_target_layers - 3
     pts = np.linspace(lo, hi, n_feats)
@@ -216,7 +235,7 @@ def kv_injected_attention(q, k_blk, v_blk, k_ctx, v_ctx, group: int,
     qpos = np.arange(c, c + B)[:, None]
     kpos = np.arange(c + B)[None, :]
     visible = np.ones((B, c + B), dtype=bool) if window is None else (qpos - kpos < window)
-    out = np.empty((B, hq, hd), dtype=F64)
+    out = np.empty((B, hq, hd), dtype=_COMPUTE[0])
     for j in range(hq):
         g = j // group
         keys = np.concatenate([_f64(k_ctx[g]), _f64(k_blk[:, g, :])], axis=0)
@@ -304,7 +323,7 @@ def draft_forward(cfg, weights: Dict[str, np.ndarray], caches: Sequence[SeqCache
     B, d = cfg.block_size, cfg.hidden
     xs = np.stack([embed_block(int(anchors[s]), weights, cfg) if x0 is None else _f64(x0[s])
                    for s in range(b)])
-    hidden = np.empty((b, cfg.n_layers, B, d), dtype=F64)
+    hidden = np.empty((b, cfg.n_layers, B, d), dtype=_COMPUTE[0])
     for l in range(cfg.n_layers):
         lw = layer_weights(weights, l)
         for s in range(b):

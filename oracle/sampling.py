@@ -164,6 +164,8 @@ class Verified:
     u_margin: np.ndarray     # [batch, m] |u_i - alpha_i| at the scanned positions (inf after)
     g_margin: np.ndarray     # [batch] perturbed-score margin of the emitted draw
     alpha: np.ndarray        # [batch, m] acceptance probabilities min(1, p/q)
+    scores: np.ndarray       # [batch, V] perturbed scores of the emitted draw (its argmax
+                             # is out_token; -inf outside the residual's support)
 
 
 def verify(drafts: np.ndarray, draft_logits: np.ndarray, target_logits: np.ndarray,
@@ -201,4 +203,4 @@ def verify(drafts: np.ndarray, draft_logits: np.ndarray, target_logits: np.ndarr
     score = np.where(has_res[:, None],
                      np.where(d > 0, np.log(np.where(d > 0, d, 1.0)), -np.inf), lp_a)
     tok, margin = gumbel_argmax(score, g)
-    return Verified(a.astype(np.int64), tok, um, margin, alpha)
+    return Verified(a.astype(np.int64), tok, um, margin, alpha, score + g)

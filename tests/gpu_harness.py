@@ -7,10 +7,20 @@ Tolerances (written here once, used by every parity test):
   * bf16 drafter: normwise relative error max|gpu-ref| / max|ref| <= 3e-2 on
     the same tensors (the GPU rounds GEMM inputs, q/k/v, P and the cache to
     bf16; the oracle rounds nothing);
-  * draft token ids bit-exact wherever the oracle's top-1 minus top-2 logit
-    margin exceeds 0.05; accept lengths bit-exact wherever every position the
-    prefix test reads (i <= min(a, B-2)) has such a margin. Excluded positions
-    are counted and must stay a minority.
+    The bound holds over the whole tensor and, separately, over every group
+    along its leading axes (each sequence of a batch, each KV head of a cache
+    slice), so an error confined to one short sequence or one head cannot hide
+    under another's larger values;
+  * draft token ids: the GPU's token must be one of the oracle's near-top
+    tokens, i.e. its oracle logit lies within 0.05 of the oracle's top-1 logit.
+    Where the oracle's top-1/top-2 margin exceeds 0.05 that leaves only the
+    oracle's own argmax (bit-exact); at a near-tie any of the tied tokens is a
+    correct draft and the GPU's pick is checked to be one of them;
+  * accept lengths and bonus tokens: the GPU's equal the prefix rule applied
+    to its own drafts (every sequence), and equal the oracle's wherever the
+    GPU's drafts agree with the oracle's on every position the prefix test
+    reads (i <= min(a, B-2)); where they do not, the first differing position
+    is a validated near-tie.
 """
 from __future__ import annotations
 
@@ -48,13 +58,54 @@ def err_stats(got, ref):
     return abs_err, abs_err / max(scale, 1e-30)
 
 
-def assert_close(cfg, got, ref, what: str) -> None:
+def group_rel_errors(got, ref, group_axes: int) -> np.ndarray:
+    """Normwise error max|gpu-ref| / max|ref| of every group formed by the
+    first group_axes axes (e.g. 1: per sequence of [b, ...])."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    lead = got.shape[:group_axes]
+    g = got.reshape(int(np.prod(lead)), -1)
+    r = ref.reshape(int(np.prod(lead)), -1)
+    if g.shape[1] == 0:
+        return np.zeros(g.shape[0])
+    err = np.max(np.abs(g - r), axis=1)
+    scale = np.max(np.abs(r), axis=1)
+    return np.where(scale > 0, err / np.maximum(scale, 1e-30), np.where(err > 0, np.inf, 0.0))
+
+
+def _check_close(cfg, got, ref, what: str, group_axes: int):
     a, r = err_stats(got, ref)
+    worst = r
     if cfg.dtype == "fp32":
         assert a <= TOL_FP32_ABS, f"{what}: max-abs {a:.3e} > {TOL_FP32_ABS}"
     else:
         assert r <= TOL_BF16_REL, f"{what}: normwise rel {r:.3e} > {TOL_BF16_REL}"
-    log(f"  {what}: max-abs {a:.3e} rel {r:.3e}")
+        if group_axes > 0 and np.asarray(ref).size:
+            per = group_rel_errors(got, ref, group_axes)
+            worst = float(per.max())
+            bad = np.argwhere(per.reshape(np.asarray(ref).shape[:group_axes]) > TOL_BF16_REL)
+            assert not len(bad), (f"{what}: normwise rel {worst:.3e} > {TOL_BF16_REL} in group(s) "
+                                  f"{bad[:5].tolist()}")
+    return a, r, worst
+
+
+def assert_close(cfg, got, ref, what: str, group_axes: int = 0) -> None:
+    """fp32: max-abs bound. bf16: normwise bound over the tensor and over every
+    group along the first group_axes axes."""
+    a, r, worst = _check_close(cfg, got, ref, what, group_axes)
+    log(f"  {what}: max-abs {a:.3e} rel {r:.3e}" +
+        (f" (worst group {worst:.3e})" if group_axes > 0 and cfg.dtype != "fp32" else ""))
+
+
+def assert_close_each(cfg, items, what: str, group_axes: int = 0) -> None:
+    """assert_close on every (label, got, ref) of items (e.g. one per sequence,
+    grouped per KV head); one log line with the worst figures."""
+    wa = wr = ww = 0.0
+    for label, got, ref in items:
+        a, r, w = _check_close(cfg, got, ref, f"{what} {label}", group_axes)
+        wa, wr, ww = max(wa, a), max(wr, r), max(ww, w)
+    log(f"  {what}: {len(items)} parts, worst max-abs {wa:.3e} rel {wr:.3e}" +
+        (f" (worst group {ww:.3e})" if group_axes > 0 and cfg.dtype != "fp32" else ""))
 
 
 def to_np(t: torch.Tensor) -> np.ndarray:
@@ -107,29 +158,57 @@ def feats_to_device(feats: List[I.HostTensor]) -> List[torch.Tensor]:
 
 
 def check_drafts(res: O.ForwardResult, drafts_gpu: np.ndarray, what: str) -> int:
+    """Every slot: the GPU's token is a valid draft, i.e. its oracle logit is
+    within MARGIN of the oracle's top-1 logit. On confident slots (oracle
+    top-1/top-2 margin > MARGIN) only the oracle's argmax qualifies, so those
+    are bit-exact. Returns the number of near-tie slots."""
+    drafts_gpu = np.asarray(drafts_gpu, dtype=np.int64)
+    V = res.logits.shape[-1]
+    assert ((drafts_gpu >= 0) & (drafts_gpu < V)).all(), f"{what}: token ids out of range"
     ok = res.margins > MARGIN
     mism = (drafts_gpu != res.drafts) & ok
     assert not mism.any(), f"{what}: {int(mism.sum())} confident drafts differ at {np.argwhere(mism)[:5]}"
+    top1 = np.take_along_axis(res.logits, res.drafts[..., None], -1)[..., 0]
+    mine = np.take_along_axis(res.logits, drafts_gpu[..., None], -1)[..., 0]
+    gap = top1 - mine
+    invalid = gap > MARGIN
+    assert not invalid.any(), (f"{what}: {int(invalid.sum())} near-tie slots hold a token whose "
+                               f"oracle logit is more than {MARGIN} below the top-1: "
+                               f"{np.argwhere(invalid)[:5].tolist()}, gaps {gap[invalid][:5]}")
     excl = int((~ok).sum())
-    log(f"  {what}: drafts bit-exact on {int(ok.sum())}/{ok.size} confident slots "
-        f"({excl} excluded, margin <= {MARGIN})")
+    differ = int(((drafts_gpu != res.drafts) & ~ok).sum())
+    log(f"  {what}: drafts bit-exact on {int(ok.sum())}/{ok.size} confident slots; "
+        f"{excl} near-tie slots (margin <= {MARGIN}) all hold a near-top token "
+        f"({differ} differ from the oracle's argmax, 0 invalid)")
     return excl
 
 
 def check_accept(res: O.ForwardResult, targets: np.ndarray, acc_gpu: np.ndarray,
                  bonus_gpu: np.ndarray, drafts_gpu: np.ndarray, what: str) -> int:
+    """Accept lengths and bonus tokens: the prefix rule on the GPU's own drafts
+    for every sequence; equal to the oracle's wherever the GPU's drafts agree
+    with the oracle's on every position the prefix test reads. Where they do
+    not, the first differing read position must be a near-tie (check_drafts
+    has validated the GPU's token there). Returns the number of sequences
+    compared with the oracle."""
     acc_o, bonus_o = O.accept(res.drafts, targets)
-    m = res.drafts.shape[1]
-    checked = 0
-    for s in range(len(acc_o)):
+    b, m = res.drafts.shape
+    checked = explained = 0
+    for s in range(b):
         a = int(acc_o[s])
-        # Property at any margin: the GPU's accept length is the longest
-        # matching prefix of its own drafts against the targets.
         a_own, b_own = O.accept(drafts_gpu[s:s + 1], targets[s:s + 1])
         assert acc_gpu[s] == a_own[0] and bonus_gpu[s] == b_own[0], f"{what}: seq {s} prefix rule"
-        if (res.margins[s, :min(a, m - 1) + 1] > MARGIN).all() or m == 0:
+        read = min(a, m - 1) + 1 if m else 0
+        same = np.asarray(drafts_gpu[s, :read]) == res.drafts[s, :read]
+        if same.all():
             assert acc_gpu[s] == a and bonus_gpu[s] == bonus_o[s], (
-                f"{what}: seq {s} accept {acc_gpu[s]} vs oracle {a}")
+                f"{what}: seq {s} accept {acc_gpu[s]} bonus {bonus_gpu[s]} vs oracle {a} "
+                f"{bonus_o[s]}")
             checked += 1
-    log(f"  {what}: accept lengths bit-exact on {checked}/{len(acc_o)} confident sequences")
+        else:
+            i = int(np.argmin(same))
+            assert res.margins[s, i] <= MARGIN, f"{what}: seq {s} differs at confident slot {i}"
+            explained += 1
+    log(f"  {what}: accept lengths equal to the oracle's on {checked}/{b} sequences; "
+        f"{explained} differ through a near-tie draft read by the prefix test")
     return checked

@@ -409,10 +409,35 @@ def check_accept_bruteforce(O):
 
 
 def check_select_layers(O):
-    ids = O.select_target_layers(36, 5)
-    assert ids[0] == 2 and ids[-1] == 34, ids          # layers 1 and L-3, +1 offset
-    assert ids == [2, 10, 18, 26, 34], ids
-    assert O.select_target_layers(32, 5) == [2, 9, 16, 23, 30]
+    """Hand-worked cases (tests/golden/target_layer_selection.json), two with
+    fractional points (halves round up, reading D12), plus properties that
+    hold for any depth: first index 2 (layer 1, +1 offset), last L-2 (layer
+    L-3, +1), strictly increasing, neighbouring gaps differing by at most 1."""
+    with open(os.path.join(GOLDEN, "target_layer_selection.json")) as f:
+        g = json.load(f)
+    for e in g["cases"]:
+        got = O.select_target_layers(e["n_target_layers"], e["n_feats"])
+        assert got == e["ids"], (e, got)
+    for L in range(8, 81):
+        for n in (3, 5):
+            ids = O.select_target_layers(L, n)
+            gaps = np.diff(ids)
+            assert len(ids) == n and ids[0] == 2 and ids[-1] == L - 2, (L, n, ids)
+            assert (gaps > 0).all() and gaps.max() - gaps.min() <= 1, (L, n, ids)
+
+
+def check_kv_cache_bytes(O):
+    """[R sec. 5.3]'s cache-size formula against the bytes the library's cache
+    layout actually allocates (K rows and 32-position V blocks, meta tensors,
+    no memory touched) for the Qwen3-8B-shaped and tiny drafters."""
+    import torch
+    from block_diffusion_drafter_amd import binding as B
+    for L, b, hkv, cap, hd, dt, es in ((5, 1, 8, 2048, 128, torch.bfloat16, 2),
+                                       (5, 32, 8, 8192, 128, torch.bfloat16, 2),
+                                       (1, 3, 2, 64, 64, torch.float32, 4)):
+        c = B.KVCache(L, b, hkv, cap, hd, dt, device="meta")
+        held = c.k.numel() * c.k.element_size() + c.v.numel() * c.v.element_size()
+        assert O.kv_cache_bytes(b, L, cap, hkv * hd, es) == held, (L, b, cap, held)
 
 
 def check_accounting(O):
@@ -436,7 +461,6 @@ def check_accounting(O):
             assert abs(out / e["output_bytes_approx"] - 1) <= e["rel_tol"], out
         else:
             assert inp < e["input_bytes_below"], inp
-    assert O.kv_cache_bytes(1, 5, 2048, 1024, 2) == 2 * 5 * 2048 * 1024 * 2
 
 
 ALL_CHECKS = [v for k, v in sorted(globals().items()) if k.startswith("check_")]

@@ -9,8 +9,8 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_harness import (MARGIN, assert_close, build_model, capacity_for, check_accept,
-                         check_drafts, feats_to_device, log, prefix_offsets, to_np)
+from gpu_harness import (assert_close, assert_close_each, build_model, capacity_for,
+                         check_accept, check_drafts, feats_to_device, log, prefix_offsets, to_np)
 from block_diffusion_drafter_amd import binding as B
 from oracle import dflash_oracle as O
 from synth import QWEN3_8B_SHAPED, SMALL_BF16, TINY_FP32
@@ -80,18 +80,21 @@ def run_flow(cfg, ctx_lens, tag, seed=0, cap_extra=0, split_append=1, degenerate
     ctx_o = O.ctx_project([f.f32() for f in feats], ow["fc"], ow["fc_norm"], cfg.rms_eps) \
         if n_tot else np.zeros((0, d))
     if n_tot:
-        assert_close(cfg, to_np(ctx_gpu[:n_tot]), ctx_o, "ctx_project")
+        # per row: every context row is checked on its own
+        assert_close(cfg, to_np(ctx_gpu[:n_tot]), ctx_o, "ctx_project", group_axes=1)
     caches = [O.prefill_cache(ctx_o[cu_all[s]:cu_all[s + 1]], 0, ow, cfg) for s in range(b)]
     for l in range(cfg.n_layers):
-        kg = np.concatenate([to_np(cache.read_positions(l, s, 0, ctx_lens[s])[0]).reshape(-1)
-                             for s in range(b)])
-        vg = np.concatenate([to_np(cache.read_positions(l, s, 0, ctx_lens[s])[1]).reshape(-1)
-                             for s in range(b)])
-        ko = np.concatenate([caches[s].k[l].reshape(-1) for s in range(b)])
-        vo = np.concatenate([caches[s].v[l].reshape(-1) for s in range(b)])
-        if ko.size:
-            assert_close(cfg, kg, ko, f"cache K layer {l}")
-            assert_close(cfg, vg, vo, f"cache V layer {l}")
+        # per sequence, grouped per KV head ([Hkv, n, hd])
+        ks, vs = [], []
+        for s in range(b):
+            if not ctx_lens[s]:
+                continue
+            kg, vg = cache.read_positions(l, s, 0, ctx_lens[s])
+            ks.append((f"seq {s}", to_np(kg), caches[s].k[l]))
+            vs.append((f"seq {s}", to_np(vg), caches[s].v[l]))
+        if ks:
+            assert_close_each(cfg, ks, f"cache K layer {l}", group_axes=1)
+            assert_close_each(cfg, vs, f"cache V layer {l}", group_axes=1)
 
     anchors = I.anchors(cfg, b, seed=3, tag=tag)
     res = O.draft_forward(cfg, ow, caches, anchors)
@@ -112,10 +115,11 @@ def run_flow(cfg, ctx_lens, tag, seed=0, cap_extra=0, split_append=1, degenerate
     assert status.item() == 0, f"device status {status.item()}"
     assert cache.ctx_len.cpu().tolist() == ctx_lens, "forward must not move ctx_len"
     for l in range(cfg.n_layers):
-        assert_close(cfg, to_np(hidden_g[:, l]), res.hidden[:, l], f"hidden after layer {l}")
+        assert_close(cfg, to_np(hidden_g[:, l]), res.hidden[:, l], f"hidden after layer {l}",
+                     group_axes=1)
     drafts = drafts_g.cpu().numpy()[:, :m].astype(np.int64)
     if m:
-        assert_close(cfg, to_np(logits_g), res.logits, "logits")
+        assert_close(cfg, to_np(logits_g), res.logits, "logits", group_axes=1)
         excl = check_drafts(res, drafts, "drafts")
         if not degenerate:
             assert excl <= max(2, 0.5 * res.drafts.size), "too many low-margin slots to be a test"

@@ -17,7 +17,8 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_harness import (MARGIN, assert_close, build_model, capacity_for, feats_to_device, log,
+from gpu_harness import (assert_close, assert_close_each, build_model, capacity_for,
+                         check_drafts, feats_to_device, log,
                          prefix_offsets, to_np)
 from block_diffusion_drafter_amd import binding as B
 from oracle import dflash_oracle as O
@@ -62,15 +63,17 @@ def oracle_append_accepted(M, cfg, caches, feats, acc):
 
 
 def compare_caches(cfg, cache, caches, what):
+    """Every sequence's cached K and V of every layer, grouped per KV head."""
     for l in range(cfg.n_layers):
-        kg = np.concatenate([to_np(cache.read_positions(l, s, 0, c.ctx_len)[0]).reshape(-1)
-                             for s, c in enumerate(caches)])
-        vg = np.concatenate([to_np(cache.read_positions(l, s, 0, c.ctx_len)[1]).reshape(-1)
-                             for s, c in enumerate(caches)])
-        assert_close(cfg, kg, np.concatenate([c.k[l].reshape(-1) for c in caches]),
-                     f"{what}: K layer {l}")
-        assert_close(cfg, vg, np.concatenate([c.v[l].reshape(-1) for c in caches]),
-                     f"{what}: V layer {l}")
+        ks, vs = [], []
+        for s, c in enumerate(caches):
+            if not c.ctx_len:
+                continue
+            kg, vg = cache.read_positions(l, s, 0, c.ctx_len)
+            ks.append((f"seq {s}", to_np(kg), c.k[l]))
+            vs.append((f"seq {s}", to_np(vg), c.v[l]))
+        assert_close_each(cfg, ks, f"{what}: K layer {l}", group_axes=1)
+        assert_close_each(cfg, vs, f"{what}: V layer {l}", group_axes=1)
 
 
 @pytest.mark.parametrize("cfg", [TINY_FP32, SMALL_BF16], ids=lambda c: c.name)
@@ -184,9 +187,8 @@ def test_gpu_round_graph_follows_the_oracle_trajectory():
     torch.cuda.synchronize()
     for r in range(rounds):
         drafts = buf.drafts.cpu().numpy().astype(np.int64)
-        ok = res.margins > MARGIN
-        assert (drafts[ok] == res.drafts[ok]).all(), f"round {r}: confident drafts differ"
-        assert_close(cfg, to_np(buf.logits), res.logits, f"round {r}: logits")
+        check_drafts(res, drafts, f"round {r}: drafts")
+        assert_close(cfg, to_np(buf.logits), res.logits, f"round {r}: logits", group_axes=1)
         # the target pass of this block: planted accept lengths against the
         # oracle's drafts, fresh features at every block position
         a_star = I.planted_accept_lengths(b, m, seed=100 + r, tag="graph")
@@ -206,8 +208,7 @@ def test_gpu_round_graph_follows_the_oracle_trajectory():
         assert cache.ctx_len.cpu().tolist() == [c.ctx_len for c in caches], f"round {r}: ctx_len"
         log(f"  round {r}: accept {a_o.tolist()}, ctx {[c.ctx_len for c in caches]}")
     drafts = buf.drafts.cpu().numpy().astype(np.int64)
-    ok = res.margins > MARGIN
-    assert (drafts[ok] == res.drafts[ok]).all()
+    check_drafts(res, drafts, f"after {rounds} rounds: drafts")
     compare_caches(cfg, cache, caches, f"after {rounds} rounds")
     g.close()
 

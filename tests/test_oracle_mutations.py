@@ -151,6 +151,15 @@ def _select_no_offset(n, k=5):
     return [i - 1 for i in _orig["select_target_layers"](n, k)]
 
 
+def _select_half_even(n, k=5):
+    # numpy's round-half-to-even instead of the half-up reading
+    return [int(v) + 1 for v in np.round(np.linspace(1, n - 3, k))]
+
+
+def _select_truncate(n, k=5):
+    return [int(v) + 1 for v in np.linspace(1, n - 3, k)]
+
+
 def _tau_missing_one(a, m):
     return _orig["tau_geometric"](a, m) - 1.0
 
@@ -213,6 +222,8 @@ MUTATIONS = {
     "accept_counts_all": ("accept", _accept_counts_all_matches),
     "accept_bonus_shifted": ("accept", _accept_bonus_shifted),
     "select_no_offset": ("select_target_layers", _select_no_offset),
+    "select_half_even": ("select_target_layers", _select_half_even),
+    "select_truncate": ("select_target_layers", _select_truncate),
     "tau_missing_one": ("tau_geometric", _tau_missing_one),
 }
 
