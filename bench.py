@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of one DFlash drafting round on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload q1] [--temperature T]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload q32] [--temperature T]
 
 A step is one pass of the whole hot path over one batch: fuse the target
 features of the rows accepted last round (1-16 rows per sequence, a seeded
@@ -16,10 +16,18 @@ Inputs are resident in HBM before the timed region. The context grows by the
 appended rows every step, as in decoding; the reported context range covers
 the whole run.
 
+The default workload is the Qwen3-8B-shaped drafter at batch 32 with ragged
+contexts of 512-8192 positions (the largest single-GPU configuration, where the
+projections are matrix-core bound); a shorter batch-1 leg (context 2048, the
+same drafter) follows it in the same process and is reported under "batch1".
+
 Prints one JSON line: throughput in drafted block-tokens/s (batch * 16 per
 step), the dominant kernel against its roofline (timed live with HIP events on
-the library's stream), the whole step against its roofline, and the CPU oracle
-timed on this host on a bounded sample of the same workload.
+the library's stream), the attention kernel's HBM rate and the projections'
+aggregate and per-class MFMA rates against the datasheet peaks and against
+peaks measured in the same process (a 1 GiB device copy; an MFMA loop), the
+whole step against its roofline, and the CPU oracle timed on this host on a
+bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -68,7 +76,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="q1", choices=["q1", "q32", "q4l", "l16", "train"],
+    ap.add_argument("--workload", default="q32", choices=["q1", "q32", "q4l", "l16", "train"],
                     help="train: the training-pattern attention of packed blocks alone "
                          "(its own metric; the drafting workloads time whole rounds)")
     ap.add_argument("--temperature", type=float, default=0.0,
@@ -88,6 +96,9 @@ def parse():
                     help="approximate CPU time budget of the oracle sample")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run one 1 GiB device copy before timing (HBM counter calibration)")
+    ap.add_argument("--no-batch1", action="store_true",
+                    help="skip the batch-1 leg that follows the default batch-32 workload")
+    ap.add_argument("--batch1-steps", type=int, default=30)
     return ap.parse_args()
 
 
@@ -118,32 +129,128 @@ def main() -> int:
     if a.window:
         variant["sliding_window"] = a.window
         variant["sliding_layers"] = tuple(range(a.layers or W.model.n_layers))
-    if variant:
+
+    def with_variant(w):
+        if not variant:
+            return w
         import dataclasses
-        W = dataclasses.replace(W, model=W.model.with_(**variant))
+        return dataclasses.replace(w, model=w.model.with_(**variant))
+
+    W = with_variant(W)
+    cfg = W.model
+    host = I.Weights(cfg, W.seeds["weights"])
+    model = B.DraftModel(cfg, torch_io.weights_to_device(host))
+
+    if a.copy_probe:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    out, leg = run_rounds(a, W, model, a.steps, a.warmup, headline=True)
+    peaks = measured_peaks(B)
+    attach_measured_peaks(out, peaks)
+
+    # the batch-1 leg: same drafter, context 2048, after the headline
+    if a.workload == "q32" and not a.no_batch1 and a.temperature == 0:
+        W1 = with_variant(WORKLOADS["q1"])
+        b1, _ = run_rounds(a, W1, model, a.batch1_steps, a.warmup, headline=False)
+        attach_measured_peaks(b1, peaks)
+        out["batch1"] = b1
+
+    if a.graph:
+        out["round_graph"] = time_round_graph(a, B, I, torch_io, W, model, leg["cache"], leg["ws"],
+                                              leg["anchor"], leg["drafts"], leg["acc"],
+                                              leg["status"])
+
+    if not a.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(W, host, leg["ctx_lens"], leg["n_new"], leg["feats"],
+                                           a.cpu_seconds)
+
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+GEMM_CLASSES = ("gemm_f32out", "gemm_resid", "gemm_swiglu", "lm_head")
+
+
+def measured_peaks(B) -> dict:
+    """Peaks measured in this process on this chip: a 1 GiB device-to-device
+    copy (read + write bytes per second) and the library's MFMA calibration
+    loop (every matrix core busy with bf16 16x16x32 MFMAs and nothing else)."""
+    import torch
+    src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record()
+    for _ in range(3):
+        dst.copy_(src)
+    c1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 3 * 2 * (1 << 30) / (c0.elapsed_time(c1) / 1e3) / 1e9
+    del src, dst
+    n_wg, iters = 1024, 8000
+    sink = torch.empty(n_wg * 8, dtype=torch.float32, device="cuda")
+    B.probe_mfma_bf16(n_wg, iters // 4, sink)  # warm-up
+    m0, m1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    m0.record()
+    fl = sum(B.probe_mfma_bf16(n_wg, iters, sink) for _ in range(3))
+    m1.record()
+    torch.cuda.synchronize()
+    mfma_tfl = fl / (m0.elapsed_time(m1) / 1e3) / 1e12
+    return {"hbm_copy_GBps": round(copy_gbs, 1), "mfma_bf16_loop_TFLOPs": round(mfma_tfl, 1),
+            "mfma_loop": f"{n_wg} workgroups x 8 waves x {iters} iterations x 8 MFMAs, 3 launches"}
+
+
+def attach_measured_peaks(out: dict, peaks: dict) -> None:
+    """Fractions of the measured peaks beside the datasheet ones."""
+    out["measured_peaks"] = peaks
+    roof = out["roofline"]
+    if roof["bound"] == "hbm":
+        roof["frac_of_measured_copy"] = round(roof["achieved"] / peaks["hbm_copy_GBps"], 4)
+    else:
+        roof["frac_of_measured_mfma_loop"] = round(roof["achieved"] /
+                                                   peaks["mfma_bf16_loop_TFLOPs"], 4)
+    for k in ("attention", "gemm"):
+        e = roof.get(k)
+        if not e:
+            continue
+        if e["unit"] == "GB/s":
+            e["frac_of_measured_copy"] = round(e["achieved"] / peaks["hbm_copy_GBps"], 4)
+        else:
+            e["frac_of_measured_mfma_loop"] = round(e["achieved"] / peaks["mfma_bf16_loop_TFLOPs"], 4)
+            for c in e.get("classes", {}).values():
+                c["frac_of_measured_mfma_loop"] = round(c["TFLOPs"] / peaks["mfma_bf16_loop_TFLOPs"], 4)
+
+
+def run_rounds(a, W, model, steps: int, warmup: int, headline: bool):
+    """Prefill W's contexts, then time `steps` drafting rounds (after `warmup`).
+    Returns the JSON record of the workload and the buffers the later legs use."""
+    import torch
+    from block_diffusion_drafter_amd import binding as B
+    from synth import inputs as I
+    from synth import torch_io
+
     cfg = W.model
     b, Bk, d = W.batch, cfg.block_size, cfg.hidden
     ctx_lens = I.ctx_lengths(W)
     max_new = cfg.block_size  # a round appends a + 1 <= B rows
-    n_prof = max(3, min(10, a.steps))
-    n_dist, n_cold = min(a.steps, 20), min(a.steps, 10)  # per-step spread; cold-MALL steps
-    total_steps = (a.warmup + n_prof + a.steps + n_dist + n_cold +
-                   (2 * (a.warmup + a.steps) if a.graph else 0))
+    n_prof = max(3, min(10, steps))
+    n_dist, n_cold = (min(steps, 20), min(steps, 10)) if headline else (0, 0)
+    total_steps = (warmup + n_prof + steps + n_dist + n_cold +
+                   (2 * (warmup + steps) if a.graph and headline else 0))
     cap = int(((int(ctx_lens.max()) + max_new * total_steps + Bk + 31) // 32) * 32)
     print(f"[bench] workload {W.name}: batch {b}, ctx {int(ctx_lens.min())}-{int(ctx_lens.max())}, "
           f"capacity {cap}", file=sys.stderr, flush=True)
-
-    host = I.Weights(cfg, W.seeds["weights"])
-    dev = torch_io.weights_to_device(host)
-    model = B.DraftModel(cfg, dev)
     dt = model.dtype
 
     # ---- prefill (untimed): the context the rounds draft against -------------
-    n_pre = int(ctx_lens.sum())
     chunk_rows = 8192
     ws = model.new_workspace(b, cap, max(chunk_rows, b * max_new))
     cache = model.new_cache(b, cap)
-    cu_all = np.concatenate([[0], np.cumsum(ctx_lens)]).astype(np.int64)
     for s in range(b):
         for lo in range(0, int(ctx_lens[s]), chunk_rows):
             n = min(chunk_rows, int(ctx_lens[s]) - lo)
@@ -199,14 +306,7 @@ def main() -> int:
         model.draft_forward(cache, anchor, drafts, ws, target_tokens=targets, accept_len=acc,
                             bonus=anchor, dev_status=status)
 
-    if a.copy_probe:
-        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
-
-    for _ in range(a.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
     assert status.item() == 0, f"device status {status.item()}"
@@ -244,20 +344,19 @@ def main() -> int:
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     e0.record()
-    for _ in range(a.steps):
+    for _ in range(steps):
         step()
     e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     B.profiler_stop()
-    ms_step = e0.elapsed_time(e1) / a.steps
-    dom = read_profile(a.steps, ctx1)[dom_name]
+    ms_step = e0.elapsed_time(e1) / steps
+    dom = read_profile(steps, ctx1)[dom_name]
     assert status.item() == 0, f"device status {status.item()}"
     value = b * Bk / (ms_step / 1e3)
 
     # ---- after the headline: per-step spread, then steps with the 256 MB MALL
-    # flushed by a 1 GiB read-modify-write before each; and a 1 GiB device copy
-    # as a measured HBM reference ---------------------------------------------
+    # flushed by a 1 GiB read-modify-write before each ----------------------------
     def timed_steps(n, before=None):
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(n)]
@@ -270,19 +369,11 @@ def main() -> int:
         torch.cuda.synchronize()
         return sorted(s0.elapsed_time(s1) for s0, s1 in ev)
 
-    spread = timed_steps(n_dist)
-    scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
-    cold = timed_steps(n_cold, before=lambda: scratch.add_(1))
-    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    dst = torch.empty_like(scratch)
-    dst.copy_(scratch)
-    c0.record()
-    for _ in range(3):
-        dst.copy_(scratch)
-    c1.record()
-    torch.cuda.synchronize()
-    copy_gbs = 3 * 2 * (1 << 30) / (c0.elapsed_time(c1) / 1e3) / 1e9
-    del scratch, dst
+    if headline:
+        spread = timed_steps(n_dist)
+        scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        cold = timed_steps(n_cold, before=lambda: scratch.add_(1))
+        del scratch
 
     # KV append alone (the round's new rows: the stacked context K/V projection
     # of every layer, then norm/RoPE and the scatter into the cache); ctx_len
@@ -301,11 +392,11 @@ def main() -> int:
     kvw = L * 2 * Hkv * hd
     app_bytes = (kvw * d * es              # K/V projection weights of every layer
                  + n_tok * d * es           # the new context rows
-                 + 2 * n_tok * kvw * 4      # fp32 projections written, then read
                  + n_tok * kvw * es)        # K/V rows scattered into the cache
     kv_append = {"ms": round(app_ms, 5), "rows": n_tok, "algorithmic_bytes": int(app_bytes),
                  "GBps": round(app_bytes / (app_ms / 1e3) / 1e9, 1),
-                 "frac_of_hbm_peak": round(app_bytes / (app_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}
+                 "frac_of_hbm_peak": round(app_bytes / (app_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                 "traffic": measured_traffic(W.name, "kv_append")}
     ctx_end = cache.ctx_len.cpu().numpy().astype(np.int64)
     assert status.item() == 0, f"device status {status.item()}"
 
@@ -318,16 +409,42 @@ def main() -> int:
     tfl = dom["flops"] / t_dom / 1e12
     if dom["flops"] / max(dom["bytes"], 1.0) <= ridge:
         roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(gbs / HBM_PEAK_GBS, 4),
-                "frac_of_measured_copy": round(gbs / copy_gbs, 4)}
+                "frac": round(gbs / HBM_PEAK_GBS, 4)}
     else:
         roof = {"bound": "mfma", "achieved": round(tfl, 1), "peak": BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(tfl / BF16_PEAK_TFLOPS, 4)}
     roof.update({"traffic": measured_traffic(W.name, dom_name), "kernel_class": dom_name,
-                 "launches_per_step": dom["launches"] // a.steps,
+                 "launches_per_step": dom["launches"] // steps,
                  "ms_per_launch": round(dom["ms"] / dom["launches"], 5),
                  "algorithmic_bytes_per_launch": dom["bytes"] / dom["launches"],
-                 "algorithmic_flops_per_launch": dom["flops"] / dom["launches"]})
+                 "algorithmic_flops_per_launch": dom["flops"] / dom["launches"],
+                 "timing": f"HIP events around every launch of the class in the timed region "
+                           f"({steps} steps)"})
+    # The attention kernel against HBM, and the projections against the MFMA
+    # peak (aggregate and per class), from the breakdown pass.
+    att = prof_all["attention"]
+    if att["launches"]:
+        ag = att["bytes"] / (att["ms"] / 1e3) / 1e9
+        roof["attention"] = {"achieved": round(ag, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                             "frac": round(ag / HBM_PEAK_GBS, 4),
+                             "traffic": measured_traffic(W.name, "attention"),
+                             "ms_per_launch": round(att["ms"] / att["launches"], 5),
+                             "timing": f"breakdown pass, every launch event-bracketed "
+                                       f"({n_prof} steps)"}
+    g_fl = sum(prof_all[c]["flops"] for c in GEMM_CLASSES)
+    g_ms = sum(prof_all[c]["ms"] for c in GEMM_CLASSES)
+    if g_ms > 0:
+        gt = g_fl / (g_ms / 1e3) / 1e12
+        classes = {c: {"TFLOPs": round(prof_all[c]["flops"] / (prof_all[c]["ms"] / 1e3) / 1e12, 1),
+                       "frac": round(prof_all[c]["flops"] / (prof_all[c]["ms"] / 1e3) / 1e12 /
+                                     BF16_PEAK_TFLOPS, 4),
+                       "ms_per_step": round(prof_all[c]["ms"] / n_prof, 5),
+                       "gflop_per_step": round(prof_all[c]["flops"] / n_prof / 1e9, 2)}
+                   for c in GEMM_CLASSES if prof_all[c]["ms"] > 0}
+        roof["gemm"] = {"achieved": round(gt, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                        "frac": round(gt / BF16_PEAK_TFLOPS, 4), "classes": classes,
+                        "timing": f"breakdown pass, every launch event-bracketed ({n_prof} steps); "
+                                  "flops 2*M*N*K of the rows actually drafted (no padding)"}
 
     # whole step against its roofline: sum over kernels of max(bytes/BW, flops/peak)
     t_roof = sum(max(e["bytes"] / (HBM_PEAK_GBS * 1e9), e["flops"] / (BF16_PEAK_TFLOPS * 1e12))
@@ -341,7 +458,7 @@ def main() -> int:
         "metric": METRIC if (L, Bk) == (5, 16) else
         f"drafted block-tokens/sec ({L}-layer, block {Bk}) + % HBM/MFMA roofline",
         "value": round(value, 1), "unit": "block-tokens/s",
-        "n_gpus": 1, "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms_step, 5),
+        "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": round(ms_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": cfg.dtype,
         "data": "synthetic: seeded random-init drafter N(0,0.02^2), N(0,1) target hidden states",
@@ -359,24 +476,17 @@ def main() -> int:
         "kernels_event_bracketed": kernels,
         "wall_s_timed": round(wall, 4),
         "drafted_tokens_per_s": round(b * (Bk - 1) / (ms_step / 1e3), 1),
-        "ms_per_step_spread": {"steps": n_dist, "p10": pct(spread, 10), "p50": pct(spread, 50),
-                               "p90": pct(spread, 90)},
-        "ms_per_step_cold_mall": {"steps": n_cold, "p50": pct(cold, 50),
-                                  "note": "1 GiB read-modify-write before each step, outside "
-                                          "its events"},
-        "measured_hbm_copy_GBps": round(copy_gbs, 1),
         "kv_append": kv_append,
     }
-
-    if a.graph:
-        out["round_graph"] = time_round_graph(a, B, I, torch_io, W, model, cache, ws, anchor,
-                                              drafts, acc, status)
-
-    if not a.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(W, host, ctx_lens, n_new, feats, a.cpu_seconds)
-
-    print(json.dumps(out), flush=True)
-    return 0
+    if headline:
+        out["ms_per_step_spread"] = {"steps": n_dist, "p10": pct(spread, 10),
+                                     "p50": pct(spread, 50), "p90": pct(spread, 90)}
+        out["ms_per_step_cold_mall"] = {"steps": n_cold, "p50": pct(cold, 50),
+                                        "note": "1 GiB read-modify-write before each step, "
+                                                "outside its events"}
+    leg = dict(cache=cache, ws=ws, anchor=anchor, drafts=drafts, acc=acc, status=status,
+               ctx_lens=ctx_lens, n_new=n_new, feats=feats)
+    return out, leg
 
 
 def time_round_graph(a, B, I, torch_io, W, model, cache, ws, anchor, drafts, acc, status):
@@ -420,11 +530,34 @@ def time_round_graph(a, B, I, torch_io, W, model, cache, ws, anchor, drafts, acc
     return res
 
 
+def blas_facts() -> dict:
+    """The BLAS NumPy runs on: vendor (from NumPy's build configuration) and the
+    threads it uses (threadpoolctl)."""
+    facts = {}
+    try:
+        cfg = np.show_config(mode="dicts")
+        facts["vendor"] = cfg["Build Dependencies"]["blas"].get("name")
+        facts["version"] = cfg["Build Dependencies"]["blas"].get("version")
+    except Exception as e:  # numpy without the dict mode
+        facts["vendor"] = f"unknown ({type(e).__name__})"
+    try:
+        import threadpoolctl
+        pools = [p for p in threadpoolctl.threadpool_info() if p.get("user_api") == "blas"]
+        if pools:
+            facts["threads"] = pools[0].get("num_threads")
+            facts["internal_api"] = pools[0].get("internal_api")
+    except Exception as e:
+        facts["threads"] = f"unknown ({type(e).__name__})"
+    return facts
+
+
 def cpu_baseline(W, host, ctx_lens, n_new, feats, budget_s):
-    """The CPU oracle (fp64 NumPy, as it stands) on one sequence of the same
-    round: fuse + inject its new rows, run the drafter forward and accept.
-    The sequence's existing context K/V is a seeded synthetic cache state
-    (setup, untimed). Reported in block-tokens/s."""
+    """The CPU oracle as it stands on one sequence of the same round: fuse +
+    inject its new rows, run the drafter forward and accept. Timed twice: with
+    the oracle's arithmetic in float32 (the reported value) and in float64
+    (its parity precision), each on about half of budget_s. The sequence's
+    existing context K/V is a seeded synthetic cache state (setup, untimed).
+    Reported in block-tokens/s."""
     from oracle import dflash_oracle as O
     from synth import inputs as I
     try:
@@ -432,30 +565,41 @@ def cpu_baseline(W, host, ctx_lens, n_new, feats, budget_s):
     except AttributeError:
         cores = os.cpu_count() or 1
     cfg = W.model
-    ow = {n: host.get(n).f32() for n in host.names()}
-    if cfg.tied_embeddings:
-        ow["lm_head"] = ow["embed"]
     c0 = int(ctx_lens[0])
-    st = I.cache_state(cfg, [c0], seed=W.seeds["hiddens"] + 100)
-    cache = O.SeqCache([st[l][0][0].f64() for l in range(cfg.n_layers)],
-                       [st[l][0][1].f64() for l in range(cfg.n_layers)])
     n0 = int(n_new[0])
-    f0 = [f.f32()[:n0] for f in feats]
     anchor = I.anchors(cfg, 1, seed=W.seeds["targets"])
     targets = I.uniform_tokens(cfg, (1, cfg.block_size), W.seeds["targets"], "bench")
-    rounds, t_used = 0, 0.0
-    while rounds < 1 or (t_used < budget_s and rounds < 20):
-        t0 = time.perf_counter()
-        ctx = O.ctx_project(f0, ow["fc"], ow["fc_norm"], cfg.rms_eps)
-        new = O.prefill_cache(ctx, c0, ow, cfg)
-        res = O.draft_forward(cfg, ow, [cache.append(new)], anchor)
-        O.accept(res.drafts, targets)
-        t_used += time.perf_counter() - t0
-        rounds += 1
-    return {"value": round(cfg.block_size * rounds / t_used, 3), "unit": "block-tokens/s",
-            "cores": cores, "kind": "oracle",
-            "sample": f"{rounds} round(s) of 1 sequence of {W.name} (ctx {c0}, {n0} new rows), "
-                      f"fp64 NumPy, {t_used:.1f} s"}
+    st = I.cache_state(cfg, [c0], seed=W.seeds["hiddens"] + 100)
+    res = {}
+    for dt, name in ((np.float32, "fp32"), (np.float64, "fp64")):
+        # weights and cache in the compute type up front (setup, untimed)
+        ow = {n: host.get(n).f32().astype(dt) for n in host.names()}
+        if cfg.tied_embeddings:
+            ow["lm_head"] = ow["embed"]
+        cache = O.SeqCache([st[l][0][0].f32().astype(dt) for l in range(cfg.n_layers)],
+                           [st[l][0][1].f32().astype(dt) for l in range(cfg.n_layers)])
+        f0 = [f.f32()[:n0].astype(dt) for f in feats]
+        rounds, t_used = 0, 0.0
+        with O.compute_dtype(dt):
+            while rounds < 1 or (t_used < budget_s / 2 and rounds < 20):
+                t0 = time.perf_counter()
+                ctx = O.ctx_project(f0, ow["fc"], ow["fc_norm"], cfg.rms_eps)
+                new = O.prefill_cache(ctx, c0, ow, cfg)
+                r = O.draft_forward(cfg, ow, [cache.append(new)], anchor)
+                O.accept(r.drafts, targets)
+                t_used += time.perf_counter() - t0
+                rounds += 1
+        res[name] = (rounds, t_used)
+        del ow, cache
+    r32, t32 = res["fp32"]
+    r64, t64 = res["fp64"]
+    return {"value": round(cfg.block_size * r32 / t32, 3), "unit": "block-tokens/s",
+            "cores": cores, "kind": "oracle", "blas": blas_facts(),
+            "fp64_value": round(cfg.block_size * r64 / t64, 3),
+            "sample": f"1 sequence of {W.name} (ctx {c0}, {n0} new rows) per round: fusion, "
+                      f"K/V injection, forward, accept; NumPy oracle with its arithmetic in "
+                      f"float32: {r32} round(s) in {t32:.1f} s (value); in float64 (its parity "
+                      f"precision): {r64} round(s) in {t64:.1f} s (fp64_value)"}
 
 
 def bench_packed(a) -> int:

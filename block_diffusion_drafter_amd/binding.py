@@ -127,6 +127,8 @@ def lib() -> ctypes.CDLL:
                                            ctypes.POINTER(ctypes.c_double),
                                            ctypes.POINTER(ctypes.c_double)]
         L.dflash_profiler_reset.restype = i32
+        L.dflash_probe_mfma_bf16.restype = i32
+        L.dflash_probe_mfma_bf16.argtypes = [i32, i32, vp, ctypes.POINTER(ctypes.c_double), vp]
         _lib = L
     return _lib
 
@@ -437,3 +439,14 @@ def profiler_read() -> Dict[str, dict]:
 
 def profiler_reset() -> None:
     _check(lib().dflash_profiler_reset(), "dflash_profiler_reset")
+
+
+def probe_mfma_bf16(n_workgroups: int, iters: int, sink: torch.Tensor) -> float:
+    """Enqueue the MFMA calibration loop on the current stream; returns its flops.
+    sink: device fp32 tensor of at least n_workgroups * 8 entries."""
+    if sink.numel() < n_workgroups * 8 or sink.dtype != torch.float32 or not sink.is_cuda:
+        raise DFlashError("sink must be a device fp32 tensor of n_workgroups * 8 entries")
+    fl = ctypes.c_double()
+    _check(lib().dflash_probe_mfma_bf16(n_workgroups, iters, _ptr(sink), ctypes.byref(fl),
+                                        _stream()), "dflash_probe_mfma_bf16")
+    return fl.value

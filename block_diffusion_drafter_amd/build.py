@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 OUT_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libdflash.so")
 SOURCES = ["gemm.hip", "gemm_mfma.hip", "attention.hip", "elementwise.hip", "sampling.hip",
-           "api.hip"]
+           "probe.hip", "api.hip"]
 ARCH = os.environ.get("DFLASH_OFFLOAD_ARCH", "gfx950")
 
 

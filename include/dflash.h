@@ -408,6 +408,20 @@ int32_t dflash_profiler_read(int32_t kind, int64_t *launches, double *total_ms,
                              double *total_bytes, double *total_flops);
 int32_t dflash_profiler_reset(void);
 
+/* Measurement aid: a calibration loop for the MFMA roofline. Enqueues on
+ * stream n_workgroups workgroups of 8 waves (two per SIMD of a CU); every
+ * wave issues iters x 8 independent bf16 16x16x32 matrix multiply-accumulates
+ * on register operands with random bits and nothing else, so the time the
+ * caller measures around the launch gives the MFMA rate this chip sustains
+ * with every matrix core busy (its clock under that load, not the nominal
+ * one). *flops (optional host pointer) receives the launch's flop count,
+ * n_workgroups * 8 * iters * 8 * 2*16*16*32. sink: device fp32 buffer of at
+ * least n_workgroups * 8 entries (one value per wave; written so the loop
+ * cannot be optimised away). Errors: DFLASH_ERR_SHAPE (a count < 1),
+ * DFLASH_ERR_NULL (sink), DFLASH_ERR_HIP (launch). */
+int32_t dflash_probe_mfma_bf16(int32_t n_workgroups, int32_t iters, float *sink, double *flops,
+                               void *stream);
+
 #ifdef __cplusplus
 }
 #endif
