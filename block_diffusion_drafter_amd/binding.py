@@ -115,6 +115,9 @@ def lib() -> ctypes.CDLL:
         L.dflash_sample_drafts.restype = i32
         L.dflash_sample_drafts.argtypes = [vp, i64, i32, i32, ctypes.c_float, ctypes.c_uint64, i32,
                                            vp, vp, vp, i64, vp]
+        L.dflash_sample_drafts_static.restype = i32
+        L.dflash_sample_drafts_static.argtypes = [vp, i64, i32, i32, ctypes.c_float,
+                                                  ctypes.c_uint64, i32, vp, vp, vp]
         L.dflash_verify_sampled.restype = i32
         L.dflash_verify_sampled.argtypes = [vp, vp, vp, i32, i32, i32, ctypes.c_float,
                                             ctypes.c_uint64, i32, vp, vp, vp, vp, i64, vp]
@@ -399,6 +402,19 @@ def sample_drafts(logits: torch.Tensor, temperature: float, seed: int, rnd: int,
                                       float(temperature), int(seed), int(rnd), _ptr(tokens),
                                       _ptr(logq), _ptr(ws), ws.numel(), _stream()),
            "dflash_sample_drafts")
+
+
+def sample_drafts_static(logits: torch.Tensor, temperature: float, seed: int, rnd: int,
+                         tokens: torch.Tensor, logq: Optional[torch.Tensor] = None) -> None:
+    """sample_drafts without a workspace (the library's static scratch): for
+    callers that cannot allocate; rows * ceil(vocab / 8192) <= 16384."""
+    rows, vocab = logits.shape
+    if logits.dtype != torch.float32 or logits.stride(1) != 1:
+        raise DFlashError("logits must be fp32 with unit column stride")
+    _check(lib().dflash_sample_drafts_static(logits.data_ptr(), logits.stride(0), rows, vocab,
+                                             float(temperature), int(seed), int(rnd),
+                                             _ptr(tokens), _ptr(logq), _stream()),
+           "dflash_sample_drafts_static")
 
 
 def verify_sampled(drafts: torch.Tensor, draft_logits: torch.Tensor,

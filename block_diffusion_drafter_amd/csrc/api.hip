@@ -327,6 +327,7 @@ const char* dflash_status_string(int32_t code) {
     case DFLASH_ERR_UNSUPPORTED: return "configuration not covered by the kernels";
     case DFLASH_ERR_HIP: return "a HIP launch reported an error";
     case DFLASH_ERR_STATE: return "profiler misuse, or graph capture while the profiler records";
+    case DFLASH_ERR_SCRATCH: return "request exceeds the library's static scratch";
     default: return "unknown status";
   }
 }
@@ -786,6 +787,27 @@ int32_t dflash_sample_drafts(const float* logits, int64_t row_stride, int32_t ro
   prof_begin(DFLASH_K_SAMPLING, (double)rows * vocab * 4, 0.0, st);
   const hipError_t e = launch_sample_drafts(logits, row_stride, rows, vocab, temperature, seed,
                                             round, tokens, logq, ws, st);
+  prof_end(st);
+  return e == hipSuccess ? DFLASH_OK : DFLASH_ERR_HIP;
+}
+
+int32_t dflash_sample_drafts_static(const float* logits, int64_t row_stride, int32_t rows,
+                                    int32_t vocab, float temperature, uint64_t seed,
+                                    int32_t round, int32_t* tokens, float* logq, void* stream) {
+  if (rows < 0 || vocab < 2 || row_stride < vocab || !(temperature > 0.f) ||
+      !std::isfinite(temperature))
+    return DFLASH_ERR_SHAPE;
+  if (rows == 0) return DFLASH_OK;
+  if (!logits || !tokens) return DFLASH_ERR_NULL;
+  if (!al16(logits) || !al16(tokens) || (logq && !al16(logq))) return DFLASH_ERR_ALIGN;
+  // The size check comes first: an oversized request touches no device state.
+  if (sample_ws_bytes(rows, vocab) > sample_static_scratch_bytes()) return DFLASH_ERR_SCRATCH;
+  void* scratch = nullptr;
+  if (sample_static_scratch(&scratch) != hipSuccess) return DFLASH_ERR_HIP;
+  hipStream_t st = (hipStream_t)stream;
+  prof_begin(DFLASH_K_SAMPLING, (double)rows * vocab * 4, 0.0, st);
+  const hipError_t e = launch_sample_drafts(logits, row_stride, rows, vocab, temperature, seed,
+                                            round, tokens, logq, scratch, st);
   prof_end(st);
   return e == hipSuccess ? DFLASH_OK : DFLASH_ERR_HIP;
 }

@@ -254,6 +254,11 @@ hipError_t launch_verify_sampled(const int32_t* drafts, const float* draft_logit
                                  int32_t* out_token, int32_t* anchor_out, void* ws,
                                  hipStream_t st);
 
+// The static scratch of the allocation-free drafting call: its size, and its
+// device address on the current device (looked up once per device).
+int64_t sample_static_scratch_bytes();
+hipError_t sample_static_scratch(void** out);
+
 // Profiler hooks (api.hip).
 void prof_begin(int kind, double bytes, double flops, hipStream_t st);
 void prof_end(hipStream_t st);

@@ -14,6 +14,7 @@
 // logits (4 per thread, one Philox block per thread), so a batch of a few
 // rows still spreads over many CUs; small kernels merge the splits.
 #include <cmath>
+#include <mutex>
 
 #include "common.h"
 #include "internal.h"
@@ -362,6 +363,42 @@ hipError_t launch_verify_sampled(const int32_t* drafts, const float* draft_logit
   hipLaunchKernelGGL(verify_finish_kernel, dim3((batch + 63) / 64), dim3(64), 0, st, keys, ns,
                      batch, block, acc, accept_len, out_token, anchor_out);
   return hipGetLastError();
+}
+
+// ---- allocation-free drafting ------------------------------------------------
+// The split statistics of dflash_sample_drafts_static live in this file-scope
+// device array instead of a caller workspace. Each GPU the library runs on
+// holds its own copy (at its own address) until the process ends. In host
+// code `sample_scratch` names a host-side stand-in, never the device memory:
+// the device address is taken once per device with hipGetSymbolAddress and
+// only that address is handed to kernels.
+constexpr int64_t kSampleScratchBytes = 256 * 1024;
+static __device__ __align__(256) unsigned char sample_scratch[kSampleScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+int64_t sample_static_scratch_bytes() { return kSampleScratchBytes; }
+
+hipError_t sample_static_scratch(void** out) {
+  *out = nullptr;
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(sample_scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 }  // namespace dflash

@@ -55,7 +55,8 @@ typedef enum dflash_status {
   DFLASH_ERR_WORKSPACE = -5,     /* workspace or packed buffer smaller than its size query */
   DFLASH_ERR_UNSUPPORTED = -6,   /* a configuration the kernels do not cover */
   DFLASH_ERR_HIP = -7,           /* a HIP launch reported an error */
-  DFLASH_ERR_STATE = -8          /* profiler misuse, or graph capture while it records */
+  DFLASH_ERR_STATE = -8,         /* profiler misuse, or graph capture while it records */
+  DFLASH_ERR_SCRATCH = -9        /* request larger than the library's static scratch */
 } dflash_status;
 
 typedef enum dflash_dtype { DFLASH_FP32 = 0, DFLASH_BF16 = 1 } dflash_dtype;
@@ -319,6 +320,24 @@ int64_t dflash_sampling_workspace_bytes(int32_t batch, int32_t block_size, int32
 int32_t dflash_sample_drafts(const float *logits, int64_t row_stride, int32_t rows, int32_t vocab,
                              float temperature, uint64_t seed, int32_t round, int32_t *tokens,
                              float *logq, void *ws, int64_t ws_bytes, void *stream);
+/* dflash_sample_drafts without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc). Same arguments, kernels, random numbers and results
+ * as dflash_sample_drafts; the per-(row, 8192-logit split) statistics that the
+ * workspace would hold (16 bytes each) live instead in a file-scope device
+ * array of 256 KiB inside the library, which every GPU the library runs on
+ * holds until the process ends. So rows * ceil(vocab / 8192) <= 16384 (e.g.
+ * 480 rows at vocab 151936, 512 at 262144); a larger request returns
+ * DFLASH_ERR_SCRATCH before anything is enqueued. Nothing is allocated: the
+ * array's device address is looked up once per device on the first call there
+ * (DFLASH_ERR_HIP if that fails). Every entry of the scratch that a call reads
+ * is written by the same call first, so no clearing is needed between calls.
+ * All calls on one GPU share that GPU's array: calls that may overlap on one
+ * device (different streams, or several host threads) race on it and must be
+ * serialised by the caller. Other errors as dflash_sample_drafts. */
+int32_t dflash_sample_drafts_static(const float *logits, int64_t row_stride, int32_t rows,
+                                    int32_t vocab, float temperature, uint64_t seed,
+                                    int32_t round, int32_t *tokens, float *logq, void *stream);
 int32_t dflash_verify_sampled(const int32_t *drafts, const float *draft_logits,
                               const float *target_logits, int32_t batch, int32_t block_size,
                               int32_t vocab, float temperature, uint64_t seed, int32_t round,

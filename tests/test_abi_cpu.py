@@ -29,7 +29,7 @@ def test_exports_every_declared_function():
 
 def test_status_strings():
     lib = B.lib()
-    for code in range(0, -9, -1):
+    for code in range(0, -10, -1):
         s = lib.dflash_status_string(code).decode()
         assert s and s != "unknown status", code
     assert lib.dflash_status_string(-99).decode() == "unknown status"
@@ -307,3 +307,18 @@ def test_packed_block_attention_rejects_bad_arguments_before_launching():
     # nothing to do: no launch, no pointer needed
     assert call(h, ctypes.byref(cache), 0, 1, 0, None, None, None, None, None, None, None) == 0
     lib.dflash_destroy(h)
+
+
+def test_sample_drafts_static_checks_on_the_host():
+    """The allocation-free drafting call refuses, before touching any device
+    state, a request larger than its static scratch (16384 split entries of
+    8192 logits), and bad shapes; an empty request is a no-op."""
+    lib = B.lib()
+    f = lib.dflash_sample_drafts_static
+    assert f(FAKE, 16384, 8193, 16384, 1.0, 1, 0, FAKE, None, None) == -9      # 16386 entries
+    assert f(FAKE, 8192 * 32, 513, 8192 * 32, 1.0, 1, 0, FAKE, None, None) == -9
+    assert f(FAKE, 1000, 4, 1000, 0.0, 1, 0, FAKE, None, None) == -2           # T <= 0
+    assert f(FAKE, 999, 4, 1000, 1.0, 1, 0, FAKE, None, None) == -2            # stride < vocab
+    assert f(None, 1000, 4, 1000, 1.0, 1, 0, FAKE, None, None) == -1
+    assert f(FAKE + 4, 1000, 4, 1000, 1.0, 1, 0, FAKE, None, None) == -4
+    assert f(FAKE, 1000, 0, 1000, 1.0, 1, 0, None, None, None) == 0            # nothing to do
