@@ -119,7 +119,8 @@ bool packs_rows(int dtype, int M, int K) {
 struct Plan {
   size_t x, h, qkv, q, po, pml, attn, act, y, amax, arr, part, sq, fwd_end;
   size_t u, ua, upart, proj_end;  // ua: tiled copy of the fused features (MFMA path)
-  size_t kv, ca, kvpart, app_end;  // ca: tiled copy of the context rows (MFMA path)
+  size_t kv, ca, kvpart, lens, app_end;  // ca: tiled copy of the context rows (MFMA path);
+                                         // lens: ctx_len snapshot [batch]
   int64_t part_elems, upart_elems, kvpart_elems;  // split-K partials (floats)
   int attn_wg, n_vtiles;  // attention workgroups per KV head; LM-head keys per row
   size_t total;
@@ -200,6 +201,7 @@ Plan make_plan(const dflash_config& c, int batch, int cap, int max_tokens) {
   p.ca = packs_rows(dt, max_tokens, (int)d) ? take(tiled_bytes(dt, max_tokens, (int)d)) : 0;
   p.kvpart_elems = splitk_elems_upto(dt, max_tokens, (int)(c.n_layers * 2 * Hkv * hd), (int)d);
   p.kvpart = take((size_t)p.kvpart_elems * 4);
+  p.lens = take((size_t)batch * 4);
   p.app_end = off;
   p.total = std::max(p.fwd_end, std::max(p.proj_end, p.app_end));
   return p;
@@ -491,7 +493,7 @@ static int32_t append_rows(const dflash_handle* h, const dflash_kv_cache* cache,
   if (!cu_new && !accept_len) return DFLASH_ERR_NULL;
   if (n_tok > 0 && (!ctx || !ws)) return DFLASH_ERR_NULL;
   if ((ctx && !al16(ctx)) || (ws && !al16(ws))) return DFLASH_ERR_ALIGN;
-  const Plan P = make_plan(c, 1, cache->capacity, n_tok);
+  const Plan P = make_plan(c, cache->batch, cache->capacity, n_tok);
   if (n_tok > 0 && ws_bytes < (int64_t)P.app_end) return DFLASH_ERR_WORKSPACE;
   hipStream_t st = (hipStream_t)stream;
   const int Hkv = c.n_kv_heads, hd = c.head_dim, L = c.n_layers;
@@ -514,6 +516,12 @@ static int32_t append_rows(const dflash_handle* h, const dflash_kv_cache* cache,
     }
     g.out = kv;
     g.out_stride = N;
+    // The projection snapshots ctx_len; the scatter reads the rows' positions
+    // from the snapshot and updates ctx_len itself (no third launch).
+    int32_t* lens = reinterpret_cast<int32_t*>((char*)ws + P.lens);
+    g.snap_src = cache->ctx_len;
+    g.snap_dst = lens;
+    g.snap_n = cache->batch;
     rc = run_gemm(c.dtype, EPI_STORE_F32, g, st);
     if (rc) return rc;
     NormRopeArgs a;
@@ -523,7 +531,8 @@ static int32_t append_rows(const dflash_handle* h, const dflash_kv_cache* cache,
     a.k_cache = cache->k;
     a.v_cache = cache->v;
     for (int l = 0; l < L; ++l) a.k_norm[l] = h->layers[l].k_norm;
-    a.ctx_len = cache->ctx_len;
+    a.ctx_len = lens;
+    a.ctx_len_out = cache->ctx_len;
     a.cu_new = cu_new;
     a.accept_len = accept_len;
     a.dev_status = dev_status;
@@ -541,8 +550,9 @@ static int32_t append_rows(const dflash_handle* h, const dflash_kv_cache* cache,
     prof_begin(DFLASH_K_NORM_ROPE, 0, 0, st);
     hipError_t e = launch_norm_rope_append(c.dtype, a, st);
     prof_end(st);
-    if (e != hipSuccess) return DFLASH_ERR_HIP;
+    return e == hipSuccess ? DFLASH_OK : DFLASH_ERR_HIP;
   }
+  // No rows: only the length bookkeeping (and the offset checks).
   prof_begin(DFLASH_K_SMALL, 0, 0, st);
   hipError_t e = launch_ctx_len_add(cache->ctx_len, cu_new, accept_len, c.block_size,
                                     cache->batch, n_tok, cache->capacity, dev_status, st);

@@ -238,6 +238,66 @@ hipError_t launch_embed(int dtype, const void* embed, const int32_t* anchor, int
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Per-head q/k RMSNorm + rotary embedding + K/V cache scatter.
+//
+// Rotary pairs: a head vector of HD channels is HD/2 pairs (channel c with
+// c + HD/2). The angle pos * inv_freq is formed in double (positions reach
+// tens of thousands of radians), reduced by 2 pi in double (Cody-Waite: 2 pi
+// as the nearest double plus its remainder), and the reduced angle goes to
+// the fp32 sincos.
+//
+// Forward (the block's rows, norm_rope_fwd_kernel): one workgroup per row
+// and group of heads, many short workgroups (at batch 1 a handful of rows
+// must still spread over the chip).
+//
+// Append (an append's new context rows, norm_rope_append_kernel): a
+// workgroup takes a tile of up to 16 consecutive new rows of ONE sequence
+// (stored at consecutive positions pos0 .. pos0 + nrows - 1) and HG of the
+// rows' head vectors (every layer's K and V heads). Keeping a sequence's rows
+// together lets the V heads be written well: V is stored channel-major inside
+// 32-position blocks, so one channel's values at consecutive positions are
+// adjacent in memory; each V head is staged in LDS and written transposed, 16
+// lanes per channel run (a wave store covers 4 channels x 16 positions). The
+// tile's (cos, sin) table is built once per workgroup. The kernel also
+// advances ctx_len: it reads the rows' positions from a snapshot of ctx_len
+// that the projection before it took, so one workgroup may update the live
+// array at any time (one launch instead of a separate length update).
+// ---------------------------------------------------------------------------
+constexpr int kNrRows = 16;
+
+__device__ __forceinline__ float2 rope_cs(const NormRopeArgs& p, int pos, int pair) {
+  float c = 1.f, s = 0.f;
+  if (p.rope_theta > 0.f) {
+    constexpr double kTwoPiHi = 6.283185307179586;         // nearest double to 2 pi
+    constexpr double kTwoPiLo = 2.4492935982947064e-16;    // 2 pi - kTwoPiHi
+    const double ang = (double)pos * p.inv_freq[pair];
+    const double k = rint(ang * (1.0 / kTwoPiHi));
+    const double r = fma(-k, kTwoPiLo, fma(-k, kTwoPiHi, ang));
+    sincosf((float)r, &s, &c);
+  }
+  return make_float2(c, s);
+}
+
+// Sum over the PAIRS lanes of one head (lanes with the same `sub`).
+template <int PAIRS>
+__device__ __forceinline__ float head_sum(float v) {
+#pragma unroll
+  for (int o = PAIRS / 2; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// Per-head RMSNorm (gain g0, g1 of the lane's pair) and rotation of one pair.
+template <int HD>
+__device__ __forceinline__ void norm_rope_pair(float x0, float x1, float g0, float g1, float eps,
+                                               float2 cs, float& o0, float& o1) {
+  const float ss = head_sum<HD / 2>(x0 * x0 + x1 * x1);
+  const float inv = rsqrtf(ss / (float)HD + eps);
+  const float y0 = x0 * inv * g0, y1 = x1 * inv * g1;
+  o0 = y0 * cs.x - y1 * cs.y;
+  o1 = y1 * cs.x + y0 * cs.y;
+}
+
 // Rotary pairs of one row: a head vector of HD channels is HD/2 pairs
 // (channel c with c + HD/2). A wave covers 64 / (HD/2) heads at once: lane
 // (sub, c) with c = lane % (HD/2) owns pair c of the iteration's head sub.
@@ -263,25 +323,6 @@ struct RopeLane {
     }
   }
 };
-
-// Sum over the PAIRS lanes of one head (lanes with the same `sub`).
-template <int PAIRS>
-__device__ __forceinline__ float head_sum(float v) {
-#pragma unroll
-  for (int o = PAIRS / 2; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
-}
-
-// Per-head RMSNorm (gain g0, g1 of the lane's pair) and rotation of one pair.
-template <int HD>
-__device__ __forceinline__ void norm_rope_pair(float x0, float x1, float g0, float g1, float eps,
-                                               const RopeLane<HD>& r, float& o0, float& o1) {
-  const float ss = head_sum<HD / 2>(x0 * x0 + x1 * x1);
-  const float inv = rsqrtf(ss / (float)HD + eps);
-  const float y0 = x0 * inv * g0, y1 = x1 * inv * g1;
-  o0 = y0 * r.c - y1 * r.s;
-  o1 = y1 * r.c + y0 * r.s;
-}
 
 // Pair c of a V head row at position pos (V is stored in 32-position blocks,
 // channel-major inside a block).
@@ -352,7 +393,8 @@ __global__ __launch_bounds__(256) void norm_rope_fwd_kernel(NormRopeArgs p) {
     const bool is_q = hc < Hq, is_v = hc >= Hq + Hkv;
     float o0 = x0[it], o1 = x1[it];
     if (!is_v)
-      norm_rope_pair<HD>(x0[it], x1[it], is_q ? qg0 : kg0, is_q ? qg1 : kg1, p.eps, rope, o0, o1);
+      norm_rope_pair<HD>(x0[it], x1[it], is_q ? qg0 : kg0, is_q ? qg1 : kg1, p.eps,
+                         make_float2(rope.c, rope.s), o0, o1);
     if (h >= NH) continue;
     if (is_q) {
       T* qo = reinterpret_cast<T*>(p.q_out) + (((size_t)s * Hq + h) * 16 + i) * HD;
@@ -373,82 +415,201 @@ __global__ __launch_bounds__(256) void norm_rope_fwd_kernel(NormRopeArgs p) {
   }
 }
 
-// Append mode: grid (appended rows, column groups); column
-// col = layer * 2*Hkv + hh of the row (hh < Hkv a key head, else a value
-// head) is written to position ctx_len[s] + (row's index in its sequence) of
-// that layer's cache.
-template <typename T, int HD, int IT>
-__global__ __launch_bounds__(256) void norm_rope_append_kernel(NormRopeArgs p) {
-  using RL = RopeLane<HD>;
-  const int row = blockIdx.x;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int sub = lane / RL::PAIRS, c = lane % RL::PAIRS;
-  const int Hkv = p.n_kv_heads, NC = p.n_layers * 2 * Hkv;
-  const int cbase = blockIdx.y * nr_heads_per_wg<HD, IT>() + wave * RL::HPW + sub;
-  const bool flagger = threadIdx.x == 0 && blockIdx.y == 0;
-  int s = -1, i = 0;
+struct NrTile {
+  int s;       // sequence (-1: this workgroup has no tile)
+  int row0;    // first source row
+  int nrows;   // rows in the tile (<= 16)
+  int pos0;    // cache position of the first row
+};
+
+// Where the tile of workgroup blockIdx.x lies (p.ctx_len is the snapshot).
+//   Accepted rows: sequence blockIdx.x, rows s*B + i for i <= accept_len[s],
+//     at ctx_len[s] + i.
+//   Prefix offsets: the sequences' new rows cut into tiles of 16
+//     (ceil(n_s / 16) tiles for sequence s, in order); wave 0 scans the tile
+//     counts 64 sequences at a time. Rows outside [0, n_tok) are never read.
+__device__ __forceinline__ NrTile nr_locate(const NormRopeArgs& p, int* sh) {
+  NrTile t{-1, 0, 0, 0};
   if (p.accept_len) {
-    // block rows: position i of sequence s, kept for i <= accept length
-    s = row / p.block;
-    i = row - s * p.block;
-    if (i > accepted_rows(p.accept_len[s], p.block) - 1) return;
-  } else {
-    for (int t = 0; t < p.batch; ++t) {
-      if (p.cu_new[t] <= row && row < p.cu_new[t + 1]) {
-        s = t;
-        break;
-      }
-    }
-    if (s < 0) {
-      if (flagger && p.dev_status) atomicOr(p.dev_status, DFLASH_DEV_OFFSETS);
-      return;
-    }
-    i = row - p.cu_new[s];
+    const int s = blockIdx.x;
+    if (s >= p.batch) return t;
+    int cl = p.ctx_len[s];
+    cl = cl < 0 ? 0 : cl;
+    t.s = s;
+    t.row0 = s * p.block;
+    t.nrows = accepted_rows(p.accept_len[s], p.block);
+    t.pos0 = cl;
+    return t;
   }
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x, T = blockIdx.x;
+    int carry = 0, found = -1, before = 0;
+    for (int base = 0; base < p.batch && found < 0; base += 64) {
+      const int s = base + lane;
+      int n = 0;
+      if (s < p.batch) n = max(0, p.cu_new[s + 1] - p.cu_new[s]);
+      const int own = (n + kNrRows - 1) / kNrRows;
+      int v = own;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int u = __shfl_up(v, o);
+        if (lane >= o) v += u;
+      }
+      // first lane whose inclusive prefix passes T
+      const unsigned long long hit = __ballot(s < p.batch && carry + v > T);
+      if (hit) {
+        const int l = __ffsll((long long)hit) - 1;
+        found = base + l;
+        before = carry + __shfl(v - own, l);
+      }
+      carry += __shfl(v, 63);
+    }
+    if (lane == 0) {
+      sh[0] = found;
+      sh[1] = found < 0 ? 0 : T - before;
+    }
+  }
+  __syncthreads();
+  const int s = sh[0];
+  if (s < 0) return t;
+  const int ti = sh[1];
+  const int n = max(0, p.cu_new[s + 1] - p.cu_new[s]);
   int cl = p.ctx_len[s];
   cl = cl < 0 ? 0 : cl;
-  const int pos = cl + i;
-  if (pos >= p.cap) {
-    if (flagger && p.dev_status) atomicOr(p.dev_status, DFLASH_DEV_CAPACITY);
-    return;
+  t.s = s;
+  t.row0 = p.cu_new[s] + kNrRows * ti;
+  t.nrows = min(kNrRows, n - kNrRows * ti);
+  if (t.row0 < 0) t.nrows = 0;
+  t.nrows = min(t.nrows, p.n_tok - t.row0);
+  t.pos0 = cl + kNrRows * ti;
+  return t;
+}
+
+// Append only, workgroup (0, 0): ctx_len[s] = snapshot[s] + rows of s (the
+// kernel reads positions from the snapshot, so this may happen at any time),
+// clamped to the capacity, with the offset checks of the prefix mode.
+__device__ __forceinline__ void nr_update_lengths(const NormRopeArgs& p) {
+  if (threadIdx.x == 0 && !p.accept_len &&
+      (p.cu_new[0] != 0 || p.cu_new[p.batch] != p.n_tok) && p.dev_status)
+    atomicOr(p.dev_status, DFLASH_DEV_OFFSETS);
+  for (int s = threadIdx.x; s < p.batch; s += blockDim.x) {
+    int n;
+    if (p.accept_len) {
+      const int a = p.accept_len[s];
+      if ((a < 0 || a >= p.block) && p.dev_status) atomicOr(p.dev_status, DFLASH_DEV_OFFSETS);
+      n = accepted_rows(a, p.block);
+    } else {
+      n = p.cu_new[s + 1] - p.cu_new[s];
+      if (n < 0) {
+        if (p.dev_status) atomicOr(p.dev_status, DFLASH_DEV_OFFSETS);
+        n = 0;
+      }
+    }
+    int cl = p.ctx_len[s];
+    cl = cl < 0 ? 0 : cl;
+    int nl = cl + n;
+    if (nl > p.cap) {
+      if (p.dev_status) atomicOr(p.dev_status, DFLASH_DEV_CAPACITY);
+      nl = p.cap;
+    }
+    p.ctx_len_out[s] = nl;
   }
-  const float* src = p.src + (int64_t)row * p.src_stride;
-  float x0[IT], x1[IT];
+}
+
+// grid (tiles, head groups of HG). Head h = l * 2 Hkv + hh of the stacked
+// context projection's row: hh < Hkv a key head of layer l, else a value head.
+template <typename T, int HD, int HG>
+__global__ __launch_bounds__(256) void norm_rope_append_kernel(NormRopeArgs p) {
+  constexpr int PAIRS = HD / 2;
+  constexpr int HPW = 64 / PAIRS;                    // items per wave step
+  constexpr int NIT = kNrRows * HG / (4 * HPW);      // items per lane group
+  constexpr int VS = HD + 4;                         // LDS row stride of a staged V head
+  static_assert(NIT * 4 * HPW == kNrRows * HG, "items split evenly");
+  __shared__ float2 rtab[kNrRows * PAIRS];
+  __shared__ float vst[HG][kNrRows][VS];
+  __shared__ int sh[2];
+
+  if (blockIdx.x == 0 && blockIdx.y == 0) nr_update_lengths(p);
+  const NrTile tile = nr_locate(p, sh);
+  if (tile.s < 0 || tile.nrows <= 0) return;
+  const int s = tile.s;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int sub = lane / PAIRS, c = lane % PAIRS;
+  const int Hkv = p.n_kv_heads;
+  const int NH = p.n_layers * 2 * Hkv;
+  const int h0 = blockIdx.y * HG;
+  // Rows at or past the capacity are dropped (and flagged).
+  const int nvalid = max(0, min(tile.nrows, p.cap - tile.pos0));
+  if (nvalid < tile.nrows && threadIdx.x == 0 && blockIdx.y == 0 && p.dev_status)
+    atomicOr(p.dev_status, DFLASH_DEV_CAPACITY);
+
+  for (int e = threadIdx.x; e < kNrRows * PAIRS; e += blockDim.x)
+    rtab[e] = (e / PAIRS) < tile.nrows ? rope_cs(p, tile.pos0 + e / PAIRS, e % PAIRS)
+                                       : make_float2(1.f, 0.f);
+
+  // Phase 1: every (head, row) item of the lane group (lane (sub, c) owns
+  // pair c of item sub): loads first, then norm + rotation; K rows are stored
+  // directly, V rows staged in LDS.
+  float x0[NIT], x1[NIT];
 #pragma unroll
-  for (int it = 0; it < IT; ++it) {
-    const int cc = min(cbase + it * 4 * RL::HPW, NC - 1);
-    x0[it] = src[cc * HD + c];
-    x1[it] = src[cc * HD + c + RL::PAIRS];
+  for (int it = 0; it < NIT; ++it) {
+    const int item = (it * 4 + wave) * HPW + sub;
+    const int k = item / kNrRows, i = item % kNrRows, h = h0 + k;
+    x0[it] = x1[it] = 0.f;
+    if (h < NH && i < tile.nrows) {
+      const float* src = p.src + (int64_t)(tile.row0 + i) * p.src_stride + (int64_t)h * HD;
+      x0[it] = src[c];
+      x1[it] = src[c + PAIRS];
+    }
   }
-  const RL rope(p, pos, c);
+  __syncthreads();  // rtab
   const size_t layer_stride = (size_t)p.cache_batch * Hkv * p.cap * HD;
 #pragma unroll
-  for (int it = 0; it < IT; ++it) {
-    const int col = cbase + it * 4 * RL::HPW;
-    const int cc = min(col, NC - 1);
-    const int l = cc / (2 * Hkv), hh = cc % (2 * Hkv);
-    float o0 = x0[it], o1 = x1[it];
-    if (hh < Hkv) {
-      const T* kg = reinterpret_cast<const T*>(p.k_norm[l]);
-      norm_rope_pair<HD>(x0[it], x1[it], to_f32(kg[c]), to_f32(kg[c + RL::PAIRS]), p.eps, rope,
-                         o0, o1);
+  for (int it = 0; it < NIT; ++it) {
+    const int item = (it * 4 + wave) * HPW + sub;
+    const int k = item / kNrRows, i = item % kNrRows, h = h0 + k;
+    const int l = min(h, NH - 1) / (2 * Hkv), hh = min(h, NH - 1) % (2 * Hkv);
+    if (hh >= Hkv) {  // value head (or past the last head): staged
+      vst[k][i][c] = x0[it];
+      vst[k][i][c + PAIRS] = x1[it];
+      continue;
     }
-    if (col >= NC) continue;
-    if (hh >= Hkv) {
-      const int g = hh - Hkv;
-      store_v<T, HD>(reinterpret_cast<T*>(p.v_cache) + l * layer_stride +
-                         (size_t)(s * Hkv + g) * p.cap * HD,
-                     pos, c, o0, o1);
-    } else {
+    const int g = hh;
+    const T* gp = reinterpret_cast<const T*>(p.k_norm[l]);
+    float o0, o1;
+    norm_rope_pair<HD>(x0[it], x1[it], to_f32(gp[c]), to_f32(gp[c + PAIRS]), p.eps,
+                       rtab[i * PAIRS + c], o0, o1);
+    if (h < NH && i < nvalid) {
       T* kr = reinterpret_cast<T*>(p.k_cache) + l * layer_stride +
-              ((size_t)(s * Hkv + hh) * p.cap + pos) * HD;
+              ((size_t)(s * Hkv + g) * p.cap + tile.pos0 + i) * HD;
       kr[c] = from_f32<T>(o0);
-      kr[c + RL::PAIRS] = from_f32<T>(o1);
+      kr[c + PAIRS] = from_f32<T>(o1);
+    }
+  }
+  __syncthreads();  // vst
+
+  // Phase 2: the staged V heads, transposed: thread (c4, j) writes channel
+  // 16 cg + c4 at position pos0 + j, cg = 0 .. HD/16 - 1.
+  const int j = threadIdx.x & 15, c4 = threadIdx.x >> 4;
+  const int pos = tile.pos0 + j;
+#pragma unroll
+  for (int k = 0; k < HG; ++k) {
+    const int h = h0 + k;
+    if (h >= NH) break;
+    const int l = h / (2 * Hkv), hh = h % (2 * Hkv);
+    if (hh < Hkv || j >= nvalid) continue;
+    const int g = hh - Hkv;
+    T* vb = reinterpret_cast<T*>(p.v_cache) + l * layer_stride + (size_t)(s * Hkv + g) * p.cap * HD +
+            (size_t)(pos / kKeyBlock) * HD * kKeyBlock + (pos % kKeyBlock);
+#pragma unroll
+    for (int cg = 0; cg < HD / 16; ++cg) {
+      const int ch = 16 * cg + c4;
+      vb[(size_t)ch * kKeyBlock] = from_f32<T>(vst[k][j][ch]);
     }
   }
 }
 
-template <int MODE, int IT>
+template <int IT>
 static hipError_t launch_nr_it(int dtype, const NormRopeArgs& a, int rows, int n_cols,
                                hipStream_t st) {
   const bool bf = dtype == DFLASH_BF16;
@@ -458,21 +619,11 @@ static hipError_t launch_nr_it(int dtype, const NormRopeArgs& a, int rows, int n
                                                    nr_heads_per_wg<HD, IT>()),              \
                      blk, 0, st, a)
   if (a.head_dim == 128) {
-    if (MODE == 0) {
-      if (bf) DF_NR(norm_rope_fwd_kernel, bf16, 128);
-      else DF_NR(norm_rope_fwd_kernel, float, 128);
-    } else {
-      if (bf) DF_NR(norm_rope_append_kernel, bf16, 128);
-      else DF_NR(norm_rope_append_kernel, float, 128);
-    }
+    if (bf) DF_NR(norm_rope_fwd_kernel, bf16, 128);
+    else DF_NR(norm_rope_fwd_kernel, float, 128);
   } else if (a.head_dim == 64) {
-    if (MODE == 0) {
-      if (bf) DF_NR(norm_rope_fwd_kernel, bf16, 64);
-      else DF_NR(norm_rope_fwd_kernel, float, 64);
-    } else {
-      if (bf) DF_NR(norm_rope_append_kernel, bf16, 64);
-      else DF_NR(norm_rope_append_kernel, float, 64);
-    }
+    if (bf) DF_NR(norm_rope_fwd_kernel, bf16, 64);
+    else DF_NR(norm_rope_fwd_kernel, float, 64);
   } else {
     return hipErrorInvalidValue;
   }
@@ -481,11 +632,27 @@ static hipError_t launch_nr_it(int dtype, const NormRopeArgs& a, int rows, int n
 }
 
 // rows x n_cols head vectors; IT = 1 below 128 rows.
-template <int MODE>
-static hipError_t launch_nr(int dtype, const NormRopeArgs& a, int rows, int n_cols,
-                            hipStream_t st) {
-  if (rows < 128) return launch_nr_it<MODE, 1>(dtype, a, rows, n_cols, st);
-  return launch_nr_it<MODE, 4>(dtype, a, rows, n_cols, st);
+static hipError_t launch_nr_fwd(int dtype, const NormRopeArgs& a, int rows, int n_cols,
+                                hipStream_t st) {
+  if (rows < 128) return launch_nr_it<1>(dtype, a, rows, n_cols, st);
+  return launch_nr_it<4>(dtype, a, rows, n_cols, st);
+}
+
+template <int HG>
+static hipError_t launch_nr_append(int dtype, const NormRopeArgs& a, int tiles, int n_heads,
+                                   hipStream_t st) {
+  const dim3 grid(tiles, (n_heads + HG - 1) / HG), blk(256);
+  const bool bf = dtype == DFLASH_BF16;
+  if (a.head_dim == 128) {
+    if (bf) hipLaunchKernelGGL((norm_rope_append_kernel<bf16, 128, HG>), grid, blk, 0, st, a);
+    else hipLaunchKernelGGL((norm_rope_append_kernel<float, 128, HG>), grid, blk, 0, st, a);
+  } else if (a.head_dim == 64) {
+    if (bf) hipLaunchKernelGGL((norm_rope_append_kernel<bf16, 64, HG>), grid, blk, 0, st, a);
+    else hipLaunchKernelGGL((norm_rope_append_kernel<float, 64, HG>), grid, blk, 0, st, a);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 // The rotary inverse frequencies of the config, in double.
@@ -499,12 +666,21 @@ static NormRopeArgs with_inv_freq(const NormRopeArgs& a0) {
 }
 
 hipError_t launch_norm_rope_forward(int dtype, const NormRopeArgs& a, hipStream_t st) {
-  return launch_nr<0>(dtype, with_inv_freq(a), a.batch * 16, a.n_heads + 2 * a.n_kv_heads, st);
+  return launch_nr_fwd(dtype, with_inv_freq(a), a.batch * 16, a.n_heads + 2 * a.n_kv_heads, st);
 }
 
+// Heads per workgroup: 2 while the tiles are few (more workgroups in
+// flight), 4 from 64 tiles (each row's rotary table serves more heads).
+
 hipError_t launch_norm_rope_append(int dtype, const NormRopeArgs& a, hipStream_t st) {
-  if (a.n_tok <= 0) return hipSuccess;
-  return launch_nr<1>(dtype, with_inv_freq(a), a.n_tok, a.n_layers * 2 * a.n_kv_heads, st);
+  if (a.n_tok <= 0 || !a.ctx_len_out) return hipErrorInvalidValue;
+  if (a.block > kNrRows) return hipErrorInvalidValue;
+  // prefix offsets: at most ceil(n_tok / 16) + batch tiles (each sequence's
+  // last tile may be partial)
+  const int tiles = a.accept_len ? a.batch : (a.n_tok + kNrRows - 1) / kNrRows + a.batch;
+  const int nh = a.n_layers * 2 * a.n_kv_heads;
+  if (tiles < 64) return launch_nr_append<2>(dtype, with_inv_freq(a), tiles, nh, st);
+  return launch_nr_append<4>(dtype, with_inv_freq(a), tiles, nh, st);
 }
 
 // One workgroup per draft row: its 1024 threads reduce the row's per-column

@@ -115,6 +115,7 @@ void gemm_mfma_kernel(GemmArgs p, int n_colblk, int n_rowblk) {
   const int xcd = id & 7, q = id >> 3;
   const int rb = q % n_rowblk;
   const int cb = (q / n_rowblk) * 8 + xcd;
+  gemm_snapshot(p, blockIdx.x == 0);
   if (cb >= n_colblk) return;
 
   const int lane = threadIdx.x & 63;
@@ -396,6 +397,7 @@ void gemm_pipe_kernel(GemmArgs p, int n_colblk, int n_rowblk) {
   const int xcd = id & 7, q = id >> 3;
   const int rb = q % n_rowblk;
   const int cb = (q / n_rowblk) * 8 + xcd;
+  gemm_snapshot(p, blockIdx.x == 0);
   if (cb >= n_colblk) return;
 
   const int lane = threadIdx.x & 63;

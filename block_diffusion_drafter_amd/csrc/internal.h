@@ -74,7 +74,20 @@ struct GemmArgs {
   float* sq_out;
   const float* sq_in;
   int sq_d;
+  // Workgroup 0 of the projection copies snap_n int32 values from snap_src to
+  // snap_dst before anything else (a context-K/V append snapshots ctx_len
+  // this way, so its scatter kernel reads positions from the copy and may
+  // update ctx_len itself). Unused: snap_dst == nullptr.
+  const int32_t* snap_src;
+  int32_t* snap_dst;
+  int snap_n;
 };
+
+// The snapshot of GemmArgs::snap_*, made by the workgroup whose flat index is 0.
+__device__ __forceinline__ void gemm_snapshot(const GemmArgs& p, bool first_wg) {
+  if (p.snap_dst && first_wg)
+    for (int i = threadIdx.x; i < p.snap_n; i += blockDim.x) p.snap_dst[i] = p.snap_src[i];
+}
 
 // Launch geometry of one weight-streaming GEMM (also used to size LM-head partials).
 struct GemmPlan {
@@ -199,6 +212,8 @@ struct NormRopeArgs {
   const int32_t* cu_new;  // append mode: row offsets of each sequence's new rows
   const int32_t* accept_len;  // append mode, block rows: when non-null, row s*block + i of
                               // sequence s is appended iff i <= accept_len[s] (cu_new unused)
+  int32_t* ctx_len_out;   // append mode: ctx_len (the live array, updated by the kernel);
+                          // ctx_len above then points at a snapshot taken before the call
   int32_t* dev_status;
   int batch, cache_batch, n_heads, n_kv_heads, head_dim, block, cap, n_layers;
   int n_tok;              // append mode
