@@ -379,6 +379,9 @@ def run_rounds(a, W, model, steps: int, warmup: int, headline: bool):
     # of every layer, then norm/RoPE and the scatter into the cache); ctx_len
     # is put back after each call, so the same positions are rewritten.
     saved_len = cache.ctx_len.clone()
+    for _ in range(2):  # untimed: the first calls after another leg ran slow
+        model.ctx_kv_append(cache, ctx_new, cu_new, ws, status)
+        cache.ctx_len.copy_(saved_len)
     n_app = 10
     app_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(n_app)]

@@ -133,35 +133,45 @@ __global__ __launch_bounds__(256) void splitk_reduce_norm_kernel(const float* __
                                                                  float* __restrict__ x, int64_t xs,
                                                                  const bf16* gain, bf16* y, int nck,
                                                                  float eps) {
+  constexpr int ZG = 4;  // slices loaded together (every load of a group before its adds)
   __shared__ float sh[4];
   const int m = blockIdx.x;
   const int64_t MN = (int64_t)M * N;
-  // Every load of the row goes out before the first store (ks <= kMfmaMaxSplit).
   float4 v[VPT], r[VPT];
-  float4 q[VPT][kMfmaMaxSplit];
 #pragma unroll
   for (int u = 0; u < VPT; ++u) {
     const int k = 4 * (threadIdx.x + u * blockDim.x);
-    const float* pp = part + (int64_t)m * N + k;
-#pragma unroll
-    for (int z = 0; z < kMfmaMaxSplit; ++z)
-      q[u][z] = k < N && z < ks ? *reinterpret_cast<const float4*>(pp + z * MN)
-                                : make_float4(0.f, 0.f, 0.f, 0.f);
     r[u] = k < N ? *reinterpret_cast<const float4*>(x + (int64_t)m * xs + k)
                  : make_float4(0.f, 0.f, 0.f, 0.f);
+    v[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  // Slices in order, ZG at a time (ks <= kMfmaMaxSplit).
+  for (int z0 = 0; z0 < ks; z0 += ZG) {
+    float4 q[VPT][ZG];
+#pragma unroll
+    for (int u = 0; u < VPT; ++u) {
+      const int k = 4 * (threadIdx.x + u * blockDim.x);
+      const float* pp = part + (int64_t)m * N + k;
+#pragma unroll
+      for (int z = 0; z < ZG; ++z)
+        q[u][z] = k < N && z0 + z < ks ? *reinterpret_cast<const float4*>(pp + (z0 + z) * MN)
+                                        : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int u = 0; u < VPT; ++u)
+#pragma unroll
+      for (int z = 0; z < ZG; ++z) {
+        if (z0 + z < ks) {
+          v[u].x += q[u][z].x;
+          v[u].y += q[u][z].y;
+          v[u].z += q[u][z].z;
+          v[u].w += q[u][z].w;
+        }
+      }
   }
 #pragma unroll
   for (int u = 0; u < VPT; ++u) {
-    float4 acc = q[u][0];
-#pragma unroll
-    for (int z = 1; z < kMfmaMaxSplit; ++z) {
-      if (z < ks) {
-        acc.x += q[u][z].x;
-        acc.y += q[u][z].y;
-        acc.z += q[u][z].z;
-        acc.w += q[u][z].w;
-      }
-    }
+    float4 acc = v[u];
     acc.x += r[u].x;
     acc.y += r[u].y;
     acc.z += r[u].z;

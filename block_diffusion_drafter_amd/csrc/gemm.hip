@@ -68,7 +68,7 @@ void gemm_stream_kernel(GemmArgs p) {
   __shared__ float sq_part[SQ ? 1024 : 1];
   __shared__ float row_inv[SQ ? 16 * MT : 1];
 
-  gemm_snapshot(p, blockIdx.x == 0 && blockIdx.y == 0);
+  if constexpr (EPI == EPI_STORE_F32) gemm_snapshot(p, blockIdx.x == 0 && blockIdx.y == 0);
   const int lane = threadIdx.x & 63;
   // Wave-uniform values live in scalar registers: chunk indices derived from
   // them never need vector loads (or their waits) in the loop.

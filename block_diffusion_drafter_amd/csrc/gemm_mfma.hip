@@ -115,7 +115,7 @@ void gemm_mfma_kernel(GemmArgs p, int n_colblk, int n_rowblk) {
   const int xcd = id & 7, q = id >> 3;
   const int rb = q % n_rowblk;
   const int cb = (q / n_rowblk) * 8 + xcd;
-  gemm_snapshot(p, blockIdx.x == 0);
+  if constexpr (EPI == EPI_STORE_F32) gemm_snapshot(p, blockIdx.x == 0);
   if (cb >= n_colblk) return;
 
   const int lane = threadIdx.x & 63;
@@ -397,7 +397,7 @@ void gemm_pipe_kernel(GemmArgs p, int n_colblk, int n_rowblk) {
   const int xcd = id & 7, q = id >> 3;
   const int rb = q % n_rowblk;
   const int cb = (q / n_rowblk) * 8 + xcd;
-  gemm_snapshot(p, blockIdx.x == 0);
+  if constexpr (EPI == EPI_STORE_F32) gemm_snapshot(p, blockIdx.x == 0);
   if (cb >= n_colblk) return;
 
   const int lane = threadIdx.x & 63;
@@ -628,48 +628,66 @@ static int mfma_colblocks(int epi, int N, int BN) {
   return (N + cols - 1) / cols;
 }
 
-// Block shapes, largest first: 256x256 (8 waves of 128x64, pipelined),
-// 256x192 (8 waves of 64x96, pipelined), 128x128 (4 waves of 64x64), 128x96
-// (4 waves of 64x48). Bigger blocks read fewer operand bytes per flop;
-// smaller ones fill the 256 CUs at fewer rows or columns. `tflops` is each
-// shape's measured throughput per CU with every CU busy (MI355X, bf16, 256 -
-// 2048 rows); with fewer CUs busy the chip clocks higher, ~35% more per CU
-// when almost all are idle.
+// Block shapes: 256x256 (8 waves of 128x64, pipelined), 256x192 (8 waves of
+// 64x96, pipelined), 256x128 and 128x256 (8 waves of 64x64, pipelined),
+// 128x128 (4 waves of 64x64), 128x96 (4 waves of 64x48). Bigger blocks read
+// fewer operand bytes per flop; smaller ones fill the 256 CUs at fewer rows
+// or columns. Each shape is costed by what one workgroup takes on MI355X
+// with every CU busy (bf16, random data, weights streamed from HBM; timed at
+// 261-512 rows): `tflops` per CU once the ring is full, plus `fixed_us` per
+// workgroup for filling the ring, the epilogue and its stores (a 128x128
+// workgroup over K = 4096 on 256 CUs: 21 + 6.6 us). Fewer busy CUs clock
+// higher, ~35% more per CU when almost all are idle.
 struct MfmaShape {
   int bm, bn;
   bool pipe;
   double tflops;
+  double fixed_us;
 };
-static const MfmaShape kShapes[4] = {{256, 256, true, 5.0}, {256, 192, true, 4.75},
-                                     {128, 128, false, 3.15}, {128, 96, false, 2.75}};
+static const MfmaShape kShapes[6] = {{256, 256, true, 4.96, 6.8},  {256, 192, true, 4.84, 6.5},
+                                     {256, 128, true, 4.6, 6.1},   {128, 256, true, 4.75, 8.3},
+                                     {128, 128, false, 3.18, 6.6}, {128, 96, false, 3.45, 5.0}};
 
 // Whether a shape can take K slices of ks: fp32-store / residual epilogues
-// only (slices write fp32 partials that splitk_reduce_kernel sums in order);
-// the pipelined kernel needs an even number (>= 8) of k=32 stages per slice,
-// the 4-wave one >= 8 stages of k = 64.
+// only (slices write fp32 partials that a reduce kernel sums in order). The
+// pipelined kernel needs an even number of k = 32 stages per slice, and at
+// least 32 of them (shorter slices spend more on filling the ring and
+// storing partials than they gain: 256x256 blocks over 16 stages ran no faster
+// than 128x128 ones over 32); the 4-wave one >= 8 stages of k = 64.
 static bool ksplit_ok(const MfmaShape& sh, int epi, int K, int ks) {
   if (ks == 1) return true;
   if (epi != EPI_STORE_F32 && epi != EPI_RESID) return false;
-  if (sh.pipe) return (K / 32) % (2 * ks) == 0 && K / 32 / ks >= 8;
+  if (sh.pipe) return (K / 32) % (2 * ks) == 0 && K / 32 / ks >= 32;
   return (K / 64) % ks == 0 && K / 64 / ks >= 8;
 }
 
 // Estimated time (us) of one launch: rounds of up to 256 workgroups, each
 // block of bm x bn x K/ks at the shape's rate per CU (raised when the round
-// leaves CUs idle), plus the fp32 output traffic at ~5 TB/s: the residual's
-// read-modify-write (latency-bound at the end of a block: counted 3x), or
-// with K slices the partials (written, then read by the reduce) and the
-// reduce's output, plus its launch.
+// leaves CUs idle) plus its fixed cost, plus, with K slices, the store of its
+// fp32 partial block at ~60 GB/s per CU; 256-row blocks that are more than a
+// quarter padding ran ~15% slower than their flops say (136 rows: 56.6 us
+// against 49.5 for two 128-row blocks); then the output traffic at ~5 TB/s:
+// without slices the residual's read-modify-write (latency-bound at the end
+// of a block: counted 3x) or the fp32 store; with slices the reduce kernel,
+// whose cost per 2^21 output elements was measured as 8.0 + 0.95 ks us with
+// the residual add and RMSNorm (2, 4, 8 slices: 9.9, 11.7, 15.5 us) and
+// 1.0 + 1.6 ks us for a plain sum (4.7, 9.9, 16.6 us at 1.5 x that size;
+// rounded up: the slices' partial stores also slow their own GEMM).
 static double mfma_time_us(const MfmaShape& sh, int epi, int M, int N, int K, int ks) {
   const long long wgs = (long long)((M + sh.bm - 1) / sh.bm) * mfma_colblocks(epi, N, sh.bn) * ks;
   const double block_mflop = 2.0 * sh.bm * sh.bn * ((double)K / ks) * 1e-6;
+  const int rows = ((M + sh.bm - 1) / sh.bm) * sh.bm;
+  const double pad_penalty = (sh.bm == 256 && 4 * (rows - M) > rows) ? 1.15 : 1.0;
+  const double part_us = ks > 1 ? (double)sh.bm * sh.bn * 4 / 60e3 : 0.0;
   double t = 0;
   for (long long left = wgs; left > 0; left -= 256) {
     const double busy = (double)(left < 256 ? left : 256);
-    t += block_mflop / (sh.tflops * (1.0 + 0.35 * (1.0 - busy / 256.0)));
+    t += pad_penalty * block_mflop / (sh.tflops * (1.0 + 0.35 * (1.0 - busy / 256.0))) +
+         sh.fixed_us + part_us;
   }
   const double out_mb = (double)M * N * 4 * 1e-6;
-  if (ks > 1) t += (2.0 * ks + (epi == EPI_RESID ? 2.0 : 1.0)) * out_mb / 5.0 + 2.0;
+  const double units = (double)M * N / (double)(1 << 21);
+  if (ks > 1) t += (epi == EPI_RESID ? 8.0 + 0.95 * ks : 1.0 + 1.6 * ks) * units;
   else t += (epi == EPI_RESID ? 3.0 : epi == EPI_STORE_F32 ? 1.0 : 0.0) * out_mb / 5.0;
   return t;
 }
@@ -679,11 +697,11 @@ struct MfmaPlan {
 };
 // The shape and K split with the least estimated time. SwiGLU needs an even
 // number of column tiles per wave (not 128x96); the LM-head argmax keeps
-// square blocks. Ties go to the larger block and fewer slices.
+// square blocks. Ties go to the earlier shape and fewer slices.
 static MfmaPlan mfma_plan(int epi, int M, int N, int K) {
   MfmaPlan best{0, 1};
   double best_t = 1e300;
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < 6; ++i) {
     const MfmaShape& sh = kShapes[i];
     if (epi == EPI_SWIGLU && sh.bn == 96) continue;
     if (epi == EPI_ARGMAX && sh.bm != sh.bn) continue;
@@ -805,6 +823,7 @@ static hipError_t launch_mfma_epi(const GemmArgs& a, hipStream_t st) {
   // Pipelined shapes: 4 ring slots of k = 32 for the LM head (128 KB; its
   // weights stream from HBM once), 3 for the others (96 / 84 KB); the 4-wave
   // shapes keep stages of k = 64 in 4 slots (32 / 28 KB each).
+  // The 64x64-wave pipelined shapes keep 4 ring slots of k = 32 (96 KB).
   switch (mfma_plan(EPI, a.M, a.N, a.K).shape) {
     case 0:
       if constexpr (EPI == EPI_ARGMAX) return launch_pipe_t<256, 256, 2, 4, 4, EPI>(a, st);
@@ -812,7 +831,13 @@ static hipError_t launch_mfma_epi(const GemmArgs& a, hipStream_t st) {
     case 1:
       if constexpr (EPI == EPI_ARGMAX) return hipErrorInvalidValue;
       else return launch_pipe_t<256, 192, 4, 2, 3, EPI>(a, st);
-    case 2: return launch_mfma_t<128, 128, 2, 2, 2, 4, EPI>(a, st);
+    case 2:
+      if constexpr (EPI == EPI_ARGMAX) return hipErrorInvalidValue;
+      else return launch_pipe_t<256, 128, 4, 2, 4, EPI>(a, st);
+    case 3:
+      if constexpr (EPI == EPI_ARGMAX) return hipErrorInvalidValue;
+      else return launch_pipe_t<128, 256, 2, 4, 4, EPI>(a, st);
+    case 4: return launch_mfma_t<128, 128, 2, 2, 2, 4, EPI>(a, st);
     default:
       if constexpr (EPI == EPI_ARGMAX || EPI == EPI_SWIGLU) return hipErrorInvalidValue;
       else return launch_mfma_t<128, 96, 2, 2, 2, 4, EPI>(a, st);

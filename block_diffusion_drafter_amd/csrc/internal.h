@@ -74,10 +74,10 @@ struct GemmArgs {
   float* sq_out;
   const float* sq_in;
   int sq_d;
-  // Workgroup 0 of the projection copies snap_n int32 values from snap_src to
-  // snap_dst before anything else (a context-K/V append snapshots ctx_len
-  // this way, so its scatter kernel reads positions from the copy and may
-  // update ctx_len itself). Unused: snap_dst == nullptr.
+  // EPI_STORE_F32 only: workgroup 0 of the projection copies snap_n int32
+  // values from snap_src to snap_dst before anything else (a context-K/V
+  // append snapshots ctx_len this way, so its scatter kernel reads positions
+  // from the copy and may update ctx_len itself). Unused: snap_dst == nullptr.
   const int32_t* snap_src;
   int32_t* snap_dst;
   int snap_n;
@@ -119,7 +119,7 @@ hipError_t launch_gemm_mfma(int epi, const GemmArgs& a, hipStream_t st);
 // outputs of at most kMfmaSplitMaxElems elements (larger ones fill the chip
 // without), so the partials of any row count up to M never exceed
 // kMfmaMaxSplit * min(M * N, kMfmaSplitMaxElems) floats.
-constexpr int kMfmaMaxSplit = 4;
+constexpr int kMfmaMaxSplit = 8;
 constexpr int64_t kMfmaSplitMaxElems = (int64_t)1 << 22;
 int mfma_gemm_colblocks(int epi, int M, int N, int K);
 // K slices the MFMA kernel splits a projection into (1 = no split); the

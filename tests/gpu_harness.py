@@ -11,11 +11,13 @@ Tolerances (written here once, used by every parity test):
     along its leading axes (each sequence of a batch, each KV head of a cache
     slice), so an error confined to one short sequence or one head cannot hide
     under another's larger values;
-  * draft token ids: the GPU's token must be one of the oracle's near-top
-    tokens, i.e. its oracle logit lies within 0.05 of the oracle's top-1 logit.
-    Where the oracle's top-1/top-2 margin exceeds 0.05 that leaves only the
-    oracle's own argmax (bit-exact); at a near-tie any of the tied tokens is a
-    correct draft and the GPU's pick is checked to be one of them;
+  * draft token ids: bit-exact wherever the oracle's top-1/top-2 margin
+    exceeds 0.05. At the other slots (near-ties) several tokens are correct
+    drafts, and the GPU's pick must be one of them: the argmax of the GPU's own
+    logits, whose oracle logit lies within max(0.05, 2 eps) of the oracle's
+    top-1, eps being the row's measured max |gpu - oracle| logit error (a
+    token beats the top-1 on the GPU only if the two differ by at most the sum
+    of their errors); without GPU logits the bound is 0.05;
   * accept lengths and bonus tokens: the GPU's equal the prefix rule applied
     to its own drafts (every sequence), and equal the oracle's wherever the
     GPU's drafts agree with the oracle's on every position the prefix test
@@ -157,11 +159,13 @@ def feats_to_device(feats: List[I.HostTensor]) -> List[torch.Tensor]:
     return [torch_io.to_device(f) for f in feats]
 
 
-def check_drafts(res: O.ForwardResult, drafts_gpu: np.ndarray, what: str) -> int:
-    """Every slot: the GPU's token is a valid draft, i.e. its oracle logit is
-    within MARGIN of the oracle's top-1 logit. On confident slots (oracle
-    top-1/top-2 margin > MARGIN) only the oracle's argmax qualifies, so those
-    are bit-exact. Returns the number of near-tie slots."""
+def check_drafts(res: O.ForwardResult, drafts_gpu: np.ndarray, what: str,
+                 logits_gpu=None) -> int:
+    """Every slot: bit-exact where the oracle's top-1/top-2 margin exceeds
+    MARGIN; elsewhere the GPU's token must be a valid near-tie pick (see the
+    module docstring). logits_gpu: the GPU's logits of the same rows
+    ([b, B-1, V], tensor or array) when the call produced them. Returns the
+    number of near-tie slots."""
     drafts_gpu = np.asarray(drafts_gpu, dtype=np.int64)
     V = res.logits.shape[-1]
     assert ((drafts_gpu >= 0) & (drafts_gpu < V)).all(), f"{what}: token ids out of range"
@@ -171,15 +175,29 @@ def check_drafts(res: O.ForwardResult, drafts_gpu: np.ndarray, what: str) -> int
     top1 = np.take_along_axis(res.logits, res.drafts[..., None], -1)[..., 0]
     mine = np.take_along_axis(res.logits, drafts_gpu[..., None], -1)[..., 0]
     gap = top1 - mine
-    invalid = gap > MARGIN
+    bound = np.full(gap.shape, MARGIN)
+    widened = 0
+    if logits_gpu is not None:
+        lg = logits_gpu.detach().float().cpu().numpy().astype(np.float64) \
+            if isinstance(logits_gpu, torch.Tensor) else np.asarray(logits_gpu, dtype=np.float64)
+        assert lg.shape == res.logits.shape, (lg.shape, res.logits.shape)
+        # the GPU's token is the argmax of its own logits (lowest id on ties)
+        own = np.argmax(lg, axis=-1)
+        assert (own == drafts_gpu).all(), f"{what}: drafts are not the argmax of the GPU's logits"
+        eps = np.max(np.abs(lg - res.logits), axis=-1)
+        bound = np.maximum(MARGIN, 2.0 * eps)
+        widened = int(((gap > MARGIN) & (gap <= bound)).sum())
+    invalid = gap > bound
     assert not invalid.any(), (f"{what}: {int(invalid.sum())} near-tie slots hold a token whose "
-                               f"oracle logit is more than {MARGIN} below the top-1: "
-                               f"{np.argwhere(invalid)[:5].tolist()}, gaps {gap[invalid][:5]}")
+                               f"oracle logit is further below the top-1 than the bound: "
+                               f"{np.argwhere(invalid)[:5].tolist()}, gaps {gap[invalid][:5]}, "
+                               f"bounds {bound[invalid][:5]}")
     excl = int((~ok).sum())
     differ = int(((drafts_gpu != res.drafts) & ~ok).sum())
     log(f"  {what}: drafts bit-exact on {int(ok.sum())}/{ok.size} confident slots; "
-        f"{excl} near-tie slots (margin <= {MARGIN}) all hold a near-top token "
-        f"({differ} differ from the oracle's argmax, 0 invalid)")
+        f"{excl} near-tie slots (margin <= {MARGIN}) all hold a valid pick "
+        f"({differ} differ from the oracle's argmax, {widened} of them beyond {MARGIN} but "
+        f"within twice the row's logit error; 0 invalid)")
     return excl
 
 

@@ -120,7 +120,7 @@ def run_flow(cfg, ctx_lens, tag, seed=0, cap_extra=0, split_append=1, degenerate
     drafts = drafts_g.cpu().numpy()[:, :m].astype(np.int64)
     if m:
         assert_close(cfg, to_np(logits_g), res.logits, "logits", group_axes=1)
-        excl = check_drafts(res, drafts, "drafts")
+        excl = check_drafts(res, drafts, "drafts", logits_g)
         if not degenerate:
             assert excl <= max(2, 0.5 * res.drafts.size), "too many low-margin slots to be a test"
     check_accept(res, targets, acc_g.cpu().numpy(), bon_g.cpu().numpy(), drafts, "accept")

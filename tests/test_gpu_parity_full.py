@@ -75,7 +75,7 @@ def compare_forward(cfg, res, drafts, logits, hidden, acc, bon, targets, what):
                      group_axes=1)
     if logits is not None:
         assert_close(cfg, to_np(logits), res.logits, f"{what}: logits", group_axes=1)
-    check_drafts(res, drafts, f"{what}: drafts")
+    check_drafts(res, drafts, f"{what}: drafts", logits)
     return check_accept(res, targets, acc, bon, drafts, f"{what}: accept")
 
 
@@ -199,8 +199,7 @@ def test_gpu_llama31_8b_shaped_batch16_64_rounds():
         a0 = I.planted_accept_lengths(1, m, seed_r, "l16")
         tgt = I.uniform_tokens(cfg, (b, Bk), seed_r, "l16.targets")
         tgt[:1] = I.plant_targets(res.drafts[:1], a0, cfg.vocab, seed_r, "l16")
-        drafts, logits, hidden, acc, bon = run_forward(M, cfg, cache, anchors, tgt, ws,
-                                                       want_logits=full)
+        drafts, logits, hidden, acc, bon = run_forward(M, cfg, cache, anchors, tgt, ws)
         if full:
             # every sequence: hidden after every layer, logits, drafts, accept
             checked = compare_forward(cfg, res, drafts, logits, hidden, acc, bon, tgt,
@@ -214,7 +213,7 @@ def test_gpu_llama31_8b_shaped_batch16_64_rounds():
             for l in (0, cfg.n_layers - 1):
                 assert_close(cfg, to_np(hidden[0, l]), res0.hidden[0, l],
                              f"round {r}: seq 0 hidden after layer {l}")
-            check_drafts(res0, drafts[:1], f"round {r}: seq 0 drafts")
+            check_drafts(res0, drafts[:1], f"round {r}: seq 0 drafts", logits[:1])
             checked0 += check_accept(res0, tgt[:1], acc[:1], bon[:1], drafts[:1],
                                      f"round {r}: seq 0 accept")
             # every other sequence: the prefix rule on its own drafts

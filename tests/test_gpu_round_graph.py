@@ -187,7 +187,7 @@ def test_gpu_round_graph_follows_the_oracle_trajectory():
     torch.cuda.synchronize()
     for r in range(rounds):
         drafts = buf.drafts.cpu().numpy().astype(np.int64)
-        check_drafts(res, drafts, f"round {r}: drafts")
+        check_drafts(res, drafts, f"round {r}: drafts", buf.logits)
         assert_close(cfg, to_np(buf.logits), res.logits, f"round {r}: logits", group_axes=1)
         # the target pass of this block: planted accept lengths against the
         # oracle's drafts, fresh features at every block position
@@ -208,7 +208,7 @@ def test_gpu_round_graph_follows_the_oracle_trajectory():
         assert cache.ctx_len.cpu().tolist() == [c.ctx_len for c in caches], f"round {r}: ctx_len"
         log(f"  round {r}: accept {a_o.tolist()}, ctx {[c.ctx_len for c in caches]}")
     drafts = buf.drafts.cpu().numpy().astype(np.int64)
-    check_drafts(res, drafts, f"after {rounds} rounds: drafts")
+    check_drafts(res, drafts, f"after {rounds} rounds: drafts", buf.logits)
     compare_caches(cfg, cache, caches, f"after {rounds} rounds")
     g.close()
 
