@@ -205,3 +205,13 @@ def test_gpu_capacity_overflow_is_flagged_and_clamped():
                         drafts, ws, dev_status=status)
     torch.cuda.synchronize()
     assert status.item() == B.DEV_TOKEN
+
+
+def test_gpu_small_bf16_merged_segments_groups_and_head_dim64():
+    # batch >= 8: sequences that span several workgroups' key ranges are
+    # merged by the last workgroup to finish (no combine launch); GQA groups
+    # 8, 1 and 4, and head_dim 64, with ragged contexts (empty, short, long)
+    ctx = [700, 33, 0, 90, 5, 300, 12, 640, 128]
+    run_flow(SMALL_BF16.with_(n_heads=16, n_kv_heads=2), ctx, "small-g8-b9")
+    run_flow(SMALL_BF16.with_(n_kv_heads=8), ctx[:8], "small-mha-b8")
+    run_flow(SMALL_BF16.with_(head_dim=64, n_heads=8, n_kv_heads=2), ctx + [47, 2000], "small-hd64-b11")
