@@ -457,7 +457,7 @@ GemmPlan plan_gemm(int dtype, int epi, int M, int N, int K, int a_seg_k) {
 }
 
 int gemm_amax_cols(int dtype, int M, int N, int K) {
-  if (gemm_uses_mfma(dtype, M, K, true, EPI_ARGMAX)) return mfma_gemm_colblocks(EPI_ARGMAX, M, N, K);
+  if (gemm_uses_mfma(dtype, M, K, true, EPI_ARGMAX)) return mfma_argmax_keys(M, N, K);
   return plan_gemm(dtype, EPI_ARGMAX, M, N, K, 0).grid_x;
 }
 

@@ -292,8 +292,9 @@ void gemm_mfma_kernel(GemmArgs p, int n_colblk, int n_rowblk) {
         for (int j = 0; j < TN; ++j) {
           const int n = (tile_n0 + wn * TN + j) * 16 + r;
           if (n < p.N) {
-            if (p.logits && m < p.M) p.logits[(int64_t)m * p.logits_stride + n] = acc[i][j][e];
-            const unsigned long long k = argmax_key(acc[i][j][e], (unsigned)n);
+            if (p.logits && m < p.M)
+              p.logits[(int64_t)m * p.logits_stride + p.col0 + n] = acc[i][j][e];
+            const unsigned long long k = argmax_key(acc[i][j][e], (unsigned)(p.col0 + n));
             key = k > key ? k : key;
           }
         }
@@ -315,7 +316,7 @@ void gemm_mfma_kernel(GemmArgs p, int n_colblk, int n_rowblk) {
           const unsigned long long k = kred[row * WGN + w];
           best = k > best ? k : best;
         }
-        p.amax[(int64_t)m * p.amax_stride + cb] = best;
+        p.amax[(int64_t)m * p.amax_stride + p.amax_col0 + cb] = best;
       }
     }
   } else if constexpr (SW) {
@@ -558,8 +559,9 @@ void gemm_pipe_kernel(GemmArgs p, int n_colblk, int n_rowblk) {
         for (int j = 0; j < TN; ++j) {
           const int n = (tile_n0 + wn * TN + j) * 16 + r;
           if (n < p.N) {
-            if (p.logits && m < p.M) p.logits[(int64_t)m * p.logits_stride + n] = acc[i][j][e];
-            const unsigned long long k = argmax_key(acc[i][j][e], (unsigned)n);
+            if (p.logits && m < p.M)
+              p.logits[(int64_t)m * p.logits_stride + p.col0 + n] = acc[i][j][e];
+            const unsigned long long k = argmax_key(acc[i][j][e], (unsigned)(p.col0 + n));
             key = k > key ? k : key;
           }
         }
@@ -581,7 +583,7 @@ void gemm_pipe_kernel(GemmArgs p, int n_colblk, int n_rowblk) {
           const unsigned long long k = kred[row * WGN + w];
           best = k > best ? k : best;
         }
-        p.amax[(int64_t)m * p.amax_stride + cb] = best;
+        p.amax[(int64_t)m * p.amax_stride + p.amax_col0 + cb] = best;
       }
     }
   } else if constexpr (SW) {
@@ -723,6 +725,34 @@ int mfma_gemm_colblocks(int epi, int M, int N, int K) {
   return mfma_colblocks(epi, N, kShapes[mfma_plan(epi, M, N, K).shape].bn);
 }
 
+// The LM head on 256x256 blocks: when its last round of 256 workgroups
+// would be less than three quarters full (batch 32: 1188 workgroups, 4.64
+// rounds), the columns of the full rounds stay on 256x256 blocks and the rest
+// runs as a second launch of 256x192 blocks that fits one round (218
+// workgroups at three quarters of the work each, instead of 164 full ones):
+// the last round then takes ~0.75 of a round's time. Returns the column
+// blocks of the first launch (0: no split) and, in *tail, of the second.
+static int lm_head_split(int M, int N, int K, int* tail) {
+  *tail = 0;
+  const MfmaPlan pl = mfma_plan(EPI_ARGMAX, M, N, K);
+  if (pl.shape != 0) return 0;
+  const int rb = (M + 255) / 256, cb = mfma_colblocks(EPI_ARGMAX, N, 256);
+  const int wgs = rb * cb, rounds = wgs / 256, last = wgs - rounds * 256;
+  if (rounds < 1 || last == 0 || 4 * last >= 3 * 256) return 0;
+  const int cb_main = rounds * 256 / rb;
+  const int n_tail = N - cb_main * 256;
+  const int cb_tail = mfma_colblocks(EPI_ARGMAX, n_tail, 192);
+  if (n_tail <= 0 || cb_tail * rb > 256) return 0;
+  *tail = cb_tail;
+  return cb_main;
+}
+
+int mfma_argmax_keys(int M, int N, int K) {
+  int tail = 0;
+  const int main = lm_head_split(M, N, K, &tail);
+  return main > 0 ? main + tail : mfma_gemm_colblocks(EPI_ARGMAX, M, N, K);
+}
+
 int mfma_gemm_ksplit(int epi, int M, int N, int K) { return mfma_plan(epi, M, N, K).ksplit; }
 
 // Sum of the K-slice partials in slice order, then the projection's epilogue:
@@ -823,6 +853,21 @@ static hipError_t launch_mfma_epi(const GemmArgs& a, hipStream_t st) {
   // Pipelined shapes: 4 ring slots of k = 32 for the LM head (128 KB; its
   // weights stream from HBM once), 3 for the others (96 / 84 KB); the 4-wave
   // shapes keep stages of k = 64 in 4 slots (32 / 28 KB each).
+  if constexpr (EPI == EPI_ARGMAX) {
+    int cb_tail = 0;
+    const int cb_main = lm_head_split(a.M, a.N, a.K, &cb_tail);
+    if (cb_main > 0) {
+      GemmArgs m = a, t = a;
+      m.N = cb_main * 256;
+      hipError_t e = launch_pipe_t<256, 256, 2, 4, 4, EPI>(m, st);
+      if (e != hipSuccess) return e;
+      t.N = a.N - m.N;
+      t.w = reinterpret_cast<const bf16*>(a.w) + (int64_t)(m.N / 16) * ((a.K + kKC - 1) / kKC) * 4 * kFRAG;
+      t.col0 = a.col0 + m.N;
+      t.amax_col0 = a.amax_col0 + cb_main;
+      return launch_pipe_t<256, 192, 4, 2, 4, EPI>(t, st);
+    }
+  }
   // The 64x64-wave pipelined shapes keep 4 ring slots of k = 32 (96 KB).
   switch (mfma_plan(EPI, a.M, a.N, a.K).shape) {
     case 0:

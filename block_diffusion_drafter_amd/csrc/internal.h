@@ -51,6 +51,9 @@ struct GemmArgs {
   int64_t amax_stride;
   float* logits;                  // EPI_ARGMAX, optional
   int64_t logits_stride;
+  int col0;                       // EPI_ARGMAX: global column of this launch's column 0 (key
+                                  // indices and logits columns are offset by it)
+  int amax_col0;                  // EPI_ARGMAX: first key column of this launch in amax rows
   // Split-K scratch of the MFMA kernel (EPI_STORE_F32 / EPI_RESID only):
   // fp32 [ksplit][M][N], part_elems floats available; nullptr: never split.
   float* part;
@@ -122,6 +125,9 @@ hipError_t launch_gemm_mfma(int epi, const GemmArgs& a, hipStream_t st);
 constexpr int kMfmaMaxSplit = 8;
 constexpr int64_t kMfmaSplitMaxElems = (int64_t)1 << 22;
 int mfma_gemm_colblocks(int epi, int M, int N, int K);
+// Keys per row the MFMA LM-head projection writes (its column blocks, over
+// both launches when its last columns run as a second launch).
+int mfma_argmax_keys(int M, int N, int K);
 // K slices the MFMA kernel splits a projection into (1 = no split); the
 // partial buffer it then needs is ksplit * M * N floats.
 int mfma_gemm_ksplit(int epi, int M, int N, int K);
