@@ -465,8 +465,8 @@ __device__ __forceinline__ void attn_wait_barrier() {
 // only when a block's max exceeds it by more than 2^8 (probabilities stay
 // <= 256, exact for the final normalisation), so the output accumulators are
 // rarely touched outside the MFMAs.
-template <int HD, int G, int NSB = 4>
-__global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(2, 2)))
+template <int HD, int G, int NSB = 4, int HPG = 1>
+__global__ __launch_bounds__(64 * G * HPG) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_partial_lds_kernel(AttnArgs p) {
   using T = bf16;
   using KB = KVBlock<T, HD>;
@@ -475,13 +475,15 @@ void attn_partial_lds_kernel(AttnArgs p) {
   constexpr int IPW = NI / G;       // fragments each wave copies per block
   static_assert(NI % G == 0, "block fragments must split evenly over the group");
   static_assert(NSB >= 3, "a slot being read, one arriving, one being filled");
-  __shared__ u32x4 ring[NSB][NI][64];
+  __shared__ u32x4 ring_all[HPG][NSB][NI][64];
 
   const int lane = threadIdx.x & 63;
-  const int j = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int j = wv % G, hg = wv / G;  // wave j of the workgroup's head group hg
   const int r = lane & 15, grp = lane >> 4;
-  const int w = blockIdx.x, g = blockIdx.y;
+  const int w = blockIdx.x, g = blockIdx.y * HPG + hg;
   const int h = g * G + j;
+  auto& ring = ring_all[hg];
   extern __shared__ int pre[];
   seq_block_prefix(p, pre);
   const KeySplit ks = key_split(p, pre);
@@ -701,7 +703,16 @@ static hipError_t launch_hd(const AttnArgs& a, hipStream_t st) {
     switch (G) {
       case 1: hipLaunchKernelGGL((attn_partial_lds_kernel<HD, 1>), grid, dim3(64), pre_bytes, st, a); break;
       case 2: hipLaunchKernelGGL((attn_partial_lds_kernel<HD, 2>), grid, dim3(128), pre_bytes, st, a); break;
-      case 4: hipLaunchKernelGGL((attn_partial_lds_kernel<HD, 4>), grid, dim3(256), pre_bytes, st, a); break;
+      case 4:
+        // Two KV heads per workgroup (one per group of four waves): the
+        // launch is one workgroup per CU, all dispatched at once, instead of
+        // two per CU of which the later-dispatched one finishes last.
+        if (a.n_kv_heads % 2 == 0)
+          hipLaunchKernelGGL((attn_partial_lds_kernel<HD, 4, 4, 2>),
+                             dim3(a.wg_per_head, a.n_kv_heads / 2, 1), dim3(512), pre_bytes, st, a);
+        else
+          hipLaunchKernelGGL((attn_partial_lds_kernel<HD, 4>), grid, dim3(256), pre_bytes, st, a);
+        break;
       case 8: hipLaunchKernelGGL((attn_partial_lds_kernel<HD, 8>), grid, dim3(512), pre_bytes, st, a); break;
       default: return hipErrorInvalidValue;
     }
