@@ -861,9 +861,25 @@ void packed_attn_tile_kernel(PackedAttnArgs p, int tiles_per_seq) {
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 15, grp = lane >> 4;
-  const int g = blockIdx.y, Hq = p.n_heads, Hkv = p.n_kv_heads, B = p.block;
+  const int Hq = p.n_heads, Hkv = p.n_kv_heads, B = p.block;
+  // Workgroup -> (sequence, KV head) pair and tile. The dispatcher deals
+  // workgroups round-robin to the 8 XCDs (each with its own L2); when the
+  // pairs split evenly over them, XCD x takes pairs x*n/8 .. (x+1)*n/8 - 1,
+  // their tiles in order, so the context prefix the tiles of one pair share is
+  // fetched into one L2 instead of all eight.
+  const int n_pairs = (p.n_blk / p.blocks_per_seq) * Hkv;
+  int pair, tile;
+  if (n_pairs % 8 == 0) {
+    const int xcd = blockIdx.x & 7, q = blockIdx.x >> 3;
+    pair = xcd * (n_pairs / 8) + q / tiles_per_seq;
+    tile = q % tiles_per_seq;
+  } else {
+    pair = blockIdx.x / tiles_per_seq;
+    tile = blockIdx.x % tiles_per_seq;
+  }
+  const int g = pair % Hkv;
   const int h = g * G + w;
-  const int s = blockIdx.x / tiles_per_seq, j0 = (blockIdx.x % tiles_per_seq) * TB;
+  const int s = pair / Hkv, j0 = tile * TB;
   const int nt = min(TB, p.blocks_per_seq - j0);
   const int blk0 = s * p.blocks_per_seq + j0;
   const int lim = min(max(p.ctx_len[s], 0), p.cap);
@@ -1005,7 +1021,7 @@ template <int HD, int TB>
 static hipError_t launch_packed_tile(const PackedAttnArgs& a, hipStream_t st) {
   const int G = a.n_heads / a.n_kv_heads;
   const int tiles = (a.blocks_per_seq + TB - 1) / TB;
-  const dim3 grid((a.n_blk / a.blocks_per_seq) * tiles, a.n_kv_heads);
+  const dim3 grid((a.n_blk / a.blocks_per_seq) * tiles * a.n_kv_heads);
   switch (G) {
     case 1: hipLaunchKernelGGL((packed_attn_tile_kernel<HD, 1, TB>), grid, dim3(64), 0, st, a, tiles); break;
     case 2: hipLaunchKernelGGL((packed_attn_tile_kernel<HD, 2, TB>), grid, dim3(128), 0, st, a, tiles); break;
