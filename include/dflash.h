@@ -36,6 +36,17 @@
  *  - A handle is immutable after dflash_create; concurrent calls with one
  *    handle on different streams are safe when their workspaces and output
  *    buffers differ.
+ *
+ * Departures from a plain row-major interface (both for the matrix cores'
+ * operand order; see dflash_kv_cache and dflash_pack_weights)
+ * ---------------------------------------------------------------------
+ *  - The V cache is not [capacity][head_dim] per (layer, sequence, KV head)
+ *    but [capacity/32][head_dim][32]: positions in blocks of 32, channel-major
+ *    inside a block. The K cache is plain [capacity][head_dim].
+ *  - The projections are not read from the caller's row-major matrices in
+ *    place: dflash_pack_weights writes a tiled copy once (3.42 GB for a
+ *    Qwen3-8B-shaped drafter) into a caller buffer, and every call reads that.
+ *    The embedding table and the norm gains are read in place.
  */
 #ifndef DFLASH_H
 #define DFLASH_H
