@@ -181,7 +181,20 @@ __global__ __launch_bounds__(kThreads) void verify_stats_kernel(const float* dra
                                  : draft_logits + (int64_t)(r - batch * B) * V;
   Lse lse;
   const int end = min(V, (split + 1) * kSplit);
-  for (int v = split * kSplit + threadIdx.x; v < end; v += kThreads) lse.add(l[v] * inv_t);
+  if ((V & 3) == 0) {
+    // Rows start 16-byte aligned (row length a multiple of 4 floats, the
+    // buffers 16-byte aligned): one 16-byte load per thread and step.
+    const float4* l4 = reinterpret_cast<const float4*>(l);
+    for (int v = split * kSplit + 4 * threadIdx.x; v < end; v += 4 * kThreads) {
+      const float4 x = l4[v >> 2];
+      lse.add(x.x * inv_t);
+      lse.add(x.y * inv_t);
+      lse.add(x.z * inv_t);
+      lse.add(x.w * inv_t);
+    }
+  } else {
+    for (int v = split * kSplit + threadIdx.x; v < end; v += kThreads) lse.add(l[v] * inv_t);
+  }
   block_lse(lse, shm, shs);
   if (threadIdx.x == 0) part[(int64_t)r * nsplit + split] = SplitStat{0ull, lse.m, lse.s};
 }
