@@ -26,13 +26,29 @@ namespace {
 constexpr int kSplit = 8192;  // logits per workgroup
 constexpr int kThreads = 256;
 
+// 128-bit product of two 64-bit words from four 32 x 32 -> 64-bit
+// multiply-adds (schoolbook, with the middle partial sums folded into the
+// multiply-adds so that none overflows 64 bits):
+//   p10 = a1 b0 + hi(a0 b0), p01 = a0 b1 + lo(p10),
+//   lo = lo(a0 b0) | lo(p01) << 32, hi = a1 b1 + hi(p10) + hi(p01).
+__device__ __forceinline__ void mul_128(uint64_t a, uint64_t b, uint64_t& hi, uint64_t& lo) {
+  const uint32_t a0 = (uint32_t)a, a1 = (uint32_t)(a >> 32);
+  const uint32_t b0 = (uint32_t)b, b1 = (uint32_t)(b >> 32);
+  const uint64_t p00 = (uint64_t)a0 * b0;
+  const uint64_t p10 = (uint64_t)a1 * b0 + (p00 >> 32);
+  const uint64_t p01 = (uint64_t)a0 * b1 + (uint32_t)p10;
+  hi = (uint64_t)a1 * b1 + (p10 >> 32) + (p01 >> 32);
+  lo = (p01 << 32) | (uint32_t)p00;
+}
+
 __device__ __forceinline__ void philox4x64(uint64_t c[4], uint64_t k0, uint64_t k1) {
   const uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
   const uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
 #pragma unroll
   for (int r = 0; r < 10; ++r) {
-    const uint64_t hi0 = __umul64hi(M0, c[0]), lo0 = M0 * c[0];
-    const uint64_t hi1 = __umul64hi(M1, c[2]), lo1 = M1 * c[2];
+    uint64_t hi0, lo0, hi1, lo1;
+    mul_128(M0, c[0], hi0, lo0);
+    mul_128(M1, c[2], hi1, lo1);
     const uint64_t n0 = hi1 ^ c[1] ^ k0, n2 = hi0 ^ c[3] ^ k1;
     c[0] = n0;
     c[1] = lo1;
