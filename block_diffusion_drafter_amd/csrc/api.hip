@@ -471,8 +471,12 @@ int32_t dflash_ctx_project(const dflash_handle* h, const void* const* feats,
   }
   g.out = u;
   g.out_stride = c.hidden;
+  // Split over K on the MFMA path: the slice reduce writes the normalised
+  // rows straight to ctx_out (no fp32 rows, no separate norm pass).
+  const bool fused = gemm_fuses_norm(c.dtype, g, EPI_STORE_F32);
+  if (fused) set_norm(g, h->w.fc_norm, ctx_out, 0, c.rms_eps);
   int32_t rc = run_gemm(c.dtype, EPI_STORE_F32, g, st);
-  if (rc) return rc;
+  if (rc || fused) return rc;
   prof_begin(DFLASH_K_RMSNORM, 0, 0, st);
   hipError_t e = launch_rmsnorm(c.dtype, u, c.hidden, h->w.fc_norm, ctx_out, c.hidden, 0, n_tok,
                                 c.hidden, c.rms_eps, n_tok, 0, 0, st);

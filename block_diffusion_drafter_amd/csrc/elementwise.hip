@@ -123,11 +123,15 @@ hipError_t launch_rmsnorm(int dtype, const float* x, int64_t x_stride, const voi
   return hipGetLastError();
 }
 
-// End of a residual projection split over K: x[m] += sum of the ks fp32
-// partials of row m (slice order, then the residual, as splitk_reduce_kernel
-// sums), and the RMSNorm of the updated row into y (tiled, nck chunks per
-// row): the next projection's normalised input, without a second pass over x.
-template <int VPT>
+// End of a projection split over K, with the RMSNorm of its rows fused.
+// RES (a residual projection): x[m] += sum of the ks fp32 partials of row m
+// (slice order, then the residual, as splitk_reduce_kernel sums), and the
+// RMSNorm of the updated row into y (tiled, nck chunks per row): the next
+// projection's normalised input, without a second pass over x. !RES (a store
+// projection whose output is only consumed normalised, the fusion): y[m] =
+// RMSNorm(sum of the partials), row-major (row stride N) when nck is 0; x is
+// neither read nor written.
+template <int VPT, bool RES>
 __global__ __launch_bounds__(256) void splitk_reduce_norm_kernel(const float* __restrict__ part,
                                                                  int ks, int M, int N,
                                                                  float* __restrict__ x, int64_t xs,
@@ -141,8 +145,8 @@ __global__ __launch_bounds__(256) void splitk_reduce_norm_kernel(const float* __
 #pragma unroll
   for (int u = 0; u < VPT; ++u) {
     const int k = 4 * (threadIdx.x + u * blockDim.x);
-    r[u] = k < N ? *reinterpret_cast<const float4*>(x + (int64_t)m * xs + k)
-                 : make_float4(0.f, 0.f, 0.f, 0.f);
+    r[u] = RES && k < N ? *reinterpret_cast<const float4*>(x + (int64_t)m * xs + k)
+                        : make_float4(0.f, 0.f, 0.f, 0.f);
     v[u] = make_float4(0.f, 0.f, 0.f, 0.f);
   }
   // Slices in order, ZG at a time (ks <= kMfmaMaxSplit).
@@ -169,34 +173,39 @@ __global__ __launch_bounds__(256) void splitk_reduce_norm_kernel(const float* __
         }
       }
   }
+  if constexpr (RES) {
 #pragma unroll
-  for (int u = 0; u < VPT; ++u) {
-    float4 acc = v[u];
-    acc.x += r[u].x;
-    acc.y += r[u].y;
-    acc.z += r[u].z;
-    acc.w += r[u].w;
-    v[u] = acc;
-    const int k = 4 * (threadIdx.x + u * blockDim.x);
-    if (k < N) *reinterpret_cast<float4*>(x + (int64_t)m * xs + k) = acc;
+    for (int u = 0; u < VPT; ++u) {
+      float4 acc = v[u];
+      acc.x += r[u].x;
+      acc.y += r[u].y;
+      acc.z += r[u].z;
+      acc.w += r[u].w;
+      v[u] = acc;
+      const int k = 4 * (threadIdx.x + u * blockDim.x);
+      if (k < N) *reinterpret_cast<float4*>(x + (int64_t)m * xs + k) = acc;
+    }
   }
-  rmsnorm_regs<bf16, VPT>(v, gain, y, m, 0, nck, N, eps, sh);
+  rmsnorm_regs<bf16, VPT>(v, gain, y, m, N, nck, N, eps, sh);
 }
 
 hipError_t launch_splitk_reduce_norm(const float* part, int ks, int M, int N, float* x,
                                      int64_t x_stride, const void* gain, void* y, int y_nck,
-                                     float eps, hipStream_t st) {
+                                     float eps, bool residual, hipStream_t st) {
   if (M <= 0) return hipSuccess;
   if (N > 8192 || N % 4 || x_stride % 4 || ks < 1 || ks > kMfmaMaxSplit) return hipErrorInvalidValue;
   const int vpt = (N + 1023) / 1024;
   dim3 grid(M), block(256);
-#define DF_RN(V)                                                                               \
-  hipLaunchKernelGGL((splitk_reduce_norm_kernel<V>), grid, block, 0, st, part, ks, M, N, x,   \
+#define DF_RN(V, R)                                                                               \
+  hipLaunchKernelGGL((splitk_reduce_norm_kernel<V, R>), grid, block, 0, st, part, ks, M, N, x,   \
                      x_stride, (const bf16*)gain, (bf16*)y, y_nck, eps)
-  if (vpt <= 1) DF_RN(1);
-  else if (vpt <= 2) DF_RN(2);
-  else if (vpt <= 4) DF_RN(4);
-  else DF_RN(8);
+#define DF_RN2(V) \
+  if (residual) DF_RN(V, true); else DF_RN(V, false)
+  if (vpt <= 1) { DF_RN2(1); }
+  else if (vpt <= 2) { DF_RN2(2); }
+  else if (vpt <= 4) { DF_RN2(4); }
+  else { DF_RN2(8); }
+#undef DF_RN2
 #undef DF_RN
   return hipGetLastError();
 }
@@ -218,13 +227,16 @@ __global__ __launch_bounds__(256) void embed_kernel(const T* E, const int32_t* a
   }
   const T* e = E + (int64_t)id * d;
   float* xr = x + (int64_t)row * d;
+  // The row stays in registers for its norm (each thread normalises the
+  // elements it stored).
+  float4 v[VPT];
 #pragma unroll
   for (int u = 0; u < VPT; ++u) {
     const int k = 4 * (threadIdx.x + u * blockDim.x);
-    if (k < d) *reinterpret_cast<float4*>(xr + k) = load4<T>(e + k);
+    v[u] = k < d ? load4<T>(e + k) : make_float4(0.f, 0.f, 0.f, 0.f);
+    if (k < d) *reinterpret_cast<float4*>(xr + k) = v[u];
   }
-  __syncthreads();
-  rmsnorm_row<T, VPT>(xr, gain, h, row, 0, nck, d, eps, sh);
+  rmsnorm_regs<T, VPT>(v, gain, h, row, 0, nck, d, eps, sh);
 }
 
 hipError_t launch_embed(int dtype, const void* embed, const int32_t* anchor, int batch, int block,

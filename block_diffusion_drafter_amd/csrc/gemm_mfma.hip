@@ -790,9 +790,9 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
 // the GEMM on the same stream), with the RMSNorm of the updated rows when the
 // caller asked for it.
 static hipError_t launch_splitk_reduce(int epi, const GemmArgs& a, hipStream_t st) {
-  if (epi == EPI_RESID && a.norm_w)
+  if ((epi == EPI_RESID || epi == EPI_STORE_F32) && a.norm_w)
     return launch_splitk_reduce_norm(a.part, a.ksplit, a.M, a.N, a.resid, a.out_stride, a.norm_w,
-                                     a.norm_out, a.norm_nck, a.norm_eps, st);
+                                     a.norm_out, a.norm_nck, a.norm_eps, epi == EPI_RESID, st);
   float* dst = epi == EPI_RESID ? a.resid : reinterpret_cast<float*>(a.out);
   const int64_t n4 = (int64_t)a.M * a.N / 4;
   const int blocks = (int)std::min<int64_t>((n4 + 255) / 256, 4096);
@@ -812,8 +812,9 @@ static int usable_ksplit(int epi, const GemmArgs& a) {
   return 1;
 }
 
-bool gemm_fuses_norm(int dtype, const GemmArgs& a) {
-  return gemm_uses_mfma(dtype, a.M, a.K, a.a_tiled != 0, EPI_RESID) && usable_ksplit(EPI_RESID, a) > 1 &&
+bool gemm_fuses_norm(int dtype, const GemmArgs& a, int epi) {
+  return (epi == EPI_RESID || epi == EPI_STORE_F32) &&
+         gemm_uses_mfma(dtype, a.M, a.K, a.a_tiled != 0, epi) && usable_ksplit(epi, a) > 1 &&
          a.N <= 8192;
 }
 

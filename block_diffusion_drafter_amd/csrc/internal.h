@@ -61,7 +61,9 @@ struct GemmArgs {
   int ksplit;                     // K slices of an MFMA launch (set by its launcher)
   // EPI_RESID on the MFMA path with K slices (gemm_fuses_norm): the reduce of
   // the slices also writes RMSNorm(resid row; norm_w) to norm_out, tiled bf16
-  // with norm_nck chunks per row. Ignored (nullptr) otherwise.
+  // with norm_nck chunks per row. EPI_STORE_F32 likewise: the reduce writes
+  // only RMSNorm(sum row; norm_w) to norm_out (row-major bf16, row stride N,
+  // when norm_nck is 0), not out. Ignored (nullptr) otherwise.
   const void* norm_w;
   void* norm_out;
   int norm_nck;
@@ -131,12 +133,13 @@ int mfma_argmax_keys(int M, int N, int K);
 // K slices the MFMA kernel splits a projection into (1 = no split); the
 // partial buffer it then needs is ksplit * M * N floats.
 int mfma_gemm_ksplit(int epi, int M, int N, int K);
-// Whether a residual projection with these arguments ends in a K-slice
-// reduce that can also write the RMSNorm of the updated rows (norm_w).
-bool gemm_fuses_norm(int dtype, const GemmArgs& a);
+// Whether a residual (EPI_RESID) or store (EPI_STORE_F32) projection with
+// these arguments ends in a K-slice reduce that can also write the RMSNorm of
+// its rows (norm_w; a store projection then writes only the normalised rows).
+bool gemm_fuses_norm(int dtype, const GemmArgs& a, int epi = EPI_RESID);
 hipError_t launch_splitk_reduce_norm(const float* part, int ks, int M, int N, float* x,
                                      int64_t x_stride, const void* gain, void* y, int y_nck,
-                                     float eps, hipStream_t st);
+                                     float eps, bool residual, hipStream_t st);
 // Keys per row that the LM-head projection writes (its column blocks).
 int gemm_amax_cols(int dtype, int M, int N, int K);
 

@@ -207,6 +207,35 @@ def test_gpu_capacity_overflow_is_flagged_and_clamped():
     assert status.item() == B.DEV_TOKEN
 
 
+def test_gpu_append_of_zero_rows_keeps_lengths_and_checks_offsets():
+    # n_tok = 0: no projection, no cache write, only the length bookkeeping
+    # and the offset checks (the round's append when no row was accepted is
+    # never empty, but a caller's split append may be).
+    cfg = TINY_FP32
+    log(f"case: append of zero rows, {cfg.name}")
+    M = build_model(cfg)
+    cap = 64
+    cache = M.gpu.new_cache(3, cap)
+    cache.ctx_len.copy_(torch.tensor([5, 0, 63], dtype=torch.int32))
+    cache.k.normal_()
+    cache.v.normal_()
+    k0, v0 = cache.k.clone(), cache.v.clone()
+    ws = M.gpu.new_workspace(3, cap, 16)
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ctx = torch.empty((0, cfg.hidden), device="cuda")
+    M.gpu.ctx_kv_append(cache, ctx, torch.zeros(4, dtype=torch.int32, device="cuda"), ws, status)
+    torch.cuda.synchronize()
+    assert status.item() == 0
+    assert cache.ctx_len.cpu().tolist() == [5, 0, 63]
+    assert torch.equal(cache.k, k0) and torch.equal(cache.v, v0)
+    # offsets that do not end at n_tok = 0 are flagged; nothing is written
+    bad = torch.tensor([0, 0, 2, 2], dtype=torch.int32, device="cuda")
+    M.gpu.ctx_kv_append(cache, ctx, bad, ws, status)
+    torch.cuda.synchronize()
+    assert status.item() & B.DEV_OFFSETS
+    assert torch.equal(cache.k, k0) and torch.equal(cache.v, v0)
+
+
 def test_gpu_small_bf16_merged_segments_groups_and_head_dim64():
     # batch >= 8: sequences that span several workgroups' key ranges are
     # merged by the last workgroup to finish (no combine launch); GQA groups
