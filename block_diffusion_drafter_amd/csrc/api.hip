@@ -526,12 +526,17 @@ static int32_t append_rows(const dflash_handle* h, const dflash_kv_cache* cache,
     g.snap_src = cache->ctx_len;
     g.snap_dst = lens;
     g.snap_n = cache->batch;
+    // Split over K: the append kernel sums the slices' partials itself.
+    g.defer_reduce = 1;
+    const int slices = gemm_store_slices(c.dtype, g);
     rc = run_gemm(c.dtype, EPI_STORE_F32, g, st);
     if (rc) return rc;
     NormRopeArgs a;
     std::memset(&a, 0, sizeof(a));
-    a.src = kv;
+    a.src = slices > 1 ? g.part : kv;
     a.src_stride = N;
+    a.src_slices = slices;
+    a.slice_stride = (int64_t)n_tok * N;
     a.k_cache = cache->k;
     a.v_cache = cache->v;
     for (int l = 0; l < L; ++l) a.k_norm[l] = h->layers[l].k_norm;

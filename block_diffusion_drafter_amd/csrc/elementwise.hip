@@ -584,6 +584,28 @@ __global__ __launch_bounds__(256) void norm_rope_append_kernel(NormRopeArgs p) {
       x1[it] = src[c + PAIRS];
     }
   }
+  // The projection's K-slice partials, added in slice order (one batch of
+  // loads per slice).
+  for (int z = 1; z < p.src_slices; ++z) {
+    float y0[NIT], y1[NIT];
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const int item = (it * 4 + wave) * HPW + sub;
+      const int k = item / kNrRows, i = item % kNrRows, h = h0 + k;
+      y0[it] = y1[it] = 0.f;
+      if (h < NH && i < tile.nrows) {
+        const float* src = p.src + z * p.slice_stride + (int64_t)(tile.row0 + i) * p.src_stride +
+                           (int64_t)h * HD;
+        y0[it] = src[c];
+        y1[it] = src[c + PAIRS];
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      x0[it] += y0[it];
+      x1[it] += y1[it];
+    }
+  }
   __syncthreads();  // rtab
   const size_t layer_stride = (size_t)p.cache_batch * Hkv * p.cap * HD;
 #pragma unroll

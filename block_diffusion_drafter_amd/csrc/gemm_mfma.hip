@@ -812,6 +812,11 @@ static int usable_ksplit(int epi, const GemmArgs& a) {
   return 1;
 }
 
+int gemm_store_slices(int dtype, const GemmArgs& a) {
+  if (!gemm_uses_mfma(dtype, a.M, a.K, a.a_tiled != 0, EPI_STORE_F32)) return 1;
+  return usable_ksplit(EPI_STORE_F32, a);
+}
+
 bool gemm_fuses_norm(int dtype, const GemmArgs& a, int epi) {
   return (epi == EPI_RESID || epi == EPI_STORE_F32) &&
          gemm_uses_mfma(dtype, a.M, a.K, a.a_tiled != 0, epi) && usable_ksplit(epi, a) > 1 &&
@@ -829,7 +834,7 @@ static hipError_t launch_mfma_t(const GemmArgs& a0, hipStream_t st) {
   hipLaunchKernelGGL((gemm_mfma_kernel<BM, BN, WGM, WGN, KF, NS, EPI>), grid, block, 0, st,
                      a, n_colblk, n_rowblk);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.ksplit == 1) return e;
+  if (e != hipSuccess || a.ksplit == 1 || (EPI == EPI_STORE_F32 && a.defer_reduce)) return e;
   return launch_splitk_reduce(EPI, a, st);
 }
 
@@ -845,7 +850,7 @@ static hipError_t launch_pipe_t(const GemmArgs& a0, hipStream_t st) {
   hipLaunchKernelGGL((gemm_pipe_kernel<BM, BN, WGM, WGN, NS, EPI>), grid, block, 0, st, a,
                      n_colblk, n_rowblk);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.ksplit == 1) return e;
+  if (e != hipSuccess || a.ksplit == 1 || (EPI == EPI_STORE_F32 && a.defer_reduce)) return e;
   return launch_splitk_reduce(EPI, a, st);
 }
 

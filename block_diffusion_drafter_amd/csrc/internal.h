@@ -59,6 +59,8 @@ struct GemmArgs {
   float* part;
   int64_t part_elems;
   int ksplit;                     // K slices of an MFMA launch (set by its launcher)
+  int defer_reduce;               // EPI_STORE_F32: leave the K slices' partials for the
+                                  // consumer to sum (gemm_store_slices of them), no reduce
   // EPI_RESID on the MFMA path with K slices (gemm_fuses_norm): the reduce of
   // the slices also writes RMSNorm(resid row; norm_w) to norm_out, tiled bf16
   // with norm_nck chunks per row. EPI_STORE_F32 likewise: the reduce writes
@@ -137,6 +139,10 @@ int mfma_gemm_ksplit(int epi, int M, int N, int K);
 // these arguments ends in a K-slice reduce that can also write the RMSNorm of
 // its rows (norm_w; a store projection then writes only the normalised rows).
 bool gemm_fuses_norm(int dtype, const GemmArgs& a, int epi = EPI_RESID);
+// K slices an EPI_STORE_F32 projection with these arguments leaves in a.part
+// (fp32 [slices][M][N], slice z at z*M*N) when a.defer_reduce is set; 1: the
+// output is in a.out as usual.
+int gemm_store_slices(int dtype, const GemmArgs& a);
 hipError_t launch_splitk_reduce_norm(const float* part, int ks, int M, int N, float* x,
                                      int64_t x_stride, const void* gain, void* y, int y_nck,
                                      float eps, bool residual, hipStream_t st);
@@ -223,6 +229,8 @@ struct NormRopeArgs {
                               // sequence s is appended iff i <= accept_len[s] (cu_new unused)
   int32_t* ctx_len_out;   // append mode: ctx_len (the live array, updated by the kernel);
                           // ctx_len above then points at a snapshot taken before the call
+  int src_slices;         // append mode: > 1: a row of src is the sum, in slice order, of
+  int64_t slice_stride;   // src_slices fp32 K-slice partials slice_stride floats apart
   int32_t* dev_status;
   int batch, cache_batch, n_heads, n_kv_heads, head_dim, block, cap, n_layers;
   int n_tok;              // append mode
