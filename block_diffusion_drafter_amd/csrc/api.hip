@@ -645,6 +645,7 @@ int32_t dflash_draft_forward(const dflash_handle* h, const dflash_kv_cache* cach
   const bool bf = c.dtype == DFLASH_BF16;
   enum { kNormNone, kNormDone, kNormDeferred };
   int pre_norm = kNormDone;
+  bool final_fused = false;  // the final norm written by the last slice reduce
   for (int l = 0; l < L; ++l) {
     const dflash_layer_weights& lw = h->layers[l];
     if (pre_norm == kNormNone) {
@@ -750,6 +751,13 @@ int32_t dflash_draft_forward(const dflash_handle* h, const dflash_kv_cache* cach
     }
     if (pre_norm != kNormNone) set_norm(g, h->layers[l + 1].in_norm, hbuf, nck_d, c.rms_eps);
     if (pre_norm == kNormDeferred) g.sq_out = sq;
+    // The last layer's slice reduce also writes the final norm of the slots
+    // after each anchor (the LM head's rows).
+    if (l + 1 == L && B > 1 && gemm_fuses_norm(c.dtype, g)) {
+      set_norm(g, h->w.final_norm, ybuf, nck_d, c.rms_eps);
+      g.norm_block = B;
+      final_fused = true;
+    }
     if ((rc = run_gemm(c.dtype, EPI_RESID, g, st))) return rc;
 
     if (hidden_out) {
@@ -761,11 +769,13 @@ int32_t dflash_draft_forward(const dflash_handle* h, const dflash_kv_cache* cach
 
   const int R = batch * (B - 1);
   if (R > 0) {
-    prof_begin(DFLASH_K_RMSNORM, 0, 0, st);
-    e = launch_rmsnorm(c.dtype, x, d, h->w.final_norm, ybuf, 0, nck_d, R, d, c.rms_eps, B - 1, B,
-                       1, st);
-    prof_end(st);
-    if (e != hipSuccess) return DFLASH_ERR_HIP;
+    if (!final_fused) {
+      prof_begin(DFLASH_K_RMSNORM, 0, 0, st);
+      e = launch_rmsnorm(c.dtype, x, d, h->w.final_norm, ybuf, 0, nck_d, R, d, c.rms_eps, B - 1,
+                         B, 1, st);
+      prof_end(st);
+      if (e != hipSuccess) return DFLASH_ERR_HIP;
+    }
     GemmArgs g = gemm_tiled(ybuf, pk + pl.lm, R, c.vocab, d);
     g.amax = amax;
     g.amax_stride = P.n_vtiles;

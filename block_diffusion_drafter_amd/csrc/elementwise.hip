@@ -136,7 +136,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_norm_kernel(const float* __
                                                                  int ks, int M, int N,
                                                                  float* __restrict__ x, int64_t xs,
                                                                  const bf16* gain, bf16* y, int nck,
-                                                                 float eps) {
+                                                                 float eps, int yblock) {
   constexpr int ZG = 4;  // slices loaded together (every load of a group before its adds)
   __shared__ float sh[4];
   const int m = blockIdx.x;
@@ -186,19 +186,27 @@ __global__ __launch_bounds__(256) void splitk_reduce_norm_kernel(const float* __
       if (k < N) *reinterpret_cast<float4*>(x + (int64_t)m * xs + k) = acc;
     }
   }
-  rmsnorm_regs<bf16, VPT>(v, gain, y, m, N, nck, N, eps, sh);
+  // yblock > 0: only rows m % yblock != 0 are normalised, into y row
+  // (m / yblock) * (yblock - 1) + m % yblock - 1 (a block's slots after its
+  // anchor; the decision is the same for the whole workgroup).
+  int yrow = m;
+  if (yblock > 0) {
+    if (m % yblock == 0) return;
+    yrow = (m / yblock) * (yblock - 1) + m % yblock - 1;
+  }
+  rmsnorm_regs<bf16, VPT>(v, gain, y, yrow, N, nck, N, eps, sh);
 }
 
 hipError_t launch_splitk_reduce_norm(const float* part, int ks, int M, int N, float* x,
                                      int64_t x_stride, const void* gain, void* y, int y_nck,
-                                     float eps, bool residual, hipStream_t st) {
+                                     float eps, bool residual, int y_block, hipStream_t st) {
   if (M <= 0) return hipSuccess;
   if (N > 8192 || N % 4 || x_stride % 4 || ks < 1 || ks > kMfmaMaxSplit) return hipErrorInvalidValue;
   const int vpt = (N + 1023) / 1024;
   dim3 grid(M), block(256);
 #define DF_RN(V, R)                                                                               \
   hipLaunchKernelGGL((splitk_reduce_norm_kernel<V, R>), grid, block, 0, st, part, ks, M, N, x,   \
-                     x_stride, (const bf16*)gain, (bf16*)y, y_nck, eps)
+                     x_stride, (const bf16*)gain, (bf16*)y, y_nck, eps, y_block)
 #define DF_RN2(V) \
   if (residual) DF_RN(V, true); else DF_RN(V, false)
   if (vpt <= 1) { DF_RN2(1); }

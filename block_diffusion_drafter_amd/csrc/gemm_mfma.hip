@@ -792,7 +792,8 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
 static hipError_t launch_splitk_reduce(int epi, const GemmArgs& a, hipStream_t st) {
   if ((epi == EPI_RESID || epi == EPI_STORE_F32) && a.norm_w)
     return launch_splitk_reduce_norm(a.part, a.ksplit, a.M, a.N, a.resid, a.out_stride, a.norm_w,
-                                     a.norm_out, a.norm_nck, a.norm_eps, epi == EPI_RESID, st);
+                                     a.norm_out, a.norm_nck, a.norm_eps, epi == EPI_RESID,
+                                     epi == EPI_RESID ? a.norm_block : 0, st);
   float* dst = epi == EPI_RESID ? a.resid : reinterpret_cast<float*>(a.out);
   const int64_t n4 = (int64_t)a.M * a.N / 4;
   const int blocks = (int)std::min<int64_t>((n4 + 255) / 256, 4096);

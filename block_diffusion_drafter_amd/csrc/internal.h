@@ -70,6 +70,9 @@ struct GemmArgs {
   void* norm_out;
   int norm_nck;
   float norm_eps;
+  int norm_block;                 // > 0 (EPI_RESID): residual row m is normalised only when
+                                  // m % norm_block != 0, into norm_out row
+                                  // (m / norm_block) * (norm_block - 1) + m % norm_block - 1
   // Weight-streaming path (bf16), the next RMSNorm deferred to its consumer:
   // an EPI_RESID projection with sq_out also writes bf16(x_new * norm_w)
   // tiled to norm_out and, for every 16-column tile j < T = ceil(N / 16) of
@@ -145,7 +148,7 @@ bool gemm_fuses_norm(int dtype, const GemmArgs& a, int epi = EPI_RESID);
 int gemm_store_slices(int dtype, const GemmArgs& a);
 hipError_t launch_splitk_reduce_norm(const float* part, int ks, int M, int N, float* x,
                                      int64_t x_stride, const void* gain, void* y, int y_nck,
-                                     float eps, bool residual, hipStream_t st);
+                                     float eps, bool residual, int y_block, hipStream_t st);
 // Keys per row that the LM-head projection writes (its column blocks).
 int gemm_amax_cols(int dtype, int M, int N, int K);
 
