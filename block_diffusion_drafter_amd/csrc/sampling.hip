@@ -2,17 +2,19 @@
 // residual resampling ("DFlash: Why a Diffusion Drafter Can Accelerate an
 // Autoregressive Model", sec. 4.2, eqs. 6-8 and Algorithm 1).
 //
-// Random numbers: Philox4x64-10 (Salmon, Moraes, Dror, Shaw, "Parallel random
+// Random numbers: Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel random
 // numbers: as easy as 1, 2, 3", SC 2011). Element i of (row, round, stream)
 // is word i % 4 of the block at counter (i / 4, row, round, stream) under key
-// (seed, 0); a uniform is ((w >> 41) + 0.5) * 2^-23 (24 significant bits:
-// exact in fp32, never 0 or 1). A
-// categorical draw is a Gumbel-max: the argmax of log-probability +
-// (-log(-log u)) over the support, lowest index on ties.
+// (low, high half of the 64-bit seed); a uniform is ((w >> 9) + 0.5) * 2^-23
+// (24 significant bits: exact in fp32, never 0 or 1). A categorical draw is a
+// Gumbel-max: the argmax of log-probability + (-log(-log u)) over the
+// support, lowest index on ties.
 //
 // Every reduction over the vocabulary is split over workgroups of 8192
-// logits (4 per thread, one Philox block per thread), so a batch of a few
-// rows still spreads over many CUs; small kernels merge the splits.
+// logits: a thread loads its 32 logits (8 steps of 4 consecutive ones) before
+// using any, takes their max and then their sum of exponentials (one exp per
+// logit, no data-dependent branch), and draws one Philox block per 4 logits;
+// small kernels merge the splits.
 #include <cmath>
 #include <mutex>
 
@@ -26,49 +28,75 @@ namespace {
 constexpr int kSplit = 8192;  // logits per workgroup
 constexpr int kThreads = 256;
 
-// 128-bit product of two 64-bit words from four 32 x 32 -> 64-bit
-// multiply-adds (schoolbook, with the middle partial sums folded into the
-// multiply-adds so that none overflows 64 bits):
-//   p10 = a1 b0 + hi(a0 b0), p01 = a0 b1 + lo(p10),
-//   lo = lo(a0 b0) | lo(p01) << 32, hi = a1 b1 + hi(p10) + hi(p01).
-__device__ __forceinline__ void mul_128(uint64_t a, uint64_t b, uint64_t& hi, uint64_t& lo) {
-  const uint32_t a0 = (uint32_t)a, a1 = (uint32_t)(a >> 32);
-  const uint32_t b0 = (uint32_t)b, b1 = (uint32_t)(b >> 32);
-  const uint64_t p00 = (uint64_t)a0 * b0;
-  const uint64_t p10 = (uint64_t)a1 * b0 + (p00 >> 32);
-  const uint64_t p01 = (uint64_t)a0 * b1 + (uint32_t)p10;
-  hi = (uint64_t)a1 * b1 + (p10 >> 32) + (p01 >> 32);
-  lo = (p01 << 32) | (uint32_t)p00;
-}
+constexpr int kIt = kSplit / (4 * kThreads);  // 4-logit steps per thread and split
 
-__device__ __forceinline__ void philox4x64(uint64_t c[4], uint64_t k0, uint64_t k1) {
-  const uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
-  const uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
+// Ten rounds: words 0 and 2 times the two multipliers (32 x 32 -> 64-bit
+// products), the products' halves exchanged with words 1 and 3 xor the round
+// key, the key bumped by the two Weyl constants between rounds.
+__device__ __forceinline__ void philox4x32(uint32_t c[4], uint32_t k0, uint32_t k1) {
+  const uint32_t M0 = 0xD2511F53u, M1 = 0xCD9E8D57u;
+  const uint32_t W0 = 0x9E3779B9u, W1 = 0xBB67AE85u;
 #pragma unroll
   for (int r = 0; r < 10; ++r) {
-    uint64_t hi0, lo0, hi1, lo1;
-    mul_128(M0, c[0], hi0, lo0);
-    mul_128(M1, c[2], hi1, lo1);
-    const uint64_t n0 = hi1 ^ c[1] ^ k0, n2 = hi0 ^ c[3] ^ k1;
+    const uint64_t p0 = (uint64_t)M0 * c[0];
+    const uint64_t p1 = (uint64_t)M1 * c[2];
+    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c[1] ^ k0;
+    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c[3] ^ k1;
     c[0] = n0;
-    c[1] = lo1;
+    c[1] = (uint32_t)p1;
     c[2] = n2;
-    c[3] = lo0;
+    c[3] = (uint32_t)p0;
     k0 += W0;
     k1 += W1;
   }
 }
 
 // The four uniforms of elements 4q .. 4q+3 of (row, round, stream).
-__device__ __forceinline__ void uniforms4(uint64_t seed, uint64_t q, uint64_t row, uint64_t rnd,
-                                          uint64_t stream, float u[4]) {
-  uint64_t c[4] = {q, row, rnd, stream};
-  philox4x64(c, seed, 0ull);
+__device__ __forceinline__ void uniforms4(uint64_t seed, uint32_t q, uint32_t row, uint32_t rnd,
+                                          uint32_t stream, float u[4]) {
+  uint32_t c[4] = {q, row, rnd, stream};
+  philox4x32(c, (uint32_t)seed, (uint32_t)(seed >> 32));
 #pragma unroll
-  for (int w = 0; w < 4; ++w) u[w] = ((float)(c[w] >> 41) + 0.5f) * 0x1p-23f;
+  for (int w = 0; w < 4; ++w) u[w] = ((float)(c[w] >> 9) + 0.5f) * 0x1p-23f;
 }
 
-__device__ __forceinline__ float gumbel(float u) { return -logf(-logf(u)); }
+// This thread's logits of a split: step i holds elements v0 + 4*kThreads*i
+// .. +3 (v0 = split*kSplit + 4*threadIdx.x), -inf past V; every load is
+// issued before any value is used.
+__device__ __forceinline__ void load_split(const float* l, int V, int split, float x[kIt][4]) {
+  const int v0 = split * kSplit + 4 * (int)threadIdx.x;
+  if ((V & 3) == 0 && (reinterpret_cast<uintptr_t>(l) & 15) == 0) {
+    // whole 16-byte groups: v < V implies v + 3 < V
+    const float4* l4 = reinterpret_cast<const float4*>(l);
+#pragma unroll
+    for (int i = 0; i < kIt; ++i) {
+      const int v = v0 + 4 * kThreads * i;
+      float4 t = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+      if (v < V) t = l4[v >> 2];
+      x[i][0] = t.x;
+      x[i][1] = t.y;
+      x[i][2] = t.z;
+      x[i][3] = t.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < kIt; ++i)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const int v = v0 + 4 * kThreads * i + w;
+        x[i][w] = v < V ? l[v] : -INFINITY;
+      }
+  }
+}
+
+// -log(-log u) from two hardware base-2 logarithms (v_log_f32, relative
+// error about 1 ulp; u in [2^-24, 1 - 2^-24] and a = -log2 u in
+// [8.6e-8, 24] are normal numbers, so no denormal scaling is needed):
+// -log(-log u) = -log(a ln 2) = -log(ln 2) - ln 2 * log2 a.
+__device__ __forceinline__ float gumbel(float u) {
+  const float a = -__builtin_amdgcn_logf(u);
+  return fmaf(-0.693147180559945309f, __builtin_amdgcn_logf(a), 0.366512920581664327f);
+}
 
 // Order-preserving key of (score, index): larger score wins, lower index on ties.
 __device__ __forceinline__ unsigned long long okey(float v, unsigned idx) {
@@ -97,6 +125,26 @@ struct Lse {
   }
   __device__ float value() const { return m + logf(s); }
 };
+
+// Log-sum-exp state of a thread's scaled logits (scaled in place): the max
+// first, then the sum of exp(x - max).
+__device__ __forceinline__ Lse tile_lse(float x[kIt][4], float inv_t) {
+  Lse l;
+#pragma unroll
+  for (int i = 0; i < kIt; ++i)
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      x[i][w] *= inv_t;
+      l.m = fmaxf(l.m, x[i][w]);
+    }
+  if (l.m != -INFINITY) {
+#pragma unroll
+    for (int i = 0; i < kIt; ++i)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) l.s += __expf(x[i][w] - l.m);
+  }
+  return l;
+}
 
 __device__ __forceinline__ unsigned long long block_max_key(unsigned long long k,
                                                             unsigned long long* sh) {
@@ -144,22 +192,36 @@ __global__ __launch_bounds__(kThreads) void sample_split_kernel(const float* log
   __shared__ float shm[kThreads / 64], shs[kThreads / 64];
   const int split = blockIdx.x, row = blockIdx.y;
   const float* l = logits + (int64_t)row * ld;
-  const int v0 = split * kSplit + 4 * threadIdx.x;
-  unsigned long long key = 0ull;
-  Lse lse;
-  for (int v = v0; v < min(V, (split + 1) * kSplit); v += 4 * kThreads) {
+  float x[kIt][4];
+  load_split(l, V, split, x);
+  Lse lse = tile_lse(x, inv_t);
+  // The thread's best perturbed score: it visits its indices in increasing
+  // order and keeps the first of equal scores, the lowest index on ties.
+  const int v0 = split * kSplit + 4 * (int)threadIdx.x;
+  float best = -INFINITY;
+  int best_v = v0;
+  auto step = [&](int i, bool full) {
+    const int v = v0 + 4 * kThreads * i;
+    if (!full && v >= V) return;
     float u[4];
-    uniforms4(seed, (uint64_t)(v >> 2), (uint64_t)row, (uint64_t)rnd, 0ull, u);
+    uniforms4(seed, (uint32_t)(v >> 2), (uint32_t)row, (uint32_t)rnd, 0u, u);
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      if (v + w < V) {
-        const float x = l[v + w] * inv_t;
-        lse.add(x);
-        const unsigned long long k = okey(x + gumbel(u[w]), (unsigned)(v + w));
-        key = k > key ? k : key;
+      const float sc = x[i][w] + gumbel(u[w]);
+      if ((full || v + w < V) && sc > best) {
+        best = sc;
+        best_v = v + w;
       }
     }
+  };
+  if ((split + 1) * kSplit <= V) {
+#pragma unroll
+    for (int i = 0; i < kIt; ++i) step(i, true);
+  } else {
+#pragma unroll
+    for (int i = 0; i < kIt; ++i) step(i, false);
   }
+  unsigned long long key = v0 < V ? okey(best, (unsigned)best_v) : 0ull;
   key = block_max_key(key, shk);
   block_lse(lse, shm, shs);
   if (threadIdx.x == 0) part[(int64_t)row * nsplit + split] = SplitStat{key, lse.m, lse.s};
@@ -195,22 +257,9 @@ __global__ __launch_bounds__(kThreads) void verify_stats_kernel(const float* dra
   const int split = blockIdx.x, r = blockIdx.y;  // r < batch*B: target; else draft
   const float* l = r < batch * B ? target_logits + (int64_t)r * V
                                  : draft_logits + (int64_t)(r - batch * B) * V;
-  Lse lse;
-  const int end = min(V, (split + 1) * kSplit);
-  if ((V & 3) == 0) {
-    // Rows start 16-byte aligned (row length a multiple of 4 floats, the
-    // buffers 16-byte aligned): one 16-byte load per thread and step.
-    const float4* l4 = reinterpret_cast<const float4*>(l);
-    for (int v = split * kSplit + 4 * threadIdx.x; v < end; v += 4 * kThreads) {
-      const float4 x = l4[v >> 2];
-      lse.add(x.x * inv_t);
-      lse.add(x.y * inv_t);
-      lse.add(x.z * inv_t);
-      lse.add(x.w * inv_t);
-    }
-  } else {
-    for (int v = split * kSplit + threadIdx.x; v < end; v += kThreads) lse.add(l[v] * inv_t);
-  }
+  float x[kIt][4];
+  load_split(l, V, split, x);
+  Lse lse = tile_lse(x, inv_t);
   block_lse(lse, shm, shs);
   if (threadIdx.x == 0) part[(int64_t)r * nsplit + split] = SplitStat{0ull, lse.m, lse.s};
 }
@@ -243,7 +292,7 @@ __global__ __launch_bounds__(kThreads) void verify_residual_kernel(
   if ((int)threadIdx.x < m) {
     const int i = threadIdx.x;
     float u4[4];
-    uniforms4(seed, (uint64_t)(i >> 2), (uint64_t)s, (uint64_t)rnd, 1ull, u4);
+    uniforms4(seed, (uint32_t)(i >> 2), (uint32_t)s, (uint32_t)rnd, 1u, u4);
     int y = drafts[(int64_t)s * m + i];
     y = y < 0 ? 0 : (y >= V ? V - 1 : y);  // ids outside the vocabulary are clamped
     const float lp = target_logits[((int64_t)s * B + i) * V + y] * inv_t - lse[s * B + i];
@@ -264,22 +313,28 @@ __global__ __launch_bounds__(kThreads) void verify_residual_kernel(
   const float lse_q = a < m ? lse[batch * B + s * m + a] : 0.f;
   const float* lp_row = target_logits + ((int64_t)s * B + a) * V;
   const float* lq_row = a < m ? draft_logits + ((int64_t)s * m + a) * V : nullptr;
-  const uint64_t grow = (uint64_t)s * B + a;
+  const uint32_t grow = (uint32_t)(s * B + a);
+  float xp[kIt][4], xq[kIt][4];
+  load_split(lp_row, V, split, xp);
+  if (lq_row) load_split(lq_row, V, split, xq);
   unsigned long long kres = 0ull, kfb = 0ull;
-  const int v0 = split * kSplit + 4 * threadIdx.x;
-  for (int v = v0; v < min(V, (split + 1) * kSplit); v += 4 * kThreads) {
+  const int v0 = split * kSplit + 4 * (int)threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < kIt; ++i) {
+    const int v = v0 + 4 * kThreads * i;
+    if (v >= V) break;
     float u[4];
-    uniforms4(seed, (uint64_t)(v >> 2), grow, (uint64_t)rnd, 2ull, u);
+    uniforms4(seed, (uint32_t)(v >> 2), grow, (uint32_t)rnd, 2u, u);
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       const int vv = v + w;
       if (vv >= V) continue;
       const float g = gumbel(u[w]);
-      const float lp = lp_row[vv] * inv_t - lse_p;
+      const float lp = xp[i][w] * inv_t - lse_p;
       const unsigned long long kf = okey(lp + g, (unsigned)vv);
       kfb = kf > kfb ? kf : kfb;
       if (lq_row) {
-        const float d = expf(lp) - expf(lq_row[vv] * inv_t - lse_q);
+        const float d = expf(lp) - expf(xq[i][w] * inv_t - lse_q);
         if (d > 0.f) {
           const unsigned long long kr = okey(logf(d) + g, (unsigned)vv);
           kres = kr > kres ? kr : kres;

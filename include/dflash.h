@@ -294,10 +294,11 @@ int32_t dflash_accept(const int32_t *draft_tokens, const int32_t *target_tokens,
  * target's and the draft's logits at the same temperature T > 0 (no top-p /
  * top-k filtering).
  *
- * Random numbers: Philox4x64-10 (Salmon et al., "Parallel random numbers: as
- * easy as 1, 2, 3", SC 2011) with key (seed, 0). Element i of a (row, round,
- * stream) triple is word i % 4 of the block at counter (i / 4, row, round,
- * stream); a uniform is ((w >> 41) + 0.5) * 2^-23. Streams: 0 drafting (row =
+ * Random numbers: Philox4x32-10 (Salmon et al., "Parallel random numbers: as
+ * easy as 1, 2, 3", SC 2011) with key (low, high 32 bits of seed). Element i
+ * of a (row, round, stream) triple is word i % 4 of the block at counter
+ * (i / 4, row, round, stream) (each word 32 bits, so round is taken modulo
+ * 2^32); a uniform is ((w >> 9) + 0.5) * 2^-23. Streams: 0 drafting (row =
  * the logits row), 1 acceptance tests (row = sequence, element = position),
  * 2 correction / bonus draws (row = sequence * block_size + position).
  * A categorical draw is the Gumbel-max argmax of log-probability +

@@ -24,19 +24,21 @@ Readings taken where the pages are silent (each repeated at its use):
     law at the position after the last candidate (target row B-1 of B rows).
   * an empty residual support (p <= q everywhere, which eq. 7 makes a
     probability-0 event but rounding can reach) falls back to sampling p.
-  * the random numbers are drawn from Philox4x64-10 (the counter-based
+  * the random numbers are drawn from Philox4x32-10 (the counter-based
     generator of Salmon, Moraes, Dror and Shaw, "Parallel random numbers: as
     easy as 1, 2, 3", SC 2011), so the GPU side can draw the same numbers from
-    the same published definition: key (seed, 0); counter (i // 4, row, round,
-    stream) with word i % 4; a uniform is ((w >> 41) + 0.5) / 2^23, exact in
-    fp32 and fp64 (24 significant bits). Streams: 0 drafting (row = draft row), 1 acceptance
+    the same published definition: key (low, high 32 bits of the 64-bit
+    seed); counter (i // 4, row, round, stream), each below 2^32, with word
+    i % 4; a uniform is ((w >> 9) + 0.5) / 2^23, exact in fp32 and fp64 (24
+    significant bits). Streams: 0 drafting (row = draft row), 1 acceptance
     uniforms (row = sequence, i = position), 2 residual / bonus draws
     (row = sequence * B + position).
   * a categorical sample uses the Gumbel-max construction: the argmax of
     log-probability + (-log(-log u)) over the support is distributed as the
     law (a standard identity; pinned here by Monte Carlo), lowest index on ties.
 
-Parity status: Philox is pinned against NumPy's Philox bit generator; the
+Parity status: Philox is pinned to the generator's published known-answer
+vectors (tests/golden/philox4x32_10_kat.txt); the
 categorical sampler and the verification rule are pinned by Monte Carlo
 against the target law (eq. 8) and by closed forms (eq. 7's acceptance mass,
 the temperature -> 0 limit reducing to the greedy rule).
@@ -47,60 +49,53 @@ from dataclasses import dataclass
 
 import numpy as np
 
-_M0 = np.uint64(0xD2E7470EE14C6C93)
-_M1 = np.uint64(0xCA5A826395121157)
-_W0 = np.uint64(0x9E3779B97F4A7C15)
-_W1 = np.uint64(0xBB67AE8584CAA73B)
+_M0 = np.uint64(0xD2511F53)
+_M1 = np.uint64(0xCD9E8D57)
+_W0 = np.uint64(0x9E3779B9)
+_W1 = np.uint64(0xBB67AE85)
 _M32 = np.uint64(0xFFFFFFFF)
 _S32 = np.uint64(32)
 
 
-def _mulhilo(a, b):
-    """Full 64x64 -> 128-bit product of uint64 arrays, as (hi, lo), from 32-bit limbs."""
-    a0, a1 = a & _M32, a >> _S32
-    b0, b1 = b & _M32, b >> _S32
-    t = a0 * b0
-    w0 = t & _M32
-    k = t >> _S32
-    t = a1 * b0 + k
-    w1 = t & _M32
-    w2 = t >> _S32
-    t = a0 * b1 + w1
-    k = t >> _S32
-    hi = a1 * b1 + w2 + k
-    lo = (t << _S32) | w0
-    return hi, lo
-
-
-def philox4x64(c0, c1, c2, c3, k0, k1):
-    """Philox4x64 with 10 rounds [Salmon et al. 2011, sec. 4]: each round
-    multiplies words 0 and 2 by the two round multipliers, exchanges the
-    halves of the products with words 1 and 3 xor the round key, and the key
-    is bumped by the two Weyl constants between rounds. Array arguments of
-    any broadcastable shape (uint64); returns the four output words."""
-    with np.errstate(over="ignore"):
-        c = [np.asarray(x, dtype=np.uint64) for x in (c0, c1, c2, c3)]
-        k = [np.asarray(k0, dtype=np.uint64), np.asarray(k1, dtype=np.uint64)]
-        for r in range(10):
-            hi0, lo0 = _mulhilo(_M0, c[0])
-            hi1, lo1 = _mulhilo(_M1, c[2])
-            c = [hi1 ^ c[1] ^ k[0], lo1, hi0 ^ c[3] ^ k[1], lo0]
-            if r < 9:
-                k = [k[0] + _W0, k[1] + _W1]
+def philox4x32(c0, c1, c2, c3, k0, k1):
+    """Philox4x32 with 10 rounds [Salmon et al. 2011, sec. 4]: each round
+    multiplies words 0 and 2 by the two round multipliers (32 x 32 -> 64-bit
+    products), exchanges the halves of the products with words 1 and 3 xor
+    the round key, and the key is bumped by the two Weyl constants between
+    rounds. Words are held in uint64 arrays of any broadcastable shape
+    (values below 2^32, so the products are exact); returns the four output
+    words."""
+    c = [np.asarray(x, dtype=np.uint64) for x in (c0, c1, c2, c3)]
+    k = [np.asarray(k0, dtype=np.uint64), np.asarray(k1, dtype=np.uint64)]
+    for x in c + k:
+        assert np.all(x <= _M32), "Philox4x32 words are 32-bit"
+    for r in range(10):
+        p0 = _M0 * c[0]
+        p1 = _M1 * c[2]
+        c = [(p1 >> _S32) ^ c[1] ^ k[0], p1 & _M32, (p0 >> _S32) ^ c[3] ^ k[1], p0 & _M32]
+        if r < 9:
+            k = [(k[0] + _W0) & _M32, (k[1] + _W1) & _M32]
     return c
+
+
+def _key(seed: int):
+    seed = int(seed) % (1 << 64)
+    return np.uint64(seed & 0xFFFFFFFF), np.uint64(seed >> 32)
+
+
+def _to_uniform(w):
+    return ((w >> np.uint64(9)).astype(np.float64) + 0.5) / float(1 << 23)
 
 
 def uniforms(seed: int, idx, row, rnd: int, stream: int) -> np.ndarray:
     """u in (0, 1) for element indices idx of (row, round, stream): word
-    idx % 4 of Philox at counter (idx // 4, row, round, stream), key (seed, 0);
-    u = ((w >> 41) + 0.5) / 2^23."""
+    idx % 4 of Philox4x32-10 at counter (idx // 4, row, round, stream), key
+    (low, high half of seed); u = ((w >> 9) + 0.5) / 2^23."""
     idx = np.asarray(idx, dtype=np.uint64)
     row = np.asarray(row, dtype=np.uint64)
-    words = philox4x64(idx >> np.uint64(2), row, np.uint64(rnd), np.uint64(stream),
-                       np.uint64(seed), np.uint64(0))
+    words = philox4x32(idx >> np.uint64(2), row, np.uint64(rnd), np.uint64(stream), *_key(seed))
     sel = (idx & np.uint64(3)).astype(np.int64)
-    w = np.choose(sel, words)
-    return ((w >> np.uint64(41)).astype(np.float64) + 0.5) / float(1 << 23)
+    return _to_uniform(np.choose(sel, words))
 
 
 def row_uniforms(seed: int, V: int, rows, rnd: int, stream: int) -> np.ndarray:
@@ -108,10 +103,10 @@ def row_uniforms(seed: int, V: int, rows, rnd: int, stream: int) -> np.ndarray:
     ([len(rows), V]), computing each Philox block once for its four elements."""
     rows = np.asarray(rows, dtype=np.uint64).reshape(-1, 1)
     nb = (V + 3) // 4
-    words = philox4x64(np.arange(nb, dtype=np.uint64)[None, :], rows, np.uint64(rnd),
-                       np.uint64(stream), np.uint64(seed), np.uint64(0))
+    words = philox4x32(np.arange(nb, dtype=np.uint64)[None, :], rows, np.uint64(rnd),
+                       np.uint64(stream), *_key(seed))
     w = np.stack(words, axis=-1).reshape(rows.shape[0], nb * 4)[:, :V]
-    return ((w >> np.uint64(41)).astype(np.float64) + 0.5) / float(1 << 23)
+    return _to_uniform(w)
 
 
 def gumbel(u: np.ndarray) -> np.ndarray:

@@ -1,6 +1,6 @@
 """Temperature > 0 drafting and verification: the HIP kernels against the
 oracle (oracle/sampling.py) on the same seeded fp32 logits and the same
-Philox4x64-10 random numbers (each side implements the generator from its
+Philox4x32-10 random numbers (each side implements the generator from its
 published definition).
 
 Decisions are compared bit-exactly wherever floating point cannot decide them

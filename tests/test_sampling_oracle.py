@@ -1,7 +1,8 @@
 """Pins of the temperature > 0 oracle (oracle/sampling.py), none of which
 re-runs its formulas:
 
-  * Philox4x64-10 against NumPy's Philox bit generator (library routine);
+  * Philox4x32-10 against the generator's published known-answer vectors
+    (tests/golden/philox4x32_10_kat.txt);
   * the Gumbel-max categorical sampler against the softmax law (Monte Carlo);
   * the verification rule against the target law, eq. 8 of the technical
     review ("DFlash: Why a Diffusion Drafter Can Accelerate an Autoregressive
@@ -11,6 +12,8 @@ re-runs its formulas:
   * the temperature -> 0 limit, which must reduce to the greedy accept rule;
   * planted mistakes (mutations) that one of the pins must catch.
 """
+from pathlib import Path
+
 import numpy as np
 import pytest
 
@@ -18,43 +21,51 @@ from oracle import dflash_oracle as O
 from oracle import sampling as S
 
 
-def numpy_philox_block(counter, key):
-    """The four words NumPy's Philox produces first; it increments its 256-bit
-    counter before each block, so this is the block at counter + 1."""
-    g = np.random.Philox(counter=np.array(counter, dtype=np.uint64),
-                         key=np.array(key, dtype=np.uint64))
-    return [int(x) for x in g.random_raw(4)]
+GOLDEN = Path(__file__).parent / "golden" / "philox4x32_10_kat.txt"
 
 
-def ours(counter, key):
-    c = list(counter)
-    # add one with carry, as NumPy does before its first block
-    for i in range(4):
-        c[i] = (c[i] + 1) % (1 << 64)
-        if c[i] != 0:
-            break
-    out = S.philox4x64(*[np.uint64(x) for x in c], np.uint64(key[0]), np.uint64(key[1]))
-    return [int(x) for x in out]
+def kat_vectors():
+    out = []
+    for line in GOLDEN.read_text().splitlines():
+        if line.strip() and not line.startswith("#"):
+            w = [int(x, 16) for x in line.split()]
+            out.append((w[:4], w[4:6], w[6:]))
+    return out
 
 
-@pytest.mark.parametrize("counter,key", [
-    ([0, 0, 0, 0], [0, 0]),
-    ([5, 7, 11, 13], [0x0123456789ABCDEF, 0xFEDCBA9876543210]),
-    ([(1 << 64) - 1, 3, 0, 9], [42, 0]),  # carry into the second word
-    ([(1 << 64) - 1, (1 << 64) - 1, 2, 0], [1 << 63, 12345]),
-])
-def test_philox_matches_numpy(counter, key):
-    assert ours(counter, key) == numpy_philox_block(counter, key)
+def test_philox_known_answer_vectors():
+    vecs = kat_vectors()
+    assert len(vecs) == 3
+    for counter, key, want in vecs:
+        got = S.philox4x32(*[np.uint64(x) for x in counter], np.uint64(key[0]), np.uint64(key[1]))
+        assert [int(x) for x in got] == want
 
 
-def test_philox_vectorised_matches_numpy_many():
-    rng = np.random.default_rng(7)
-    c = rng.integers(0, 1 << 62, size=(64, 4), dtype=np.uint64)
-    k = rng.integers(0, 1 << 62, size=(64, 2), dtype=np.uint64)
-    got = S.philox4x64(c[:, 0] + np.uint64(1), c[:, 1], c[:, 2], c[:, 3], k[:, 0], k[:, 1])
-    for j in range(64):
-        ref = numpy_philox_block([int(x) for x in c[j]], [int(x) for x in k[j]])
-        assert [int(got[w][j]) for w in range(4)] == ref
+def test_philox_known_answer_vectors_as_one_array_call():
+    vecs = kat_vectors()
+    c = np.array([v[0] for v in vecs], dtype=np.uint64)
+    k = np.array([v[1] for v in vecs], dtype=np.uint64)
+    got = S.philox4x32(c[:, 0], c[:, 1], c[:, 2], c[:, 3], k[:, 0], k[:, 1])
+    for j, (_, _, want) in enumerate(vecs):
+        assert [int(got[w][j]) for w in range(4)] == want
+
+
+def test_philox_refuses_words_of_more_than_32_bits():
+    with pytest.raises(AssertionError):
+        S.philox4x32(np.uint64(1 << 32), 0, 0, 0, 0, 0)
+
+
+def test_seed_halves_are_the_key():
+    # the 64-bit seed is the key (low word, high word): a seed that differs
+    # only in its high half draws different numbers
+    a = S.uniforms(5, np.arange(8), 0, 0, 0)
+    b = S.uniforms(5 + (1 << 32), np.arange(8), 0, 0, 0)
+    assert not np.array_equal(a, b)
+    vecs = kat_vectors()
+    counter, key, want = vecs[2]
+    seed = key[0] | (key[1] << 32)
+    u = S.uniforms(seed, np.arange(4) + 4 * counter[0], counter[1], counter[2], counter[3])
+    assert np.array_equal(u, (np.array(want, dtype=np.float64) // 512 + 0.5) / (1 << 23))
 
 
 def test_uniforms_lattice():
@@ -67,7 +78,7 @@ def test_uniforms_lattice():
 
 def test_row_uniforms_equal_elementwise_definition():
     V = 37
-    rows = np.array([0, 3, 1 << 40])
+    rows = np.array([0, 3, (1 << 32) - 1])
     a = S.row_uniforms(9, V, rows, 5, 2)
     b = S.uniforms(9, np.arange(V)[None, :], rows[:, None], 5, 2)
     assert np.array_equal(a, b)
@@ -175,6 +186,13 @@ def mutated(monkeypatch, name):
         monkeypatch.setattr(S, "verify", bad)
     elif name == "gumbel_sign":
         monkeypatch.setattr(S, "gumbel", lambda u: np.log(-np.log(u)))
+    elif name == "philox_key_not_bumped":
+        monkeypatch.setattr(S, "_W0", np.uint64(0))
+        monkeypatch.setattr(S, "_W1", np.uint64(0))
+    elif name == "philox_multipliers_swapped":
+        m0, m1 = S._M0, S._M1
+        monkeypatch.setattr(S, "_M0", m1)
+        monkeypatch.setattr(S, "_M1", m0)
     elif name == "temperature_ignored":
         orig_ls = S.log_softmax
         monkeypatch.setattr(S, "log_softmax", lambda logits, T: orig_ls(logits, 1.0))
@@ -185,6 +203,8 @@ def mutated(monkeypatch, name):
     ("residual_from_target", test_worked_example_acceptance_and_correction),
     ("gumbel_sign", test_gumbel_max_samples_the_softmax_law),
     ("temperature_ignored", test_gumbel_max_samples_the_softmax_law),
+    ("philox_key_not_bumped", test_philox_known_answer_vectors),
+    ("philox_multipliers_swapped", test_philox_known_answer_vectors),
 ])
 def test_mutation_is_caught(monkeypatch, name, pin):
     mutated(monkeypatch, name)
