@@ -288,6 +288,7 @@ def run_rounds(a, W, model, steps: int, warmup: int, headline: bool):
             .reshape(b, Bk, V)).cuda()
         samp_ws = B.sampling_workspace(b, Bk, V)
         out_tok = torch.empty(b, dtype=torch.int32, device="cuda")
+        logq = torch.empty(b * m, dtype=torch.float32, device="cuda")
     rnd = [0]
 
     def step():
@@ -297,9 +298,10 @@ def run_rounds(a, W, model, steps: int, warmup: int, headline: bool):
             # sample the candidates from the draft's laws, verify them against
             # the target's; the emitted token is written over the anchor
             model.draft_forward(cache, anchor, drafts, ws, logits=logits, dev_status=status)
-            B.sample_drafts(logits.view(b * m, V), T, 1234, rnd[0], drafts.view(-1), samp_ws)
+            B.sample_drafts(logits.view(b * m, V), T, 1234, rnd[0], drafts.view(-1), samp_ws,
+                            logq=logq)
             B.verify_sampled(drafts, logits, t_logits, T, 1234, rnd[0], acc, out_tok, samp_ws,
-                             anchor_out=anchor)
+                             anchor_out=anchor, draft_logq=logq)
             rnd[0] += 1
             return
         # the bonus token is written over the anchor: next round's anchor

@@ -119,7 +119,7 @@ def lib() -> ctypes.CDLL:
         L.dflash_sample_drafts_static.argtypes = [vp, i64, i32, i32, ctypes.c_float,
                                                   ctypes.c_uint64, i32, vp, vp, vp]
         L.dflash_verify_sampled.restype = i32
-        L.dflash_verify_sampled.argtypes = [vp, vp, vp, i32, i32, i32, ctypes.c_float,
+        L.dflash_verify_sampled.argtypes = [vp, vp, vp, vp, i32, i32, i32, ctypes.c_float,
                                             ctypes.c_uint64, i32, vp, vp, vp, vp, i64, vp]
         L.dflash_profiler_start.restype = i32
         L.dflash_profiler_start.argtypes = [i32, ctypes.c_uint32]
@@ -420,10 +420,14 @@ def sample_drafts_static(logits: torch.Tensor, temperature: float, seed: int, rn
 def verify_sampled(drafts: torch.Tensor, draft_logits: torch.Tensor,
                    target_logits: torch.Tensor, temperature: float, seed: int, rnd: int,
                    accept_len: torch.Tensor, out_token: torch.Tensor, ws: torch.Tensor,
-                   anchor_out: Optional[torch.Tensor] = None) -> None:
-    """drafts [b, B-1], draft logits [b, B-1, V], target logits [b, B, V]."""
+                   anchor_out: Optional[torch.Tensor] = None,
+                   draft_logq: Optional[torch.Tensor] = None) -> None:
+    """drafts [b, B-1], draft logits [b, B-1, V], target logits [b, B, V];
+    draft_logq [b, B-1] (optional): log q of the drawn candidates, as
+    sample_drafts returned it at this temperature."""
     b, Bk, vocab = target_logits.shape
-    _check(lib().dflash_verify_sampled(_ptr(drafts), _ptr(draft_logits), _ptr(target_logits), b,
+    _check(lib().dflash_verify_sampled(_ptr(drafts), _ptr(draft_logits), _ptr(draft_logq),
+                                       _ptr(target_logits), b,
                                        Bk, vocab, float(temperature), int(seed), int(rnd),
                                        _ptr(accept_len), _ptr(out_token), _ptr(anchor_out),
                                        _ptr(ws), ws.numel(), _stream()), "dflash_verify_sampled")

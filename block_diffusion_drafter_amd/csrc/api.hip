@@ -842,7 +842,8 @@ int32_t dflash_sample_drafts_static(const float* logits, int64_t row_stride, int
 }
 
 int32_t dflash_verify_sampled(const int32_t* drafts, const float* draft_logits,
-                              const float* target_logits, int32_t batch, int32_t block_size,
+                              const float* draft_logq, const float* target_logits,
+                              int32_t batch, int32_t block_size,
                               int32_t vocab, float temperature, uint64_t seed, int32_t round,
                               int32_t* accept_len, int32_t* out_token, int32_t* anchor_out,
                               void* ws, int64_t ws_bytes, void* stream) {
@@ -856,13 +857,16 @@ int32_t dflash_verify_sampled(const int32_t* drafts, const float* draft_logits,
   for (const void* q : ps)
     if (!al16(q)) return DFLASH_ERR_ALIGN;
   if (anchor_out && !al16(anchor_out)) return DFLASH_ERR_ALIGN;
+  if (draft_logq && !al16(draft_logq)) return DFLASH_ERR_ALIGN;
   if (ws_bytes < verify_ws_bytes(batch, block_size, vocab)) return DFLASH_ERR_WORKSPACE;
   hipStream_t st = (hipStream_t)stream;
-  // bytes: every target and draft row is read once for its normaliser, the
-  // emitted row twice more (stats, residual)
-  const double rows = (double)batch * block_size + (double)batch * (block_size - 1) + 2.0 * batch;
+  // bytes: every target row (and without log q every draft row) is read once
+  // for its normaliser, the emitted position's target and draft rows once more
+  const double rows = (double)batch * block_size +
+                      (draft_logq ? 0.0 : (double)batch * (block_size - 1)) + 2.0 * batch;
   prof_begin(DFLASH_K_SAMPLING, rows * vocab * 4, 0.0, st);
-  const hipError_t e = launch_verify_sampled(drafts, draft_logits, target_logits, batch, block_size,
+  const hipError_t e = launch_verify_sampled(drafts, draft_logits, draft_logq, target_logits,
+                                             batch, block_size,
                                              vocab, temperature, seed, round, accept_len,
                                              out_token, anchor_out, ws, st);
   prof_end(st);

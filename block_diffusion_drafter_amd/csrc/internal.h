@@ -284,7 +284,8 @@ hipError_t launch_sample_drafts(const float* logits, int64_t ld, int rows, int v
                                 uint64_t seed, int rnd, int32_t* tokens, float* logq, void* ws,
                                 hipStream_t st);
 hipError_t launch_verify_sampled(const int32_t* drafts, const float* draft_logits,
-                                 const float* target_logits, int batch, int block, int vocab,
+                                 const float* draft_logq, const float* target_logits, int batch,
+                                 int block, int vocab,
                                  float temp, uint64_t seed, int rnd, int32_t* accept_len,
                                  int32_t* out_token, int32_t* anchor_out, void* ws,
                                  hipStream_t st);

@@ -264,41 +264,57 @@ __global__ __launch_bounds__(kThreads) void verify_stats_kernel(const float* dra
   if (threadIdx.x == 0) part[(int64_t)r * nsplit + split] = SplitStat{0ull, lse.m, lse.s};
 }
 
-// Per row: log-sum-exp of logits / T from its split partials.
-__global__ void verify_lse_kernel(const SplitStat* part, int nsplit, int rows, float* lse) {
-  const int r = blockIdx.x * blockDim.x + threadIdx.x;
-  if (r >= rows) return;
+// Log-sum-exp of one row's logits / T from its split partials, merged in
+// split order.
+__device__ __forceinline__ float row_lse(const SplitStat* part, int64_t row, int nsplit) {
   Lse l;
-  for (int i = 0; i < nsplit; ++i) l.merge(part[(int64_t)r * nsplit + i].m, part[(int64_t)r * nsplit + i].s);
-  lse[r] = l.value();
+  for (int i = 0; i < nsplit; ++i) l.merge(part[row * nsplit + i].m, part[row * nsplit + i].s);
+  return l.value();
 }
 
-// Per sequence and split: the accept test of every position (eq. 6, one
-// thread per position) and the left-to-right scan for the first rejection,
-// repeated by every split of the sequence (identical inputs, identical
-// result); then the Gumbel-max partial over this split of the emitted law:
-// the residual [p - q]_+ at the first rejected position (eq. 7), with the
-// target law as fallback when the residual support is empty, or the target's
-// next law when every candidate survived (bonus).
+// Per sequence and split: the normalisers of the sequence's rows from the
+// split partials (target rows; draft rows too unless log q of the drawn
+// candidates is given, which recovers them as logit / T - log q), the accept
+// test of every position (eq. 6, one thread per position) and the
+// left-to-right scan for the first rejection, repeated by every split of the
+// sequence (identical inputs, identical result); then the Gumbel-max partial
+// over this split of the emitted law: the residual [p - q]_+ at the first
+// rejected position (eq. 7), with the target law as fallback when the
+// residual support is empty, or the target's next law when every candidate
+// survived (bonus).
 __global__ __launch_bounds__(kThreads) void verify_residual_kernel(
-    const int32_t* drafts, const float* draft_logits, const float* target_logits, int batch, int B,
-    int V, float inv_t, uint64_t seed, int rnd, const float* lse, int nsplit,
-    unsigned long long* keys, int32_t* accept_out) {
+    const int32_t* drafts, const float* draft_logits, const float* draft_logq,
+    const float* target_logits, int batch, int B, int V, float inv_t, uint64_t seed, int rnd,
+    const SplitStat* stats, int nsplit, unsigned long long* keys, int32_t* accept_out) {
   __shared__ unsigned long long shk[kThreads / 64];
   __shared__ int sh_ok[64];
+  __shared__ float sh_lsep[64], sh_lseq[64];
   __shared__ int sh_a;
   const int split = blockIdx.x, s = blockIdx.y;
-  const int m = B - 1;  // m <= 16 < kThreads
-  if ((int)threadIdx.x < m) {
+  const int m = B - 1;  // m + 1 <= 17 < kThreads
+  if ((int)threadIdx.x <= m) {
     const int i = threadIdx.x;
-    float u4[4];
-    uniforms4(seed, (uint32_t)(i >> 2), (uint32_t)s, (uint32_t)rnd, 1u, u4);
-    int y = drafts[(int64_t)s * m + i];
-    y = y < 0 ? 0 : (y >= V ? V - 1 : y);  // ids outside the vocabulary are clamped
-    const float lp = target_logits[((int64_t)s * B + i) * V + y] * inv_t - lse[s * B + i];
-    const float lq = draft_logits[((int64_t)s * m + i) * V + y] * inv_t - lse[batch * B + s * m + i];
-    const float alpha = fminf(1.f, expf(lp - lq));
-    sh_ok[i] = u4[i & 3] < alpha;
+    const float lse_p = row_lse(stats, (int64_t)s * B + i, nsplit);
+    sh_lsep[i] = lse_p;
+    if (i < m) {
+      float u4[4];
+      uniforms4(seed, (uint32_t)(i >> 2), (uint32_t)s, (uint32_t)rnd, 1u, u4);
+      int y = drafts[(int64_t)s * m + i];
+      y = y < 0 ? 0 : (y >= V ? V - 1 : y);  // ids outside the vocabulary are clamped
+      const float xq = draft_logits[((int64_t)s * m + i) * V + y] * inv_t;
+      float lq, lse_q;
+      if (draft_logq) {
+        lq = draft_logq[(int64_t)s * m + i];
+        lse_q = xq - lq;
+      } else {
+        lse_q = row_lse(stats, (int64_t)batch * B + (int64_t)s * m + i, nsplit);
+        lq = xq - lse_q;
+      }
+      sh_lseq[i] = lse_q;
+      const float lp = target_logits[((int64_t)s * B + i) * V + y] * inv_t - lse_p;
+      const float alpha = fminf(1.f, expf(lp - lq));
+      sh_ok[i] = u4[i & 3] < alpha;
+    }
   }
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -309,8 +325,8 @@ __global__ __launch_bounds__(kThreads) void verify_residual_kernel(
   }
   __syncthreads();
   const int a = sh_a;
-  const float lse_p = lse[s * B + a];
-  const float lse_q = a < m ? lse[batch * B + s * m + a] : 0.f;
+  const float lse_p = sh_lsep[a];
+  const float lse_q = a < m ? sh_lseq[a] : 0.f;
   const float* lp_row = target_logits + ((int64_t)s * B + a) * V;
   const float* lq_row = a < m ? draft_logits + ((int64_t)s * m + a) * V : nullptr;
   const uint32_t grow = (uint32_t)(s * B + a);
@@ -382,7 +398,7 @@ int64_t sample_ws_bytes(int rows, int vocab) {
 
 namespace {
 struct VerifyWs {
-  int64_t stats, keys, lse, acc, total;
+  int64_t stats, keys, acc, total;
 };
 VerifyWs verify_ws(int batch, int block, int vocab) {
   const int64_t ns = sampling_splits(vocab);
@@ -391,8 +407,7 @@ VerifyWs verify_ws(int batch, int block, int vocab) {
   VerifyWs w{};
   w.stats = 0;
   w.keys = al(rows * ns * (int64_t)sizeof(SplitStat));
-  w.lse = w.keys + al((int64_t)batch * ns * 16);
-  w.acc = w.lse + al(rows * 4);
+  w.acc = w.keys + al((int64_t)batch * ns * 16);
   w.total = w.acc + al((int64_t)batch * 4);
   return w;
 }
@@ -417,31 +432,27 @@ hipError_t launch_sample_drafts(const float* logits, int64_t ld, int rows, int v
 }
 
 hipError_t launch_verify_sampled(const int32_t* drafts, const float* draft_logits,
-                                 const float* target_logits, int batch, int block, int vocab,
-                                 float temp, uint64_t seed, int rnd, int32_t* accept_len,
-                                 int32_t* out_token, int32_t* anchor_out, void* ws,
-                                 hipStream_t st) {
+                                 const float* draft_logq, const float* target_logits, int batch,
+                                 int block, int vocab, float temp, uint64_t seed, int rnd,
+                                 int32_t* accept_len, int32_t* out_token, int32_t* anchor_out,
+                                 void* ws, hipStream_t st) {
   if (batch <= 0) return hipSuccess;
   const int ns = sampling_splits(vocab);
   const float inv_t = 1.0f / temp;
   char* w = reinterpret_cast<char*>(ws);
   const VerifyWs L = verify_ws(batch, block, vocab);
-  const int64_t stats_rows = (int64_t)batch * block + (int64_t)batch * (block - 1);
+  // target rows, then (without log q) the draft rows
+  const int64_t stats_rows = (int64_t)batch * block + (draft_logq ? 0 : (int64_t)batch * (block - 1));
   SplitStat* stats = reinterpret_cast<SplitStat*>(w + L.stats);
   unsigned long long* keys = reinterpret_cast<unsigned long long*>(w + L.keys);
-  float* lse = reinterpret_cast<float*>(w + L.lse);
   int32_t* acc = reinterpret_cast<int32_t*>(w + L.acc);
   hipLaunchKernelGGL(verify_stats_kernel, dim3(ns, (unsigned)stats_rows), dim3(kThreads), 0, st,
                      draft_logits, target_logits, batch, block, vocab, inv_t, stats, ns);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(verify_lse_kernel, dim3((unsigned)((stats_rows + 63) / 64)), dim3(64), 0, st,
-                     stats, ns, (int)stats_rows, lse);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(verify_residual_kernel, dim3(ns, batch), dim3(kThreads), 0, st, drafts,
-                     draft_logits, target_logits, batch, block, vocab, inv_t, seed, rnd, lse, ns,
-                     keys, acc);
+                     draft_logits, draft_logq, target_logits, batch, block, vocab, inv_t, seed,
+                     rnd, stats, ns, keys, acc);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(verify_finish_kernel, dim3((batch + 63) / 64), dim3(64), 0, st, keys, ns,

@@ -321,7 +321,12 @@ int32_t dflash_accept(const int32_t *draft_tokens, const int32_t *target_tokens,
  * all B-1 are accepted, the bonus token drawn from the target's law at
  * position B-1. anchor_out (optional) receives out_token (the next anchor).
  * drafts: int32 [batch, B-1]; draft_logits: fp32 [batch, B-1, vocab] (the
- * logits the candidates were drawn from); target_logits: fp32
+ * logits the candidates were drawn from); draft_logq (optional, may be null):
+ * fp32 [batch, B-1], log q_i(drafts[s][i]) as dflash_sample_drafts returned
+ * it for these rows at this temperature -- when given, each draft row's
+ * normaliser is recovered from it (logit / T - log q of the drawn token)
+ * instead of by a pass over the draft rows, which halves the bytes read;
+ * target_logits: fp32
  * [batch, B, vocab] (the target's logits at the B-1 candidate positions and
  * the position after them). round separates the random numbers of
  * successive rounds. Candidate ids outside [0, vocab) are clamped.
@@ -351,7 +356,8 @@ int32_t dflash_sample_drafts_static(const float *logits, int64_t row_stride, int
                                     int32_t vocab, float temperature, uint64_t seed,
                                     int32_t round, int32_t *tokens, float *logq, void *stream);
 int32_t dflash_verify_sampled(const int32_t *drafts, const float *draft_logits,
-                              const float *target_logits, int32_t batch, int32_t block_size,
+                              const float *draft_logq, const float *target_logits,
+                              int32_t batch, int32_t block_size,
                               int32_t vocab, float temperature, uint64_t seed, int32_t round,
                               int32_t *accept_len, int32_t *out_token, int32_t *anchor_out,
                               void *ws, int64_t ws_bytes, void *stream);

@@ -221,14 +221,16 @@ def test_sampling_calls_reject_bad_arguments_before_launching():
     assert samp(logits=None) == -1
     assert samp(tokens=FAKE + 4) == -4
     assert samp(wsb=16) == -5
-    ver = lambda block=16, T=1.0, drafts=FAKE, ws=FAKE, wsb=need, batch=2: lib.dflash_verify_sampled(
-        drafts, FAKE, FAKE, batch, block, 1000, T, 1, 0, FAKE, FAKE, None, ws, wsb, None)
+    ver = lambda block=16, T=1.0, drafts=FAKE, ws=FAKE, wsb=need, batch=2, logq=None: \
+        lib.dflash_verify_sampled(drafts, FAKE, logq, FAKE, batch, block, 1000, T, 1, 0, FAKE,
+                                  FAKE, None, ws, wsb, None)
     assert ver(block=1) == -2
     assert ver(block=18) == -2
     assert ver(T=-1.0) == -2
     assert ver(batch=0, drafts=None) == 0
     assert ver(drafts=None) == -1
     assert ver(ws=FAKE + 8) == -4
+    assert ver(logq=FAKE + 4) == -4
     assert ver(wsb=need // 4) == -5
 
 

@@ -60,15 +60,16 @@ def test_gpu_sample_drafts_matches_oracle(rows, V, T):
     log(f"  tokens bit-exact on {int(ok.sum())}/{rows} confident rows")
 
 
-def run_verify(drafts, dl, tl, T, seed, rnd, anchor=False):
+def run_verify(drafts, dl, tl, T, seed, rnd, anchor=False, logq=None):
     b, m = drafts.shape
     V = dl.shape[-1]
     acc = torch.full((b,), -1, dtype=torch.int32, device="cuda")
     out = torch.full((b,), -1, dtype=torch.int32, device="cuda")
     anc = torch.full((b,), -1, dtype=torch.int32, device="cuda") if anchor else None
     ws = B.sampling_workspace(b, m + 1, V)
+    lq = None if logq is None else torch.from_numpy(logq.astype(np.float32)).cuda()
     B.verify_sampled(torch.from_numpy(drafts.astype(np.int32)).cuda(), torch.from_numpy(dl).cuda(),
-                     torch.from_numpy(tl).cuda(), T, seed, rnd, acc, out, ws, anc)
+                     torch.from_numpy(tl).cuda(), T, seed, rnd, acc, out, ws, anc, draft_logq=lq)
     torch.cuda.synchronize()
     res = (acc.cpu().numpy(), out.cpu().numpy())
     if anchor:
@@ -76,14 +77,16 @@ def run_verify(drafts, dl, tl, T, seed, rnd, anchor=False):
     return res
 
 
+@pytest.mark.parametrize("with_logq", [False, True])
 @pytest.mark.parametrize("b,Bk,V,T,mode", [
     (16, 16, 151936, 1.0, "near"),
     (24, 16, 1000, 0.8, "near"),
     (12, 8, 500, 1.2, "far"),
     (6, 16, 300, 1.0, "equal"),
 ])
-def test_gpu_verify_sampled_matches_oracle(b, Bk, V, T, mode):
-    log(f"case: verify_sampled batch {b} block {Bk} vocab {V} T {T} ({mode})")
+def test_gpu_verify_sampled_matches_oracle(b, Bk, V, T, mode, with_logq):
+    log(f"case: verify_sampled batch {b} block {Bk} vocab {V} T {T} ({mode}), "
+        f"draft log q {'given' if with_logq else 'not given'}")
     m = Bk - 1
     dl = logits((b, m, V), 31, f"vd{V}{mode}", 2.0)
     if mode == "near":    # target close to the draft: long accepted prefixes
@@ -93,9 +96,13 @@ def test_gpu_verify_sampled_matches_oracle(b, Bk, V, T, mode):
         tl = logits((b, Bk, V), 34, f"vf{V}", 2.0)
     else:                 # p == q: every candidate is accepted, bonus from row B-1
         tl = np.concatenate([dl, logits((b, 1, V), 35, f"ve{V}", 2.0)], axis=1)
-    drafts = S.sample_drafts(dl.reshape(b * m, V), T, seed=77, rnd=2).tokens.reshape(b, m)
+    drawn = S.sample_drafts(dl.reshape(b * m, V), T, seed=77, rnd=2)
+    drafts = drawn.tokens.reshape(b, m)
     ref = S.verify(drafts, dl, tl, T, seed=78, rnd=2)
-    acc, out = run_verify(drafts, dl, tl, T, 78, 2, anchor=True)
+    # log q of the drawn candidates, as the drafting call returns it (here the
+    # oracle's, rounded to fp32)
+    acc, out = run_verify(drafts, dl, tl, T, 78, 2, anchor=True,
+                          logq=drawn.logq.reshape(b, m) if with_logq else None)
     assert ((acc >= 0) & (acc <= m)).all() and ((out >= 0) & (out < V)).all()
     if mode == "equal":
         assert (acc == m).all() and (ref.accept_len == m).all()
