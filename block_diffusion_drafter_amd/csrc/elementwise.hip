@@ -354,15 +354,6 @@ struct RopeLane {
   }
 };
 
-// Pair c of a V head row at position pos (V is stored in 32-position blocks,
-// channel-major inside a block).
-template <typename T, int HD>
-__device__ __forceinline__ void store_v(T* vbase, int pos, int c, float x0, float x1) {
-  T* blk = vbase + (size_t)(pos / kKeyBlock) * HD * kKeyBlock + (pos % kKeyBlock);
-  blk[(size_t)c * kKeyBlock] = from_f32<T>(x0);
-  blk[(size_t)(c + HD / 2) * kKeyBlock] = from_f32<T>(x1);
-}
-
 // Heads (or append columns) per workgroup: 4 waves x IT iterations x
 // RopeLane::HPW heads per iteration. A wave loads all its heads' pairs
 // first, then normalises and stores them: one memory latency per wave. Few
@@ -371,16 +362,70 @@ __device__ __forceinline__ void store_v(T* vbase, int pos, int c, float x0, floa
 template <int HD, int IT>
 __host__ __device__ constexpr int nr_heads_per_wg() { return 4 * IT * (64 / (HD / 2)); }
 
-// Forward mode: grid (batch * 16 block slots, head groups); workgroup
-// (slot, y) takes heads y * nr_heads_per_wg + (it * 4 + wave) * HPW + sub of
-// the row's Hq + 2*Hkv. Slots i >= block only zero-fill the padded Q rows.
+// V heads of the forward mode: the 16 workgroups of sequence s (slots
+// s*16 .. s*16+15, last grid row) split its Hkv*HD value columns; each copies
+// its columns of the block's rows through LDS (row-wise loads) and writes
+// them to the channel-major cache blocks a column at a time, four threads per
+// column, each with four consecutive positions (one 32-byte run per column
+// instead of one 2-byte store per channel and position).
+constexpr int kNrVCols = 128;  // columns a workgroup stages at a time
+template <typename T, int HD>
+__device__ __forceinline__ void nr_fwd_values(const NormRopeArgs& p, int s, int part) {
+  __shared__ float tile[16][kNrVCols + 1];
+  const int Hq = p.n_heads, Hkv = p.n_kv_heads;
+  const int total = Hkv * HD, per = (total + 15) / 16;
+  const int col_lo = part * per, col_hi = min(total, col_lo + per);
+  int cl = p.ctx_len[s];
+  cl = cl < 0 ? 0 : cl;
+  const float* src = p.src + (int64_t)s * p.block * p.src_stride + (int64_t)(Hq + Hkv) * HD;
+  for (int c0 = col_lo; c0 < col_hi; c0 += kNrVCols) {
+    const int nc = min(kNrVCols, col_hi - c0);
+    if (c0 > col_lo) __syncthreads();  // the previous chunk's reads are done
+    // Every load of the chunk in flight at once (16 rows x 128 columns over
+    // the 256 threads: up to 8 each), then into LDS.
+    constexpr int kPer = 16 * kNrVCols / 256;
+    float v[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int idx = threadIdx.x + 256 * u, r = idx / nc, cc = idx - r * nc;
+      v[u] = idx < 16 * nc && r < p.block ? src[(int64_t)r * p.src_stride + c0 + cc] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int idx = threadIdx.x + 256 * u, r = idx / nc, cc = idx - r * nc;
+      if (idx < 16 * nc) tile[r][cc] = v[u];
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < 4 * nc; idx += blockDim.x) {
+      const int cc = idx >> 2, q = idx & 3, col = c0 + cc;
+      const int g = col / HD, ch = col - g * HD;
+      T* vb = reinterpret_cast<T*>(p.v_cache) + (size_t)(s * Hkv + g) * p.cap * HD;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * q + e, pos = cl + r;
+        if (r < p.block && pos < p.cap)
+          vb[(size_t)(pos / kKeyBlock) * HD * kKeyBlock + (size_t)ch * kKeyBlock + pos % kKeyBlock] =
+              from_f32<T>(tile[r][cc]);
+      }
+    }
+  }
+}
+
+// Forward mode: grid (batch * 16 block slots, Q/K head groups + 1); workgroup
+// (slot, y) takes Q/K heads y * nr_heads_per_wg + (it * 4 + wave) * HPW + sub
+// of the row's Hq + Hkv; the last grid row writes the V heads
+// (nr_fwd_values). Slots i >= block only zero-fill the padded Q rows.
 template <typename T, int HD, int IT>
 __global__ __launch_bounds__(256) void norm_rope_fwd_kernel(NormRopeArgs p) {
   using RL = RopeLane<HD>;
   const int slot = blockIdx.x, s = slot / 16, i = slot % 16;
+  if (blockIdx.y == gridDim.y - 1) {
+    nr_fwd_values<T, HD>(p, s, i);
+    return;
+  }
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int sub = lane / RL::PAIRS, c = lane % RL::PAIRS;
-  const int Hq = p.n_heads, Hkv = p.n_kv_heads, NH = Hq + 2 * Hkv;
+  const int Hq = p.n_heads, Hkv = p.n_kv_heads, NQK = Hq + Hkv;
   const int hbase = blockIdx.y * nr_heads_per_wg<HD, IT>() + wave * RL::HPW + sub;
   if (i >= p.block) {
 #pragma unroll
@@ -399,7 +444,7 @@ __global__ __launch_bounds__(256) void norm_rope_fwd_kernel(NormRopeArgs p) {
   float x0[IT], x1[IT];
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
-    const int hc = min(hbase + it * 4 * RL::HPW, NH - 1);
+    const int hc = min(hbase + it * 4 * RL::HPW, NQK - 1);
     x0[it] = src[hc * HD + c];
     x1[it] = src[hc * HD + c + RL::PAIRS];
   }
@@ -419,28 +464,21 @@ __global__ __launch_bounds__(256) void norm_rope_fwd_kernel(NormRopeArgs p) {
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
     const int h = hbase + it * 4 * RL::HPW;
-    const int hc = min(h, NH - 1);
-    const bool is_q = hc < Hq, is_v = hc >= Hq + Hkv;
-    float o0 = x0[it], o1 = x1[it];
-    if (!is_v)
-      norm_rope_pair<HD>(x0[it], x1[it], is_q ? qg0 : kg0, is_q ? qg1 : kg1, p.eps,
-                         make_float2(rope.c, rope.s), o0, o1);
-    if (h >= NH) continue;
+    const int hc = min(h, NQK - 1);
+    const bool is_q = hc < Hq;
+    float o0, o1;
+    norm_rope_pair<HD>(x0[it], x1[it], is_q ? qg0 : kg0, is_q ? qg1 : kg1, p.eps,
+                       make_float2(rope.c, rope.s), o0, o1);
+    if (h >= NQK) continue;
     if (is_q) {
       T* qo = reinterpret_cast<T*>(p.q_out) + (((size_t)s * Hq + h) * 16 + i) * HD;
       qo[c] = from_f32<T>(o0);
       qo[c + RL::PAIRS] = from_f32<T>(o1);
     } else if (in_cap) {
-      if (is_v) {
-        const int g = h - Hq - Hkv;
-        store_v<T, HD>(reinterpret_cast<T*>(p.v_cache) + (size_t)(s * Hkv + g) * p.cap * HD, pos,
-                       c, o0, o1);
-      } else {
-        const int g = h - Hq;
-        T* kr = reinterpret_cast<T*>(p.k_cache) + ((size_t)(s * Hkv + g) * p.cap + pos) * HD;
-        kr[c] = from_f32<T>(o0);
-        kr[c + RL::PAIRS] = from_f32<T>(o1);
-      }
+      const int g = h - Hq;
+      T* kr = reinterpret_cast<T*>(p.k_cache) + ((size_t)(s * Hkv + g) * p.cap + pos) * HD;
+      kr[c] = from_f32<T>(o0);
+      kr[c + RL::PAIRS] = from_f32<T>(o1);
     }
   }
 }
@@ -661,6 +699,7 @@ __global__ __launch_bounds__(256) void norm_rope_append_kernel(NormRopeArgs p) {
   }
 }
 
+// Grid: rows x (Q/K head groups + one row for the V heads).
 template <int IT>
 static hipError_t launch_nr_it(int dtype, const NormRopeArgs& a, int rows, int n_cols,
                                hipStream_t st) {
@@ -668,7 +707,7 @@ static hipError_t launch_nr_it(int dtype, const NormRopeArgs& a, int rows, int n
   const dim3 blk(256);
 #define DF_NR(K, T, HD)                                                                     \
   hipLaunchKernelGGL((K<T, HD, IT>), dim3(rows, (n_cols + nr_heads_per_wg<HD, IT>() - 1) / \
-                                                   nr_heads_per_wg<HD, IT>()),              \
+                                                   nr_heads_per_wg<HD, IT>() + 1),          \
                      blk, 0, st, a)
   if (a.head_dim == 128) {
     if (bf) DF_NR(norm_rope_fwd_kernel, bf16, 128);
@@ -718,7 +757,7 @@ static NormRopeArgs with_inv_freq(const NormRopeArgs& a0) {
 }
 
 hipError_t launch_norm_rope_forward(int dtype, const NormRopeArgs& a, hipStream_t st) {
-  return launch_nr_fwd(dtype, with_inv_freq(a), a.batch * 16, a.n_heads + 2 * a.n_kv_heads, st);
+  return launch_nr_fwd(dtype, with_inv_freq(a), a.batch * 16, a.n_heads + a.n_kv_heads, st);
 }
 
 // Heads per workgroup: 2 while the tiles are few (more workgroups in
