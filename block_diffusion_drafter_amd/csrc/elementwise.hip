@@ -825,12 +825,59 @@ __global__ __launch_bounds__(1024) void argmax_rows_kernel(const unsigned long l
   }
 }
 
+// The same for a sequence's rows together: one workgroup per sequence, wave
+// w reduces row s*m + w (m <= 16), and the workgroup applies the accept rule
+// to the drafts it just computed (no cross-workgroup handoff). For rows of
+// few keys (the MFMA LM head's column blocks); rows of thousands of keys
+// (the weight-streaming LM head's tiles) keep a workgroup each.
+__global__ __launch_bounds__(1024) void argmax_seq_kernel(const unsigned long long* amax,
+                                                          int64_t stride, int n_cols, int block,
+                                                          int32_t* drafts, const int32_t* targets,
+                                                          int32_t* accept_len, int32_t* bonus) {
+  __shared__ int32_t tok[16];
+  const int s = blockIdx.x, m = block - 1;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (wave < m) {
+    const int64_t row = (int64_t)s * m + wave;
+    const unsigned long long* keys = amax + row * stride;
+    unsigned long long best = 0ull;
+#pragma unroll 4
+    for (int c = lane; c < n_cols; c += 64) {
+      const unsigned long long k = keys[c];
+      best = k > best ? k : best;
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const unsigned long long other = __shfl_xor(best, o);
+      best = other > best ? other : best;
+    }
+    if (lane == 0) {
+      const int32_t t = (int32_t)argmax_index(best);
+      drafts[row] = t;
+      tok[wave] = t;
+    }
+  }
+  __syncthreads();
+  if (targets && threadIdx.x == 0) {
+    const int32_t* t = targets + (int64_t)s * block;
+    int a = 0;
+    while (a < m && tok[a] == t[a]) ++a;
+    accept_len[s] = a;
+    bonus[s] = t[a];
+  }
+}
+
 hipError_t launch_argmax_accept(const unsigned long long* amax, int64_t stride, int n_cols,
                                 int batch, int block, int32_t* drafts, const int32_t* targets,
                                 int32_t* accept_len, int32_t* bonus, int32_t* arrivals,
                                 hipStream_t st) {
   if (batch <= 0 || block < 2 || block > 17) return block == 1 ? hipSuccess : hipErrorInvalidValue;
   if (targets && !arrivals) return hipErrorInvalidValue;
+  if (n_cols <= 2048) {
+    hipLaunchKernelGGL(argmax_seq_kernel, dim3(batch), dim3(1024), 0, st, amax, stride, n_cols,
+                       block, drafts, targets, accept_len, bonus);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(argmax_rows_kernel, dim3(batch * (block - 1)), dim3(1024), 0, st, amax, stride,
                      n_cols, block, drafts, targets, accept_len, bonus, arrivals);
   return hipGetLastError();
