@@ -605,21 +605,43 @@ __global__ __launch_bounds__(512) void attn_combine_kernel(AttnArgs p) {
   const int t = threadIdx.x, j = t >> 6, q = t & 15, c = (t >> 4) & 3;
   if (q >= p.block) return;
   const size_t e0 = part_entry(p, g, w0, s);  // segment k is entry e0 + k
-  float M = -INFINITY;
-#pragma unroll 8
-  for (int k = 0; k < nch; ++k) M = fmaxf(M, p.part_ml[(((e0 + k) * G + j) * 16 + q) * 2]);
   const int ch0 = 4 * CPL * slice + CPL * c;
-  float L = 0.f, o[CPL];
+  // Segments in groups of four: every load of a group (each segment's max,
+  // sum and partial channels) goes out at once, then the group is merged
+  // into the running (max, sum, output), rescaled to the new max.
+  constexpr int KG = 4;
+  float M = -INFINITY, L = 0.f, o[CPL];
 #pragma unroll
   for (int i = 0; i < CPL; ++i) o[i] = 0.f;
-#pragma unroll 4
-  for (int k = 0; k < nch; ++k) {
-    const size_t item = (e0 + k) * G + j;
-    const float wk = exp2f(p.part_ml[(item * 16 + q) * 2] - M);
-    L += p.part_ml[(item * 16 + q) * 2 + 1] * wk;
-    const float* po = p.part_o + (item * HD + ch0) * 16 + q;
+  for (int k0 = 0; k0 < nch; k0 += KG) {
+    float mk[KG], lk[KG], ok[KG][CPL];
 #pragma unroll
-    for (int i = 0; i < CPL; ++i) o[i] += po[i * 16] * wk;
+    for (int u = 0; u < KG; ++u) {
+      const bool ok_k = k0 + u < nch;
+      const size_t item = (e0 + min(k0 + u, nch - 1)) * G + j;
+      const float* po = p.part_o + (item * HD + ch0) * 16 + q;
+      mk[u] = ok_k ? p.part_ml[(item * 16 + q) * 2] : -INFINITY;
+      lk[u] = ok_k ? p.part_ml[(item * 16 + q) * 2 + 1] : 0.f;
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) ok[u][i] = ok_k ? po[i * 16] : 0.f;
+    }
+    float Mn = M;
+#pragma unroll
+    for (int u = 0; u < KG; ++u) Mn = fmaxf(Mn, mk[u]);
+    // A sequence whose queries saw no key yet (sliding window) keeps -inf.
+    const float ref = Mn == -INFINITY ? 0.f : Mn;
+    const float a = exp2f(M - ref);
+    L *= a;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) o[i] *= a;
+#pragma unroll
+    for (int u = 0; u < KG; ++u) {
+      const float wk = exp2f(mk[u] - ref);
+      L += lk[u] * wk;
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) o[i] += ok[u][i] * wk;
+    }
+    M = Mn;
   }
   const float inv = 1.0f / L;
   T* out = reinterpret_cast<T*>(p.out);
