@@ -60,16 +60,17 @@ __device__ __forceinline__ void uniforms4(uint64_t seed, uint32_t q, uint32_t ro
   for (int w = 0; w < 4; ++w) u[w] = ((float)(c[w] >> 9) + 0.5f) * 0x1p-23f;
 }
 
-// This thread's logits of a split: step i holds elements v0 + 4*kThreads*i
-// .. +3 (v0 = split*kSplit + 4*threadIdx.x), -inf past V; every load is
-// issued before any value is used.
-__device__ __forceinline__ void load_split(const float* l, int V, int split, float x[kIt][4]) {
-  const int v0 = split * kSplit + 4 * (int)threadIdx.x;
+// This thread's logits of a split of IT*4*kThreads logits: step i holds
+// elements v0 + 4*kThreads*i .. +3 (v0 = split*IT*4*kThreads +
+// 4*threadIdx.x), -inf past V; every load is issued before any value is used.
+template <int IT = kIt>
+__device__ __forceinline__ void load_split(const float* l, int V, int split, float x[IT][4]) {
+  const int v0 = split * (IT * 4 * kThreads) + 4 * (int)threadIdx.x;
   if ((V & 3) == 0 && (reinterpret_cast<uintptr_t>(l) & 15) == 0) {
     // whole 16-byte groups: v < V implies v + 3 < V
     const float4* l4 = reinterpret_cast<const float4*>(l);
 #pragma unroll
-    for (int i = 0; i < kIt; ++i) {
+    for (int i = 0; i < IT; ++i) {
       const int v = v0 + 4 * kThreads * i;
       float4 t = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
       if (v < V) t = l4[v >> 2];
@@ -80,7 +81,7 @@ __device__ __forceinline__ void load_split(const float* l, int V, int split, flo
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < kIt; ++i)
+    for (int i = 0; i < IT; ++i)
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
         const int v = v0 + 4 * kThreads * i + w;
@@ -234,10 +235,18 @@ __global__ void sample_finish_kernel(const float* logits, int64_t ld, float inv_
   if (row >= rows) return;
   unsigned long long key = 0ull;
   Lse lse;
-  for (int i = 0; i < nsplit; ++i) {
-    const SplitStat& p = part[(int64_t)row * nsplit + i];
-    key = p.key > key ? p.key : key;
-    lse.merge(p.m, p.s);
+  // Splits in groups of 8, every load of a group before its merges (in
+  // split order).
+  for (int i0 = 0; i0 < nsplit; i0 += 8) {
+    SplitStat q[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      q[u] = i0 + u < nsplit ? part[(int64_t)row * nsplit + i0 + u] : SplitStat{0ull, -INFINITY, 0.f};
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      key = q[u].key > key ? q[u].key : key;
+      lse.merge(q[u].m, q[u].s);
+    }
   }
   const int tok = (int)argmax_index(key);
   tokens[row] = tok;
@@ -268,7 +277,17 @@ __global__ __launch_bounds__(kThreads) void verify_stats_kernel(const float* dra
 // split order.
 __device__ __forceinline__ float row_lse(const SplitStat* part, int64_t row, int nsplit) {
   Lse l;
-  for (int i = 0; i < nsplit; ++i) l.merge(part[row * nsplit + i].m, part[row * nsplit + i].s);
+  for (int i0 = 0; i0 < nsplit; i0 += 8) {  // groups of 8: loads first
+    float m[8], sm[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const bool ok = i0 + u < nsplit;
+      m[u] = ok ? part[row * nsplit + i0 + u].m : -INFINITY;
+      sm[u] = ok ? part[row * nsplit + i0 + u].s : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) l.merge(m[u], sm[u]);
+  }
   return l.value();
 }
 
@@ -282,10 +301,13 @@ __device__ __forceinline__ float row_lse(const SplitStat* part, int64_t row, int
 // rejected position (eq. 7), with the target law as fallback when the
 // residual support is empty, or the target's next law when every candidate
 // survived (bonus).
+template <int IT>
 __global__ __launch_bounds__(kThreads) void verify_residual_kernel(
     const int32_t* drafts, const float* draft_logits, const float* draft_logq,
     const float* target_logits, int batch, int B, int V, float inv_t, uint64_t seed, int rnd,
     const SplitStat* stats, int nsplit, unsigned long long* keys, int32_t* accept_out) {
+  // nsplit: splits of the statistics (kSplit logits each); this kernel's own
+  // splits over the emitted row are IT*4*kThreads logits each (gridDim.x).
   __shared__ unsigned long long shk[kThreads / 64];
   __shared__ int sh_ok[64];
   __shared__ float sh_lsep[64], sh_lseq[64];
@@ -330,13 +352,13 @@ __global__ __launch_bounds__(kThreads) void verify_residual_kernel(
   const float* lp_row = target_logits + ((int64_t)s * B + a) * V;
   const float* lq_row = a < m ? draft_logits + ((int64_t)s * m + a) * V : nullptr;
   const uint32_t grow = (uint32_t)(s * B + a);
-  float xp[kIt][4], xq[kIt][4];
-  load_split(lp_row, V, split, xp);
-  if (lq_row) load_split(lq_row, V, split, xq);
+  float xp[IT][4], xq[IT][4];
+  load_split<IT>(lp_row, V, split, xp);
+  if (lq_row) load_split<IT>(lq_row, V, split, xq);
   unsigned long long kres = 0ull, kfb = 0ull;
-  const int v0 = split * kSplit + 4 * (int)threadIdx.x;
+  const int v0 = split * (IT * 4 * kThreads) + 4 * (int)threadIdx.x;
 #pragma unroll
-  for (int i = 0; i < kIt; ++i) {
+  for (int i = 0; i < IT; ++i) {
     const int v = v0 + 4 * kThreads * i;
     if (v >= V) break;
     float u[4];
@@ -361,8 +383,8 @@ __global__ __launch_bounds__(kThreads) void verify_residual_kernel(
   kres = block_max_key(kres, shk);
   kfb = block_max_key(kfb, shk);
   if (threadIdx.x == 0) {
-    keys[((int64_t)s * nsplit + split) * 2 + 0] = kres;
-    keys[((int64_t)s * nsplit + split) * 2 + 1] = kfb;
+    keys[((int64_t)s * gridDim.x + split) * 2 + 0] = kres;
+    keys[((int64_t)s * gridDim.x + split) * 2 + 1] = kfb;
   }
 }
 
@@ -372,11 +394,19 @@ __global__ void verify_finish_kernel(const unsigned long long* keys, int nsplit,
   const int s = blockIdx.x * blockDim.x + threadIdx.x;
   if (s >= batch) return;
   unsigned long long kr = 0ull, kf = 0ull;
-  for (int i = 0; i < nsplit; ++i) {
-    const unsigned long long a = keys[((int64_t)s * nsplit + i) * 2 + 0];
-    const unsigned long long b = keys[((int64_t)s * nsplit + i) * 2 + 1];
-    kr = a > kr ? a : kr;
-    kf = b > kf ? b : kf;
+  for (int i0 = 0; i0 < nsplit; i0 += 8) {  // groups of 8: loads first
+    unsigned long long a[8], b[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const bool ok = i0 + u < nsplit;
+      a[u] = ok ? keys[((int64_t)s * nsplit + i0 + u) * 2 + 0] : 0ull;
+      b[u] = ok ? keys[((int64_t)s * nsplit + i0 + u) * 2 + 1] : 0ull;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      kr = a[u] > kr ? a[u] : kr;
+      kf = b[u] > kf ? b[u] : kf;
+    }
   }
   const int a = accept_in[s];
   // residual draw when the rejected position's residual support is non-empty,
@@ -391,6 +421,14 @@ __global__ void verify_finish_kernel(const unsigned long long* keys, int nsplit,
 }  // namespace
 
 int sampling_splits(int vocab) { return (vocab + kSplit - 1) / kSplit; }
+
+namespace {
+// Splits of the emitted row in the residual pass at IT*4*kThreads logits each.
+int residual_splits(int vocab, int it) {
+  const int n = it * 4 * kThreads;
+  return (vocab + n - 1) / n;
+}
+}  // namespace
 
 int64_t sample_ws_bytes(int rows, int vocab) {
   return (int64_t)rows * sampling_splits(vocab) * (int64_t)sizeof(SplitStat);
@@ -407,7 +445,7 @@ VerifyWs verify_ws(int batch, int block, int vocab) {
   VerifyWs w{};
   w.stats = 0;
   w.keys = al(rows * ns * (int64_t)sizeof(SplitStat));
-  w.acc = w.keys + al((int64_t)batch * ns * 16);
+  w.acc = w.keys + al((int64_t)batch * residual_splits(vocab, 1) * 16);
   w.total = w.acc + al((int64_t)batch * 4);
   return w;
 }
@@ -450,12 +488,22 @@ hipError_t launch_verify_sampled(const int32_t* drafts, const float* draft_logit
                      draft_logits, target_logits, batch, block, vocab, inv_t, stats, ns);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(verify_residual_kernel, dim3(ns, batch), dim3(kThreads), 0, st, drafts,
-                     draft_logits, draft_logq, target_logits, batch, block, vocab, inv_t, seed,
-                     rnd, stats, ns, keys, acc);
+  // The residual pass covers one row per sequence: few sequences take finer
+  // splits (2048 or 1024 logits) so that the pass still spreads over the CUs.
+  const int it = (int64_t)batch * residual_splits(vocab, 8) >= 256 ? 8
+                 : (int64_t)batch * residual_splits(vocab, 2) >= 256 ? 2 : 1;
+  const int nres = residual_splits(vocab, it);
+#define DF_RES(I)                                                                                \
+  hipLaunchKernelGGL(verify_residual_kernel<I>, dim3(nres, batch), dim3(kThreads), 0, st, drafts, \
+                     draft_logits, draft_logq, target_logits, batch, block, vocab, inv_t, seed,   \
+                     rnd, stats, ns, keys, acc)
+  if (it == 8) DF_RES(8);
+  else if (it == 2) DF_RES(2);
+  else DF_RES(1);
+#undef DF_RES
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(verify_finish_kernel, dim3((batch + 63) / 64), dim3(64), 0, st, keys, ns,
+  hipLaunchKernelGGL(verify_finish_kernel, dim3((batch + 63) / 64), dim3(64), 0, st, keys, nres,
                      batch, block, acc, accept_len, out_token, anchor_out);
   return hipGetLastError();
 }
