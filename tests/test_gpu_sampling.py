@@ -79,7 +79,9 @@ def run_verify(drafts, dl, tl, T, seed, rnd, anchor=False, logq=None):
 
 @pytest.mark.parametrize("with_logq", [False, True])
 @pytest.mark.parametrize("b,Bk,V,T,mode", [
-    (16, 16, 151936, 1.0, "near"),
+    (16, 16, 151936, 1.0, "near"),   # residual pass in 8192-logit splits
+    (4, 16, 151936, 1.0, "far"),     # 2048-logit splits (few sequences)
+    (1, 16, 151936, 0.9, "far"),     # 1024-logit splits
     (24, 16, 1000, 0.8, "near"),
     (12, 8, 500, 1.2, "far"),
     (6, 16, 300, 1.0, "equal"),
