@@ -646,9 +646,11 @@ struct MfmaShape {
   double tflops;
   double fixed_us;
 };
-static const MfmaShape kShapes[6] = {{256, 256, true, 4.96, 6.8},  {256, 192, true, 4.84, 6.5},
-                                     {256, 128, true, 4.6, 6.1},   {128, 256, true, 4.75, 8.3},
-                                     {128, 128, false, 3.18, 6.6}, {128, 96, false, 3.45, 5.0}};
+static constexpr int kNShapes = 7;
+static const MfmaShape kShapes[kNShapes] = {
+    {256, 256, true, 4.96, 6.8},  {256, 192, true, 4.84, 6.5}, {256, 128, true, 4.6, 6.1},
+    {128, 256, true, 4.75, 8.3},  {128, 128, false, 3.18, 6.6}, {128, 96, false, 3.45, 5.0},
+    {96, 256, true, 4.3, 8.3}};
 
 // Whether a shape can take K slices of ks: fp32-store / residual epilogues
 // only (slices write fp32 partials that a reduce kernel sums in order). The
@@ -703,9 +705,15 @@ struct MfmaPlan {
 static MfmaPlan mfma_plan(int epi, int M, int N, int K) {
   MfmaPlan best{0, 1};
   double best_t = 1e300;
-  for (int i = 0; i < 6; ++i) {
+  for (int i = 0; i < kNShapes; ++i) {
     const MfmaShape& sh = kShapes[i];
     if (epi == EPI_SWIGLU && sh.bn == 96) continue;
+    // 96-row blocks (waves of 48x64) only for stores and residual adds whose
+    // rows they cover with less padding than 128-row blocks (261 rows: 288
+    // computed instead of 384).
+    if (sh.bm == 96 && (epi == EPI_SWIGLU || epi == EPI_ARGMAX ||
+                        (M + 95) / 96 * 96 >= (M + 127) / 128 * 128))
+      continue;
     if (epi == EPI_ARGMAX && sh.bm != sh.bn) continue;
     if (sh.pipe && (K / 32) % 2) continue;
     for (int ks = 1; ks <= kMfmaMaxSplit; ks *= 2) {
@@ -890,6 +898,9 @@ static hipError_t launch_mfma_epi(const GemmArgs& a, hipStream_t st) {
       if constexpr (EPI == EPI_ARGMAX) return hipErrorInvalidValue;
       else return launch_pipe_t<128, 256, 2, 4, 4, EPI>(a, st);
     case 4: return launch_mfma_t<128, 128, 2, 2, 2, 4, EPI>(a, st);
+    case 6:
+      if constexpr (EPI == EPI_ARGMAX || EPI == EPI_SWIGLU) return hipErrorInvalidValue;
+      else return launch_pipe_t<96, 256, 2, 4, 4, EPI>(a, st);
     default:
       if constexpr (EPI == EPI_ARGMAX || EPI == EPI_SWIGLU) return hipErrorInvalidValue;
       else return launch_mfma_t<128, 96, 2, 2, 2, 4, EPI>(a, st);

@@ -98,6 +98,48 @@ def test_gpu_qwen3_8b_shaped_batch32_ragged_planted_accept():
     assert checked >= W.batch // 2, f"only {checked}/{W.batch} accept lengths compared"
 
 
+def test_gpu_qwen3_8b_shaped_batch32_append():
+    """The batch-32 round's append: 261 new rows over 32 ragged sequences
+    (the projections' 96-row blocks), every sequence and layer against the
+    oracle. Only the positions matter here, so the cache starts empty of
+    values with the workload's context lengths."""
+    W = WORKLOADS["q32"]
+    cfg = W.model
+    ctx_lens = I.ctx_lengths(W)
+    # the round's draw of 1..B new rows per sequence (261 in all)
+    n_new = np.random.Generator(np.random.PCG64(W.seeds["round_base"])).integers(
+        1, cfg.block_size + 1, size=W.batch).astype(np.int32)
+    n_tok = int(n_new.sum())
+    log(f"case: {W.name} append, {n_tok} new rows {n_new.tolist()}")
+    M = build_model(cfg)
+    cap = capacity_for(int(ctx_lens.max()) + int(n_new.max()), cfg.block_size)
+    cache = M.gpu.new_cache(W.batch, cap)
+    cache.ctx_len.copy_(torch.as_tensor(ctx_lens.astype(np.int32)))
+    ws = M.gpu.new_workspace(W.batch, cap, n_tok)
+    feats = I.target_hiddens(cfg, n_tok, seed=W.seeds["round_base"], tag="q32.append")
+    ctx = torch.empty((n_tok, cfg.hidden), dtype=M.gpu.dtype, device="cuda")
+    M.gpu.ctx_project([torch_io.to_device(f) for f in feats], ctx, ws)
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    cu = prefix_offsets(n_new)
+    M.gpu.ctx_kv_append(cache, ctx, torch.from_numpy(cu).cuda(), ws, status)
+    torch.cuda.synchronize()
+    assert status.item() == 0
+    assert cache.ctx_len.cpu().numpy().tolist() == (ctx_lens + n_new).tolist()
+
+    ow = M.oracle_w
+    ctx_o = O.ctx_project([f.f32() for f in feats], ow["fc"], ow["fc_norm"], cfg.rms_eps)
+    assert_close(cfg, to_np(ctx), ctx_o, "q32: ctx_project of new rows", group_axes=1)
+    ks, vs = [], []
+    for s in range(W.batch):
+        new = O.prefill_cache(ctx_o[cu[s]:cu[s + 1]], int(ctx_lens[s]), ow, cfg)
+        for l in range(cfg.n_layers):
+            kg, vg = cache.read_positions(l, s, int(ctx_lens[s]), int(n_new[s]))
+            ks.append((f"seq {s} layer {l}", to_np(kg), new.k[l]))
+            vs.append((f"seq {s} layer {l}", to_np(vg), new.v[l]))
+    assert_close_each(cfg, ks, "q32: appended K", group_axes=1)
+    assert_close_each(cfg, vs, "q32: appended V", group_axes=1)
+
+
 def test_gpu_qwen3_8b_shaped_batch4_ctx32768_append():
     W = WORKLOADS["q4l"]
     cfg = W.model
