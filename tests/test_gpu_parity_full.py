@@ -2,6 +2,8 @@
 
 * batch 32, ragged contexts 512-8192, accept lengths planted on 0..15 against
   the oracle's drafts, fused accept;
+* batch 32, the round's 261 new rows over the ragged contexts: ctx_project and
+  every sequence's and layer's appended K/V;
 * batch 4 at 32768 context: 1-16 new rows per sequence fused and injected with
   ctx_project + ctx_kv_append, then the forward;
 * LLaMA-3.1-8B-shaped batch 16, 64 consecutive rounds (append, forward,
