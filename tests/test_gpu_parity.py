@@ -170,6 +170,15 @@ def test_gpu_qwen3_8b_shaped_batch1_ctx2048():
     run_flow(QWEN3_8B_SHAPED, [2048], "q1")
 
 
+def test_gpu_qwen3_dims_batch18_96row_blocks():
+    # Qwen3-8B-shaped projections (small vocabulary, short contexts) at batch
+    # 18: 270 context rows project and append on 96-row blocks, and the 288
+    # forward rows run O and down on 96-row blocks with K slices.
+    ctx = [0, 13, 9, 20, 23, 10, 12, 6, 25, 25, 19, 16, 16, 18, 20, 17, 21, 0]
+    assert sum(ctx) == 270
+    run_flow(QWEN3_8B_SHAPED.with_(vocab=4096), ctx, "q-dims-b18")
+
+
 def test_gpu_capacity_overflow_is_flagged_and_clamped():
     cfg = TINY_FP32
     log(f"case: capacity overflow, {cfg.name}")
