@@ -105,9 +105,8 @@ def parse():
 def main() -> int:
     a = parse()
     if a.gpus != 1:
-        print(f"bench.py runs on exactly one GPU; --gpus {a.gpus} is not supported by this "
-              "single-GPU build (the drafter pass needs no exchange between GPUs).",
-              file=sys.stderr)
+        print(f"bench.py runs on exactly one GPU; --gpus {a.gpus} is not supported "
+              "(the drafter pass needs no exchange between GPUs).", file=sys.stderr)
         return 2
     import torch
     from block_diffusion_drafter_amd import binding as B
